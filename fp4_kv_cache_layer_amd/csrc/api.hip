@@ -1,0 +1,216 @@
+// C ABI of the CSA2 layer step (declared in include/csa2.h): host-side
+// argument validation, workspace sizing and kernel dispatch.  Nothing here
+// allocates device memory or synchronises a stream.
+#include "csa2.h"
+#include "csa2_internal.h"
+
+#include <cmath>
+
+using namespace csa2;
+
+namespace {
+
+csa2_timing_ring* g_rings[CSA2_NUM_KCLASSES] = {nullptr, nullptr, nullptr, nullptr};
+
+struct TimedLaunch {
+  csa2_timing_ring* ring;
+  hipStream_t s;
+  int slot;
+  TimedLaunch(int cls, hipStream_t st) : ring(g_rings[cls]), s(st), slot(-1) {
+    if (ring && ring->count < ring->capacity) {
+      slot = ring->count;
+      (void)hipEventRecord(ring->start[slot], s);
+    }
+  }
+  ~TimedLaunch() {
+    if (slot >= 0) {
+      (void)hipEventRecord(ring->stop[slot], s);
+      ring->count = slot + 1;
+    }
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ilog2_pow2(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+csa2_status check_cache(const csa2_cache_view* c, CacheArgs* out) {
+  if (!c || !c->kv || !c->idx_k || !c->page_table) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(c->kv, 16) || !aligned(c->idx_k, 16) || !aligned(c->page_table, 4)) return CSA2_ERR_INVALID_ARG;
+  if (c->num_pages < 1 || c->num_seqs < 1 || c->max_pages < 1) return CSA2_ERR_INVALID_ARG;
+  const int lg = ilog2_pow2(c->page_size);
+  if (lg < 0 || c->page_size < CSA2_MIN_PAGE_SIZE) return CSA2_ERR_INVALID_ARG;
+  if ((int64_t)c->max_pages * c->page_size > INT32_MAX) return CSA2_ERR_UNSUPPORTED;
+  out->kv = c->kv;
+  out->idx_k = c->idx_k;
+  out->page_table = c->page_table;
+  out->max_pages = c->max_pages;
+  out->lg_page = lg;
+  return CSA2_OK;
+}
+
+csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+csa2_status validate_index(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                           const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis,
+                           const int32_t* out_idx, const int32_t* out_cnt, const void* ws, size_t ws_bytes,
+                           CacheArgs* ca) {
+  if (nq < 0 || h_idx < 1 || h_idx > CSA2_MAX_H_IDX || k < 1 || k > CSA2_MAX_K || max_vis < 0)
+    return CSA2_ERR_INVALID_ARG;
+  csa2_status st = check_cache(c, ca);
+  if (st != CSA2_OK) return st;
+  if ((int64_t)max_vis > (int64_t)c->max_pages * c->page_size) return CSA2_ERR_INVALID_ARG;
+  if (nq == 0) return CSA2_OK;
+  if (!q_idx || !w || !q_seq || !q_vis || !out_idx || !out_cnt || !ws) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(q_seq, 4) || !aligned(q_vis, 4) ||
+      !aligned(out_idx, 16) || !aligned(out_cnt, 4) || !aligned(ws, 16))
+    return CSA2_ERR_INVALID_ARG;
+  if (ws_bytes < index_ws_bytes(nq, max_vis)) return CSA2_ERR_WORKSPACE;
+  return CSA2_OK;
+}
+
+csa2_status validate_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
+                          const int32_t* cnt, int32_t nq, int32_t h, int32_t k, float sm_scale, const float* out,
+                          const float* lse, CacheArgs* ca) {
+  if (nq < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return CSA2_ERR_INVALID_ARG;
+  csa2_status st = check_cache(c, ca);
+  if (st != CSA2_OK) return st;
+  if (nq == 0) return CSA2_OK;
+  if (!q || !q_seq || !idx || !cnt || !out) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(q_seq, 4) || !aligned(idx, 4) || !aligned(cnt, 4) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+csa2_status validate_append(const csa2_cache_view* c, const int32_t* slots, const uint16_t* kv_rows,
+                            const uint16_t* idxk_rows, int32_t n, CacheArgs* ca) {
+  if (n < 0) return CSA2_ERR_INVALID_ARG;
+  csa2_status st = check_cache(c, ca);
+  if (st != CSA2_OK) return st;
+  if (n == 0) return CSA2_OK;
+  if (!slots || !kv_rows || !idxk_rows) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(slots, 4) || !aligned(kv_rows, 16) || !aligned(idxk_rows, 16)) return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                      const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
+                      int32_t* out_cnt, void* ws, hipStream_t s) {
+  const IndexWs iw = index_ws_carve(ws, nq, max_vis);
+  if (max_vis > 0) {
+    TimedLaunch t(CSA2_KCLASS_SCAN, s);
+    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s));
+    if (st != CSA2_OK) return st;
+  }
+  TimedLaunch t(CSA2_KCLASS_SELECT, s);
+  return hip_status(launch_topk_select(iw, q_vis, nq, k, out_idx, out_cnt, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(csa2_status st) {
+  switch (st) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported request";
+    case CSA2_ERR_WORKSPACE: return "workspace too small";
+    case CSA2_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring) {
+  if (kernel_class < 0 || kernel_class >= CSA2_NUM_KCLASSES) return CSA2_ERR_INVALID_ARG;
+  if (ring && (ring->capacity < 0 || (ring->capacity > 0 && (!ring->start || !ring->stop))))
+    return CSA2_ERR_INVALID_ARG;
+  g_rings[kernel_class] = ring;
+  return CSA2_OK;
+}
+
+size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
+  (void)h_idx; (void)h; (void)k;
+  if (nq <= 0 || max_vis < 0) return 0;
+  if (mode == CSA2_REUSE) return 0;
+  return index_ws_bytes(nq, max_vis);
+}
+
+csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
+  if (ws_bytes == 0) return CSA2_OK;
+  if (!ws || !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_fill_zero(ws, ws_bytes, s));
+}
+
+csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots, const uint16_t* kv_rows,
+                                  const uint16_t* idxk_rows, int32_t n, hipStream_t s) {
+  CacheArgs ca;
+  csa2_status st = validate_append(c, slots, kv_rows, idxk_rows, n, &ca);
+  if (st != CSA2_OK || n == 0) return st;
+  TimedLaunch t(CSA2_KCLASS_APPEND, s);
+  return hip_status(launch_append_quant(ca.kv, ca.idx_k, slots, kv_rows, idxk_rows, n, s));
+}
+
+csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                            const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis,
+                            int32_t* out_idx, int32_t* out_cnt, void* ws, size_t ws_bytes, hipStream_t s) {
+  CacheArgs ca;
+  csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
+  if (st != CSA2_OK || nq == 0) return st;
+  return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, s);
+}
+
+csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
+                             const int32_t* cnt, int32_t nq, int32_t h, int32_t k, float sm_scale, float* out,
+                             float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws; (void)ws_bytes;
+  CacheArgs ca;
+  csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
+  if (st != CSA2_OK || nq == 0) return st;
+  TimedLaunch t(CSA2_KCLASS_ATTN, s);
+  return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, s));
+}
+
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
+  if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
+  CacheArgs ca;
+  csa2_status st;
+  if (mode == CSA2_FULL) {
+    st = validate_append(a->cache, a->new_slots, a->new_kv, a->new_idxk, a->n_new, &ca);
+    if (st != CSA2_OK) return st;
+  } else if (a->n_new != 0 || a->new_slots || a->new_kv || a->new_idxk) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  if (mode != CSA2_REUSE) {
+    st = validate_index(a->cache, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx,
+                        a->cnt, a->ws, a->ws_bytes, &ca);
+    if (st != CSA2_OK) return st;
+  } else if (a->q_idx || a->w || a->h_idx != 0) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  st = validate_attn(a->cache, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out, a->lse, &ca);
+  if (st != CSA2_OK) return st;
+
+  if (mode == CSA2_FULL && a->n_new > 0) {
+    TimedLaunch t(CSA2_KCLASS_APPEND, s);
+    st = hip_status(launch_append_quant(ca.kv, ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s));
+    if (st != CSA2_OK) return st;
+  }
+  if (a->nq == 0) return CSA2_OK;
+  if (mode != CSA2_REUSE) {
+    st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt, a->ws, s);
+    if (st != CSA2_OK) return st;
+  }
+  TimedLaunch t(CSA2_KCLASS_ATTN, s);
+  return hip_status(launch_sparse_attn(ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
+                                       a->lse, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the CSA2 kernels (gfx950 only).
+//
+// Number formats follow the choices stated in include/csa2.h: main-KV rows
+// are E2M1 codes with one E8M0 scale per 32 values, indexer rows are OCP
+// E4M3FN.  The E2M1 format for the main KV is named on the aiany.app
+// "DeepSeek-V4.1-Flash" page, "What Sets It Apart".
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLatent = 512;
+constexpr int kIndexDim = 128;
+constexpr int kKvRowBytes = 272;
+constexpr int kCodeBytes = 256;
+constexpr int kHistBits = 11;                 // first radix digit of the score key
+constexpr int kHistBins = 1 << kHistBits;
+
+// ---------------------------------------------------------------------------
+// E8M0 block exponent: the smallest integer e with amax <= 6 * 2^e, read off
+// the fp32 bit pattern of amax.  For amax = 1.f * 2^E (normal), 6 * 2^e >=
+// amax holds first at e = E - 2 when 1.f <= 1.5 and at e = E - 1 otherwise;
+// amax below 2^-126 (or zero) needs e < -127 and is clamped there.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_exponent(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  int ef = (int)((u >> 23) & 0xFF);
+  if (ef == 0) return -127;
+  int e = ef - 127 - 2 + ((u & 0x7FFFFF) > 0x400000 ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E2M1 code of r = x / 2^e (|r| <= 6 by construction): round to the nearest of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}; at a midpoint the code with a 0 low bit wins,
+// so 0.25, 1.25, 2.5 and 5 round down and 0.75, 1.75 and 3.5 round up.  The
+// magnitude code is the number of decision points at or below |r|.
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+  float a = fabsf(r);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(r) >> 28) & 0x8u);
+}
+
+// OCP E4M3FN byte of an fp32 value: round to nearest even, saturate to 448,
+// sign bit copied (so -0 and small negatives give 0x80).
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t c;
+  if (a >= 448.0f) {
+    c = 0x7E;
+  } else if (a < 0.015625f) {                  // below 2^-6: multiples of 2^-9
+    c = (uint32_t)__builtin_rintf(a * 512.0f); // exact product; rint is ties-to-even
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);           // round the 23-bit mantissa to 3 bits
+    c = (u >> 20) - (120u << 3);                // rebias 127 -> 7, keep 3 mantissa bits
+    if (c > 0x7E) c = 0x7E;
+  }
+  return c | sign;
+}
+
+// fp32 score -> unsigned key whose order is the float order; -0 counts as +0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// E8M0 byte -> fp32 scale 2^(b-127); byte 0 is the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_to_float(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// Physical row of logical entry t of a sequence: page table lookup.
+__device__ __forceinline__ int64_t entry_row(const int32_t* __restrict__ pt_row, int t, int lg_ps) {
+  int page = pt_row[t >> lg_ps];
+  return ((int64_t)page << lg_ps) + (t & ((1 << lg_ps) - 1));
+}
+
+}  // namespace csa2

@@ -1,0 +1,124 @@
+// Indexer scan: s_t = sum_h w_h * max(0, q_h . k_t) over every visible entry
+// of a query's sequence, with the scores written to the workspace and a
+// histogram of their top 11 key bits accumulated for the Top-K select.
+//
+// The scan over the cached indexer-K is the step the Full and Reindex modes
+// spend their indexing compute on ("Unlocking Extreme Context Scaling with
+// DeepSeek-V4.1-Flash", section "Compressed Sparse Attention 2 (CSA2)"); the
+// pages give no formula, the one above is the reading stated in csa2.h.
+//
+// Dot products run on the gfx950 FP8 matrix core: one
+// V_MFMA_F32_16X16X128_F8F6F4 multiplies the (zero-padded to 16) indexer
+// heads by 16 entries over the full 128-wide dimension.  Lane l supplies
+// head / entry (l % 16) and bytes [32*(l/16), +32) of its row, so each lane
+// streams 32 contiguous bytes of one indexer-K row per tile and a wave
+// streams 2 KB.  The result puts entry (l % 16) and heads 4*(l/16)+i in lane
+// l, so the ReLU * w reduction is 4 FMAs and two cross-lane adds.
+#include "csa2_device.h"
+#include "csa2_internal.h"
+
+namespace csa2 {
+
+constexpr int kScanWaves = 4;
+constexpr int kScanUnroll = 4;          // 16-entry tiles in flight per wave
+
+int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 63) / 64 * 64; }
+
+size_t index_ws_bytes(int32_t nq, int32_t max_vis) {
+  return (size_t)nq * kHistBins * 4 + (size_t)nq * (size_t)index_vstride(max_vis) * 4;
+}
+
+IndexWs index_ws_carve(void* ws, int32_t nq, int32_t max_vis) {
+  IndexWs r;
+  r.hist = reinterpret_cast<uint32_t*>(ws);
+  r.scores = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + (size_t)nq * kHistBins * 4);
+  r.vstride = index_vstride(max_vis);
+  return r;
+}
+
+__global__ void __launch_bounds__(kScanWaves * 64)
+index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                  const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
+                  int h_idx, int nchunks, IndexWs ws) {
+  __shared__ uint32_t hist[kHistBins];
+  const int q = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x - q * nchunks;
+  const int vis = q_vis[q];
+  const int t0 = chunk * kScanChunk;
+  if (t0 >= vis) return;                              // uniform for the block
+  const int t1 = min(vis, t0 + kScanChunk);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < h_idx) {
+    const intx4* src = reinterpret_cast<const intx4*>(q_idx + ((int64_t)q * h_idx + r) * kIndexDim + 32 * g);
+    const intx4 lo = src[0], hi = src[1];
+    a = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < h_idx) ? w[(int64_t)q * h_idx + 4 * g + i] : 0.0f;
+
+  const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
+  float* srow = ws.scores + (int64_t)q * ws.vstride;
+  const int ntiles = (t1 - t0 + 15) >> 4;
+  __syncthreads();
+
+  for (int base = wave * kScanUnroll; base < ntiles; base += kScanWaves * kScanUnroll) {
+    intx8 b[kScanUnroll];
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int j = base + u;
+      if (j < ntiles) {
+        const int t = t0 + 16 * j + r;                // same page as the tile start (< vis)
+        const int64_t row = entry_row(pt_row, t0 + 16 * j, c.lg_page) + r;
+        const intx4* src = reinterpret_cast<const intx4*>(c.idx_k + row * kIndexDim + 32 * g);
+        const intx4 lo = src[0], hi = src[1];
+        b[u] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        (void)t;
+      } else {
+        b[u] = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int j = base + u;
+      if (j >= ntiles) break;
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[u], acc, 0, 0, 0, 0, 0, 0);
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.0f);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      const int t = t0 + 16 * j + r;
+      if (g == 0 && t < t1) {
+        uint32_t u32 = __float_as_uint(part);
+        if ((u32 << 1) == 0) u32 = 0;                 // -0 -> +0
+        srow[t] = __uint_as_float(u32);
+        atomicAdd(&hist[score_key(__uint_as_float(u32)) >> (32 - kHistBits)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
+  for (int i = tid; i < kHistBins; i += kScanWaves * 64) {
+    const uint32_t v = hist[i];
+    if (v) atomicAdd(&gh[i], v);
+  }
+}
+
+hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                             const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                             hipStream_t s) {
+  const int nchunks = (max_vis + kScanChunk - 1) / kScanChunk;
+  const int64_t blocks = (int64_t)nq * nchunks;
+  hipLaunchKernelGGL(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, s, c, q_idx, w, q_seq,
+                     q_vis, h_idx, nchunks, ws);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

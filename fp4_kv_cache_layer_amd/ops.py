@@ -1,0 +1,201 @@
+"""Python binding of the CSA2 C ABI: argument marshalling only.
+
+Every function takes device tensors, passes their pointers and the current
+HIP stream to libcsa2.so, and raises if the library reports an error.  The
+computation itself runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+FULL, REINDEX, REUSE = L.CSA2_FULL, L.CSA2_REINDEX, L.CSA2_REUSE
+KV_ROW_BYTES, IDXK_ROW_BYTES, D_LATENT, D_INDEX = 272, 128, 512, 128
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("CSA2 ops take device tensors")
+    if not t.is_contiguous():
+        raise ValueError("CSA2 ops take contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, dtypes, name: str):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+_BF16 = (torch.int16, torch.bfloat16, torch.uint16)
+
+
+class Cache:
+    """One Full layer's paged global cache in device memory.
+
+    kv    [num_pages][page_size][272] uint8 (E2M1 codes + E8M0 scales)
+    idx_k [num_pages][page_size][128] uint8 (E4M3FN)
+    page_table [num_seqs][max_pages] int32, seq_lens [num_seqs] int32.
+    """
+
+    def __init__(self, num_pages: int, page_size: int, page_table: torch.Tensor,
+                 seq_lens: Optional[torch.Tensor] = None, device="cuda", kv=None, idx_k=None):
+        self.kv = kv if kv is not None else torch.zeros((num_pages, page_size, KV_ROW_BYTES), dtype=torch.uint8, device=device)
+        self.idx_k = idx_k if idx_k is not None else torch.zeros((num_pages, page_size, IDXK_ROW_BYTES), dtype=torch.uint8, device=device)
+        self.page_table = page_table.to(device=device, dtype=torch.int32).contiguous()
+        ns = self.page_table.shape[0]
+        self.seq_lens = (seq_lens if seq_lens is not None else torch.zeros(ns, dtype=torch.int32)).to(device=device, dtype=torch.int32).contiguous()
+        self.num_pages, self.page_size = num_pages, page_size
+        self._view = L.CacheView(_ptr(self.kv), _ptr(self.idx_k), _ptr(self.page_table), _ptr(self.seq_lens),
+                                 num_pages, page_size, ns, self.page_table.shape[1])
+
+    @property
+    def view(self) -> L.CacheView:
+        return self._view
+
+    @property
+    def num_seqs(self) -> int:
+        return self.page_table.shape[0]
+
+    @property
+    def max_pages(self) -> int:
+        return self.page_table.shape[1]
+
+
+def csa2_workspace_bytes(mode: int, nq: int, max_vis: int, h_idx: int, h: int, k: int) -> int:
+    return int(L.load().csa2_workspace_bytes(mode, nq, max_vis, h_idx, h, k))
+
+
+def csa2_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    L.check("csa2_workspace_init", L.load().csa2_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def workspace(mode: int, nq: int, max_vis: int, h_idx: int, h: int, k: int, device="cuda", stream=None) -> torch.Tensor:
+    """A zero-initialised workspace sized for the given call shape."""
+    n = csa2_workspace_bytes(mode, nq, max_vis, h_idx, h, k)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    csa2_workspace_init(ws, stream)
+    return ws
+
+
+def csa2_append_quant_fp4(cache: Cache, slots: torch.Tensor, kv_rows: torch.Tensor, idxk_rows: torch.Tensor,
+                          stream=None) -> None:
+    _need(slots, (torch.int32,), "slots")
+    _need(kv_rows, _BF16, "kv_rows")
+    _need(idxk_rows, _BF16, "idxk_rows")
+    n = slots.numel()
+    if kv_rows.numel() != n * D_LATENT or idxk_rows.numel() != n * D_INDEX:
+        raise ValueError("append: row tensors do not match the slot count")
+    L.check("csa2_append_quant_fp4", L.load().csa2_append_quant_fp4(
+        ctypes.byref(cache.view), _ptr(slots), _ptr(kv_rows), _ptr(idxk_rows), n, _stream(stream)))
+
+
+def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor,
+                    k: int, max_vis: int, ws: torch.Tensor, out_idx: Optional[torch.Tensor] = None,
+                    out_cnt: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    nq, h_idx = q_idx.shape[0], q_idx.shape[1]
+    _need(q_idx, (torch.uint8,), "q_idx")
+    _need(w, (torch.float32,), "w")
+    if out_idx is None:
+        out_idx = torch.empty((nq, k), dtype=torch.int32, device=q_idx.device)
+    if out_cnt is None:
+        out_cnt = torch.empty(nq, dtype=torch.int32, device=q_idx.device)
+    L.check("csa2_index_topk", L.load().csa2_index_topk(
+        ctypes.byref(cache.view), _ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(q_vis), nq, h_idx, k, max_vis,
+        _ptr(out_idx), _ptr(out_cnt), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_cnt
+
+
+def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: torch.Tensor, cnt: torch.Tensor,
+                     sm_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     with_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    _need(q, _BF16, "q")
+    nq, h = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((nq, h, D_LATENT), dtype=torch.float32, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((nq, h), dtype=torch.float32, device=q.device)
+    L.check("csa2_sparse_attn", L.load().csa2_sparse_attn(
+        ctypes.byref(cache.view), _ptr(q), _ptr(q_seq), _ptr(idx), _ptr(cnt), nq, h, k, float(sm_scale),
+        _ptr(out), _ptr(lse), None, 0, _stream(stream)))
+    return out, lse
+
+
+class LayerCall:
+    """Prepared arguments of one csa2_layer_step call (pointers fixed at
+    construction, so repeated launches cost one ctypes call each)."""
+
+    def __init__(self, mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor,
+                 k: int, max_vis: int, sm_scale: float, idx: torch.Tensor, cnt: torch.Tensor,
+                 out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                 q_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                 new_slots: Optional[torch.Tensor] = None, new_kv: Optional[torch.Tensor] = None,
+                 new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+        self.mode = mode
+        self.cache = cache
+        self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws)
+        a = L.StepArgs()
+        a.cache = ctypes.pointer(cache.view)
+        if mode == FULL and new_slots is not None and new_slots.numel() > 0:
+            a.new_slots, a.new_kv, a.new_idxk, a.n_new = _ptr(new_slots), _ptr(new_kv), _ptr(new_idxk), new_slots.numel()
+        if mode in (FULL, REINDEX):
+            a.q_idx, a.w, a.h_idx = _ptr(q_idx), _ptr(w), q_idx.shape[1]
+            a.ws, a.ws_bytes = _ptr(ws), ws.numel()
+        a.q, a.h, a.sm_scale = _ptr(q), q.shape[1], float(sm_scale)
+        a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = _ptr(q_seq), _ptr(q_vis), q.shape[0], k, max_vis
+        a.idx, a.cnt, a.out, a.lse = _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse)
+        self.args = a
+        self._ref = ctypes.byref(a)
+        self._fn = L.load().csa2_layer_step
+
+    def __call__(self, stream=None) -> None:
+        st = self._fn(self.mode, self._ref, _stream(stream))
+        if st:
+            L.check("csa2_layer_step", st)
+
+
+def csa2_layer_step(mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor, k: int,
+                    max_vis: int, sm_scale: float, idx: torch.Tensor, cnt: torch.Tensor, out: torch.Tensor,
+                    lse: Optional[torch.Tensor] = None, q_idx=None, w=None, new_slots=None, new_kv=None,
+                    new_idxk=None, ws=None, stream=None) -> None:
+    LayerCall(mode, cache, q, q_seq, q_vis, k, max_vis, sm_scale, idx, cnt, out, lse, q_idx, w,
+              new_slots, new_kv, new_idxk, ws)(stream)
+
+
+class TimingRing:
+    """Device-event ring for one kernel class (see csa2_set_timing)."""
+
+    def __init__(self, kernel_class: int, capacity: int):
+        self.kernel_class = kernel_class
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        for a, b in self.events:          # materialise the hipEvent handles
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        self._start = (ctypes.c_void_p * capacity)(*[a.cuda_event for a, _ in self.events])
+        self._stop = (ctypes.c_void_p * capacity)(*[b.cuda_event for _, b in self.events])
+        self.ring = L.TimingRing(ctypes.cast(self._start, ctypes.POINTER(ctypes.c_void_p)),
+                                 ctypes.cast(self._stop, ctypes.POINTER(ctypes.c_void_p)), capacity, 0)
+
+    def install(self) -> None:
+        self.ring.count = 0
+        L.check("csa2_set_timing", L.load().csa2_set_timing(self.kernel_class, ctypes.byref(self.ring)))
+
+    def uninstall(self) -> None:
+        L.check("csa2_set_timing", L.load().csa2_set_timing(self.kernel_class, None))
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.events[:self.ring.count]]

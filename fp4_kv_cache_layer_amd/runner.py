@@ -1,0 +1,98 @@
+"""Device-side set-up and execution of one workload's CSA2 layer group.
+
+Builds the paged cache by bulk quantize-on-append of the workload's cached
+rows, prepares every layer's inputs and outputs, and runs the layers in group
+order: Reindex and Reuse layers read the Full layer's cache, Reuse layers
+read the Full layer's indices.  All compute goes through libcsa2.so.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+import workloads as W
+from . import ops
+
+APPEND_CHUNK = 1 << 20          # rows per bulk append call
+
+
+class DeviceCase:
+    def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda"):
+        self.spec = spec
+        self.device = device
+        self.gen_device = gen_device
+        pt = torch.from_numpy(W.page_table(spec))
+        seq_lens = torch.tensor([spec.seq_len_after(s) for s in range(spec.num_seqs)], dtype=torch.int32)
+        self.page_table = pt
+        self.cache = ops.Cache(spec.total_pages(), spec.page_size, pt, seq_lens, device=device)
+        self.q_seq = torch.from_numpy(spec.q_seq()).to(device)
+        self.q_vis = torch.from_numpy(spec.q_vis()).to(device)
+        self.max_vis = int(spec.q_vis().max()) if spec.nq else 0
+        self._fill_cache()
+        self._layers()
+
+    # -- cache fill: cached entries written by bulk append; new rows kept for the Full layer --
+    def _fill_cache(self):
+        spec, dev = self.spec, self.device
+        new_s, new_kv, new_ik = [], [], []
+        pt_np = self.page_table.numpy()
+        for s in range(spec.num_seqs):
+            kv = W.kv_rows(spec, s, self.gen_device)
+            ik = W.idxk_rows(spec, s, self.gen_device)
+            c = spec.cached[s]
+            for a in range(0, c, APPEND_CHUNK):
+                b = min(c, a + APPEND_CHUNK)
+                slots = torch.from_numpy(W.slots_for(spec, pt_np, s, a, b)).to(dev)
+                ops.csa2_append_quant_fp4(self.cache, slots, kv[a:b].to(dev).contiguous(), ik[a:b].to(dev).contiguous())
+            if spec.n_new:
+                new_s.append(torch.from_numpy(W.slots_for(spec, pt_np, s, c, c + spec.n_new)))
+                new_kv.append(kv[c:c + spec.n_new].to(dev))
+                new_ik.append(ik[c:c + spec.n_new].to(dev))
+            del kv, ik
+        if spec.n_new:
+            self.new_slots = torch.cat(new_s).to(dev).contiguous()
+            self.new_kv = torch.cat(new_kv).contiguous()
+            self.new_ik = torch.cat(new_ik).contiguous()
+        else:
+            self.new_slots = self.new_kv = self.new_ik = None
+
+    def _layers(self):
+        spec, dev = self.spec, self.device
+        nq, k = spec.nq, spec.k
+        self.ws = ops.workspace(ops.FULL, nq, self.max_vis, spec.h_idx, spec.h, k, device=dev)
+        self.inputs = []
+        self.outputs = []
+        self.calls: List[ops.LayerCall] = []
+        full_idx = full_cnt = None
+        for li, mode in enumerate(spec.modes):
+            qi, w, q = W.layer_queries(spec, li, self.gen_device)
+            qi, w, q = qi.to(dev).contiguous(), w.to(dev).contiguous(), q.to(dev).contiguous()
+            self.inputs.append((qi, w, q))
+            out = torch.empty((nq, spec.h, 512), dtype=torch.float32, device=dev)
+            lse = torch.empty((nq, spec.h), dtype=torch.float32, device=dev)
+            if mode == ops.REUSE:
+                idx, cnt = full_idx, full_cnt
+                call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                     idx, cnt, out, lse)
+            else:
+                idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+                cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+                if mode == ops.FULL:
+                    call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                         idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
+                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=self.ws)
+                    full_idx, full_cnt = idx, cnt
+                else:
+                    call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                         idx, cnt, out, lse, q_idx=qi, w=w, ws=self.ws)
+            self.outputs.append(dict(idx=idx, cnt=cnt, out=out, lse=lse))
+            self.calls.append(call)
+
+    def run_group(self, stream=None) -> None:
+        for c in self.calls:
+            c(stream)
+
+    def results_host(self) -> List[dict]:
+        torch.cuda.synchronize()
+        return [{key: (v.cpu().numpy() if v is not None else None) for key, v in o.items()} for o in self.outputs]

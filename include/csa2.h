@@ -1,0 +1,215 @@
+/*
+ * csa2.h - C ABI of one Compressed Sparse Attention 2 (CSA2) layer step over
+ * an FP4 (E2M1 + E8M0) global KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the step is.  CSA2 runs every layer in one of three static modes that
+ * share one global KV cache and one sparse selection across layers
+ * ("Unlocking Extreme Context Scaling with DeepSeek-V4.1-Flash", section
+ * "Compressed Sparse Attention 2 (CSA2)"; the same three modes in
+ * "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+ * Method):
+ *   Full    - writes fresh main-KV and indexer-K entries, scores them and
+ *             selects new Top-512 indices, then attends;
+ *   Reindex - scores a new indexer query against the last Full layer's
+ *             indexer-K and selects afresh, then attends over that layer's KV;
+ *   Reuse   - attends with the main KV and Top-K indices of an earlier layer,
+ *             skipping the indexer.
+ * The main KV is stored in the E2M1 FP4 format ("DeepSeek-V4.1-Flash",
+ * aiany.app item, "What Sets It Apart"), at about half the bytes of FP8
+ * ("Unlocking Extreme Context Scaling ...", "Deployment and
+ * Infrastructure"), and the global KV lives in HBM ("DeepSeek-V4.1-Flash",
+ * researchpod.app episode summary).
+ *
+ * Formats fixed here (the pages name the formats but not their layout):
+ *   main-KV row  : 512 latent values, one E8M0 scale per 32 consecutive
+ *                  values; 272 bytes = 256 bytes of E2M1 codes (element 2i
+ *                  in the low nibble of byte i, 2i+1 in the high nibble)
+ *                  followed by 16 scale bytes (value 2^(byte-127)).
+ *                  Encoding: scale = smallest 2^e with amax <= 6 * 2^e
+ *                  (e clamped to [-127, 127], all-zero block -> byte 0);
+ *                  code = round-to-nearest of x / 2^e on the E2M1 grid, ties
+ *                  to the even code, sign bit copied from x.
+ *   indexer-K row: 128 OCP E4M3FN bytes, round-to-nearest-even from bf16,
+ *                  saturating at +-448, sign bit copied.
+ *   indexer score: s_t = sum_h w_h * max(0, q_h . k_t), fp32 accumulation of
+ *                  exact FP8 products; a zero score counts as +0.
+ *   Top-K        : the first min(k, V) entries under (score descending,
+ *                  index ascending), written in ascending index order,
+ *                  slots beyond the count set to -1.
+ *   attention    : K = V = the dequantised latent row shared by all heads;
+ *                  O[h] = sum_j softmax_j(sm_scale * q_h . X_j) X_j over the
+ *                  selected rows, fp32; LSE[h] = natural-log normaliser.
+ *
+ * Conventions for every entry point.
+ *   - All data pointers are device pointers owned by the caller.  The library
+ *     allocates no memory and keeps no state between calls except what the
+ *     caller's workspace carries (see csa2_workspace_bytes).
+ *   - Work is enqueued on the given HIP stream and is asynchronous.  Argument
+ *     errors are found on the host before anything is enqueued and return a
+ *     status; execution errors surface at the caller's next stream sync.
+ *   - Device-resident values (seq_lens, q_vis, q_seq, page-table entries,
+ *     slots, idx, cnt) are trusted: the caller guarantees q_vis[i] <=
+ *     seq_len(q_seq[i]) <= max_pages * page_size and that every page-table
+ *     entry a query can reach lies in [0, num_pages).  Out-of-range device
+ *     data is undefined behaviour.
+ *   - Every pointer must be 16-byte aligned (w, q_seq, q_vis, cnt, lse,
+ *     slots: 4-byte aligned suffices); a zero count (n == 0 or nq == 0)
+ *     returns CSA2_OK and enqueues nothing.
+ *   - Indices are logical entry positions inside a sequence (not physical
+ *     slots), so a Reuse layer can hand them on unchanged.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_D_LATENT        512
+#define CSA2_D_INDEX         128
+#define CSA2_KV_ROW_BYTES    272
+#define CSA2_IDXK_ROW_BYTES  128
+#define CSA2_MAX_K           2048
+#define CSA2_MAX_H_IDX       16
+#define CSA2_MAX_H           128
+#define CSA2_MIN_PAGE_SIZE   64
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment      */
+  CSA2_ERR_UNSUPPORTED = 2,   /* valid request this library does not serve */
+  CSA2_ERR_WORKSPACE = 3,     /* ws_bytes below csa2_workspace_bytes(...)  */
+  CSA2_ERR_HIP = 4            /* a HIP launch failed                        */
+} csa2_status;
+
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode;
+
+/* One Full layer's global cache (all pointers device memory, caller-owned).
+ * Logical entry t of sequence s lives at page page_table[s*max_pages +
+ * t/page_size], row t % page_size of that page. */
+typedef struct {
+  uint8_t*       kv;          /* [num_pages][page_size][272] main-KV rows     */
+  uint8_t*       idx_k;       /* [num_pages][page_size][128] indexer-K rows   */
+  const int32_t* page_table;  /* [num_seqs][max_pages]                        */
+  const int32_t* seq_lens;    /* [num_seqs] valid entries (informational)     */
+  int32_t num_pages;
+  int32_t page_size;          /* power of two, >= CSA2_MIN_PAGE_SIZE          */
+  int32_t num_seqs;
+  int32_t max_pages;
+} csa2_cache_view;
+
+/* Quantize-on-append ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ * Compression", Method: FP4 global KV with an inference system built to
+ * serve the format).  Encodes n bf16 rows and writes them at physical slots
+ * slots[i] = page * page_size + row:
+ *   kv_rows   [n][512] bf16 bit patterns -> c->kv    (272-byte FP4 rows)
+ *   idxk_rows [n][128] bf16 bit patterns -> c->idx_k (128-byte E4M3 rows)
+ * Slots must be distinct within one call.  The caller updates seq_lens and
+ * the page table.  Output bytes are deterministic. */
+csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots,
+                                  const uint16_t* kv_rows, const uint16_t* idxk_rows,
+                                  int32_t n, hipStream_t s);
+
+/* Bytes of workspace an index_topk / layer_step call needs (0 for Reuse).
+ * The workspace holds per-query score and histogram buffers.  Its histogram
+ * part carries state: every call leaves it zeroed for the next one, so zero
+ * the whole workspace once after allocating it (csa2_workspace_init does
+ * this).  Calls that share one workspace must not run concurrently. */
+size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis,
+                            int32_t h_idx, int32_t h, int32_t k);
+
+/* Zero-fills ws_bytes of workspace on stream s (a fill kernel, no memset
+ * node, so it may be captured in a graph). */
+csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Indexer scoring + Top-K ("Unlocking Extreme Context Scaling ...", section
+ * CSA2: Full and Reindex modes score indexer queries against the cached
+ * indexer-K and select Top-512).  For query i of sequence q_seq[i], entries
+ * 0..q_vis[i]-1 are scored with
+ *   q_idx [nq][h_idx][128] E4M3 bytes, w [nq][h_idx] fp32,
+ * and out_idx [nq][k] int32 receives the selection in ascending index order
+ * (-1 padded), out_cnt [nq] the count min(k, q_vis[i]).
+ * max_vis is a host upper bound on q_vis (sizes the grid and workspace).
+ * 1 <= h_idx <= 16, 1 <= k <= CSA2_MAX_K. */
+csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,
+                            const int32_t* q_seq, const int32_t* q_vis,
+                            int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis,
+                            int32_t* out_idx, int32_t* out_cnt,
+                            void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Sparse attention over the selected rows (all three modes end here).
+ *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
+ *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq],
+ *   out [nq][h][512] fp32, lse [nq][h] fp32 (nullable).
+ * 1 <= h <= 128; sm_scale > 0 and finite.  ws may be NULL. */
+csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq,
+                             const int32_t* idx, const int32_t* cnt,
+                             int32_t nq, int32_t h, int32_t k, float sm_scale,
+                             float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Arguments of one layer.  Fields a mode does not use must be NULL / 0. */
+typedef struct {
+  const csa2_cache_view* cache;  /* Full: its own cache (written);
+                                    Reindex/Reuse: the source Full layer's   */
+  const int32_t*  new_slots;     /* Full only: rows appended before scoring  */
+  const uint16_t* new_kv;
+  const uint16_t* new_idxk;
+  int32_t         n_new;
+  const uint8_t*  q_idx;         /* Full, Reindex */
+  const float*    w;
+  int32_t         h_idx;
+  const uint16_t* q;             /* all modes */
+  int32_t         h;
+  float           sm_scale;
+  const int32_t*  q_seq;
+  const int32_t*  q_vis;
+  int32_t         nq;
+  int32_t         k;
+  int32_t         max_vis;
+  int32_t*        idx;           /* Full/Reindex: written; Reuse: read       */
+  int32_t*        cnt;
+  float*          out;
+  float*          lse;           /* nullable */
+  void*           ws;
+  size_t          ws_bytes;
+} csa2_step_args;
+
+/* One CSA2 layer in the given mode:
+ *   Full    = append (if n_new > 0) -> index_topk -> sparse_attn
+ *   Reindex = index_topk on the source cache -> sparse_attn
+ *   Reuse   = sparse_attn with the given idx/cnt */
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s);
+
+/* Static description of a status code. */
+const char* csa2_status_string(csa2_status st);
+
+/* Per-kernel device timing for measurement.  While a ring is installed for
+ * a kernel class, every launch of that class records hipEvent pairs
+ * start[count] / stop[count] on the launch stream around the kernel and
+ * increments count, until count reaches capacity.  Events are created and
+ * destroyed by the caller (hipEventCreate); the ring struct must outlive its
+ * installation.  Classes: 0 append, 1 indexer scan, 2 Top-K select,
+ * 3 attention.  Pass ring = NULL to uninstall.  Process-wide, not
+ * thread-safe: meant for benchmarks. */
+typedef struct {
+  hipEvent_t* start;     /* [capacity] */
+  hipEvent_t* stop;      /* [capacity] */
+  int32_t     capacity;
+  int32_t     count;     /* launches recorded so far */
+} csa2_timing_ring;
+
+#define CSA2_KCLASS_APPEND 0
+#define CSA2_KCLASS_SCAN   1
+#define CSA2_KCLASS_SELECT 2
+#define CSA2_KCLASS_ATTN   3
+#define CSA2_NUM_KCLASSES  4
+csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

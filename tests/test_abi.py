@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+
+import pytest
+
+from fp4_kv_cache_layer_amd import _lib as L
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libcsa2.so not built")
+
+FAKE = 0x100000          # aligned, never dereferenced: every call below fails validation or is a no-op
+
+
+def _view(**kw):
+    v = dict(kv=FAKE, idx_k=FAKE, page_table=FAKE, seq_lens=FAKE, num_pages=4, page_size=64, num_seqs=1, max_pages=4)
+    v.update(kw)
+    return L.CacheView(**v)
+
+
+def test_exports_every_header_function():
+    lib = L.load()
+    names = L.header_functions()
+    assert set(names) >= {"csa2_append_quant_fp4", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_step",
+                          "csa2_workspace_bytes", "csa2_workspace_init", "csa2_status_string", "csa2_set_timing"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = L.load()
+    for st in range(5):
+        assert lib.csa2_status_string(st)
+    assert lib.csa2_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    lib = L.load()
+    assert lib.csa2_workspace_bytes(L.CSA2_REUSE, 32, 65537, 8, 64, 512) == 0
+    full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
+    assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
+    assert full >= 32 * 65537 * 4 + 32 * 2048 * 4
+    assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
+
+
+def _topk(lib, view, **kw):
+    a = dict(q_idx=FAKE, w=FAKE, q_seq=FAKE, q_vis=FAKE, nq=1, h_idx=8, k=512, max_vis=200,
+             out_idx=FAKE, out_cnt=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.csa2_index_topk(ctypes.byref(view), a["q_idx"], a["w"], a["q_seq"], a["q_vis"], a["nq"], a["h_idx"],
+                               a["k"], a["max_vis"], a["out_idx"], a["out_cnt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(h_idx=0), dict(h_idx=17), dict(k=0), dict(k=2049), dict(nq=-1),
+                                dict(max_vis=-1), dict(max_vis=257), dict(q_idx=None), dict(w=None),
+                                dict(out_idx=None), dict(ws=None), dict(q_idx=FAKE + 8)])
+def test_index_topk_rejects(kw):
+    assert _topk(L.load(), _view(), **kw) == L.CSA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("vkw", [dict(page_size=48), dict(page_size=32), dict(page_size=0), dict(kv=None),
+                                 dict(page_table=None), dict(num_pages=0), dict(kv=FAKE + 4)])
+def test_cache_view_rejects(vkw):
+    assert _topk(L.load(), _view(**vkw)) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_index_topk_workspace_too_small_and_empty():
+    lib = L.load()
+    assert _topk(lib, _view(), ws_bytes=100) == L.CSA2_ERR_WORKSPACE
+    assert _topk(lib, _view(), nq=0, q_idx=None, ws=None) == L.CSA2_OK          # nothing enqueued
+
+
+def _attn(lib, view, **kw):
+    a = dict(q=FAKE, q_seq=FAKE, idx=FAKE, cnt=FAKE, nq=1, h=64, k=512, sm_scale=0.044, out=FAKE, lse=None)
+    a.update(kw)
+    return lib.csa2_sparse_attn(ctypes.byref(view), a["q"], a["q_seq"], a["idx"], a["cnt"], a["nq"], a["h"], a["k"],
+                                a["sm_scale"], a["out"], a["lse"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw", [dict(h=0), dict(h=129), dict(k=0), dict(sm_scale=0.0), dict(sm_scale=float("inf")),
+                                dict(sm_scale=-1.0), dict(q=None), dict(out=None), dict(out=FAKE + 4)])
+def test_sparse_attn_rejects(kw):
+    assert _attn(L.load(), _view(), **kw) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_append_rejects_and_empty():
+    lib = L.load()
+    v = _view()
+    assert lib.csa2_append_quant_fp4(ctypes.byref(v), FAKE, FAKE, FAKE, -1, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_append_quant_fp4(ctypes.byref(v), None, FAKE, FAKE, 3, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_append_quant_fp4(ctypes.byref(v), FAKE, FAKE + 2, FAKE, 3, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_append_quant_fp4(ctypes.byref(v), None, None, None, 0, None) == L.CSA2_OK
+
+
+def test_layer_step_mode_field_rules():
+    lib = L.load()
+    v = _view()
+    a = L.StepArgs()
+    a.cache = ctypes.pointer(v)
+    a.q, a.h, a.sm_scale, a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = FAKE, 64, 0.04, FAKE, FAKE, 1, 512, 100
+    a.idx, a.cnt, a.out = FAKE, FAKE, FAKE
+    assert lib.csa2_layer_step(7, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.q_idx = FAKE                                       # Reuse must not carry indexer inputs
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.q_idx, a.n_new, a.new_slots = None, 1, FAKE        # Reindex must not append
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.n_new, a.new_slots = 0, None
+    assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG   # Full needs q_idx/w/ws
+    a.nq = 0
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK              # nothing to do
+    assert lib.csa2_layer_step(L.CSA2_REUSE, None, None) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_set_timing_validation():
+    lib = L.load()
+    assert lib.csa2_set_timing(9, None) == L.CSA2_ERR_INVALID_ARG
+    r = L.TimingRing(None, None, 4, 0)
+    assert lib.csa2_set_timing(1, ctypes.byref(r)) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_set_timing(1, None) == L.CSA2_OK

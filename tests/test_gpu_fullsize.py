@@ -1,0 +1,89 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times, checked against the fp64 oracle on sampled queries (each sampled
+query is scored over its whole visible context by the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import csa2_oracle as O
+from tests.gpu_util import (LSE_RTOL, OUT_ATOL, OVERLAP_MIN, add_kv_rows, check_selection_valid, need_gpu,
+                            overlap_stats, say, single_seq_cache)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _check_sampled(spec, sample, exact=False):
+    from fp4_kv_cache_layer_amd import runner
+    say(f"[fullsize] {spec.name}: building ({spec.num_seqs} seqs, {sum(spec.cached)} cached entries)")
+    dc = runner.DeviceCase(spec, gen_device="cuda")
+    say(f"[fullsize] {spec.name}: running group {spec.modes}")
+    dc.run_group()
+    got = dc.results_host()
+    q_seq, q_vis = spec.q_seq(), spec.q_vis()
+    full_idx = got[0]["idx"]
+    inter = total = 0
+    for i in sample:
+        s, vis = int(q_seq[i]), int(q_vis[i])
+        say(f"  query {i} seq {s} vis {vis}")
+        cache = single_seq_cache(spec, s, vis, "cuda")
+        sel_rows = set()
+        for li, mode in enumerate(spec.modes):
+            g = got[li]
+            qi, w, q = (x.cpu().numpy() for x in dc.inputs[li])
+            if mode != O.REUSE:
+                sc = O.index_scores(cache, 0, vis, qi[i], w[i])
+                oi, oc = O.select_topk(sc, spec.k)
+                if exact:
+                    assert g["cnt"][i] == oc and np.array_equal(g["idx"][i], oi)
+                else:
+                    ov, _ = overlap_stats(g["idx"][i:i + 1], g["cnt"][i:i + 1], oi[None], [oc])
+                    say(f"    layer {li}: overlap {ov:.5f}")
+                    inter += round(ov * oc)
+                    total += oc
+                    check_selection_valid(g["idx"][i], g["cnt"][i], oi, oc, sc, spec.k)
+            else:
+                assert np.array_equal(g["idx"][i], full_idx[i])
+            sel_rows |= set(g["idx"][i, :g["cnt"][i]].tolist())
+        add_kv_rows(cache, spec, s, sel_rows, "cuda")
+        for li, mode in enumerate(spec.modes):
+            g = got[li]
+            q = dc.inputs[li][2].cpu().numpy().view(np.uint16)
+            o, lse = O.attend(cache, 0, q[i], g["idx"][i], int(g["cnt"][i]), spec.sm_scale)
+            err = np.abs(g["out"][i] - o).max()
+            lerr = np.max(np.abs(g["lse"][i] - lse) / np.maximum(1, np.abs(lse)))
+            say(f"    layer {li}: max|dO| {err:.2e} lse rel {lerr:.1e}")
+            assert err <= OUT_ATOL and lerr <= LSE_RTOL
+    if total:
+        say(f"  aggregate overlap {inter / total:.6f}")
+        assert inter / total >= OVERLAP_MIN
+    del dc
+    torch.cuda.empty_cache()
+
+
+def test_config1_decode_b32_64k_group():
+    _check_sampled(W.config(1), sample=[0, 17, 31])
+
+
+def test_config1_integer_exact():
+    _check_sampled(W.config(1, integer_indexer=True), sample=[5, 30], exact=True)
+
+
+def test_config2_prefill_sampled_rows():
+    _check_sampled(W.config(2), sample=[0, 1, 2047, 4095])
+
+
+def test_config3_decode_1m():
+    _check_sampled(W.config(3), sample=[0, 7])
+
+
+def test_config4_ragged_paged():
+    spec = W.config(4)
+    lens = np.array(spec.cached)
+    sample = sorted({int(lens.argmin()), int(lens.argmax()), int(np.argsort(lens)[len(lens) // 2])})
+    _check_sampled(spec, sample=sample)

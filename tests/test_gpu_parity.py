@@ -1,0 +1,263 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small cases span several tiles and ragged tails; every input is drawn on the
+host by the shared seeded generators so both sides see the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import csa2_oracle as O
+from tests import casebuild as CB
+from tests.gpu_util import (LSE_RTOL, OUT_ATOL, OVERLAP_MIN, check_selection_valid, need_gpu, overlap_stats, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _ops():
+    from fp4_kv_cache_layer_amd import ops, runner
+    return ops, runner
+
+
+# ---------------------------------------------------------------------------
+# quantize-on-append: bit-exact bytes
+# ---------------------------------------------------------------------------
+
+def _finite_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = O.bf16_to_f64(bits)
+    return bits[np.isfinite(x)]
+
+
+@pytest.mark.parametrize("arrangement", ["shuffled", "sorted", "alone"])
+def test_append_bit_exact_every_bf16(arrangement):
+    ops, _ = _ops()
+    say(f"[append] every finite bf16, {arrangement}")
+    pats = _finite_bf16_patterns()
+    rng = np.random.default_rng(3)
+    if arrangement == "shuffled":
+        pats = rng.permutation(pats)
+    elif arrangement == "alone":
+        # each value leads a block of tiny companions, so it sets the block scale alone
+        blocks = np.full((pats.size, 32), 0x0001, dtype=np.uint16)
+        blocks[:, 0] = pats
+        blocks[:, 1::2] |= 0x8000
+        pats = blocks.reshape(-1)
+    n = (pats.size + 511) // 512
+    kv = np.zeros(n * 512, dtype=np.uint16)
+    kv[:pats.size] = pats
+    kv = kv.reshape(n, 512)
+    ik = np.resize(pats, n * 128).reshape(n, 128)
+    ps = 64
+    npg = (n + ps - 1) // ps + 1
+    cache = ops.Cache(npg, ps, torch.arange(npg, dtype=torch.int32)[None])
+    slots = torch.from_numpy(np.random.default_rng(4).permutation(npg * ps)[:n].astype(np.int32)).cuda()
+    ops.csa2_append_quant_fp4(cache, slots, torch.from_numpy(kv.view(np.int16)).cuda(),
+                              torch.from_numpy(ik.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    got_kv = cache.kv.reshape(-1, 272)[slots.long()].cpu().numpy()
+    got_ik = cache.idx_k.reshape(-1, 128)[slots.long()].cpu().numpy()
+    want_kv = O.quantize_kv_rows(O.bf16_to_f64(kv))
+    want_ik = O.quantize_idxk_rows(O.bf16_to_f64(ik))
+    bad = np.nonzero((got_kv != want_kv).any(1))[0]
+    assert bad.size == 0, f"{bad.size} kv rows differ; first {bad[:3]}"
+    assert np.array_equal(got_ik, want_ik)
+
+
+# ---------------------------------------------------------------------------
+# indexer + Top-K
+# ---------------------------------------------------------------------------
+
+def _run_case(spec):
+    _, runner = _ops()
+    dc = runner.DeviceCase(spec, gen_device="cpu")
+    dc.run_group()
+    return dc, dc.results_host()
+
+
+def _compare_group(spec, exact_topk: bool):
+    say(f"[group] {spec.name} seed={spec.seed} seqs={spec.num_seqs} cached={spec.cached[:6]} "
+        f"n_new={spec.n_new} h_idx={spec.h_idx} h={spec.h} k={spec.k} int={spec.integer_indexer}")
+    dc, got = _run_case(spec)
+    case = CB.build(spec)
+    ref = CB.run_group(case)
+    # oracle cache after the Full layer's append, to evaluate attention over the GPU's selection
+    ocache = case.fresh_cache()
+    if case.new_slots.size:
+        O.append_quant_fp4(ocache, case.new_slots, case.new_kv, case.new_ik)
+    q_seq, q_vis = spec.q_seq(), spec.q_vis()
+    for li, (g, r, L) in enumerate(zip(got, ref, case.layers)):
+        if L.mode != O.REUSE:
+            if exact_topk:
+                assert np.array_equal(g["cnt"], r["cnt"]), f"layer {li} cnt"
+                bad = np.nonzero((g["idx"] != r["idx"]).any(1))[0]
+                assert bad.size == 0, f"layer {li}: {bad.size} queries differ, first {bad[:3]}"
+            else:
+                ov, worst = overlap_stats(g["idx"], g["cnt"], r["idx"], r["cnt"])
+                say(f"  layer {li} overlap {ov:.6f} worst {worst:.4f}")
+                assert ov >= OVERLAP_MIN
+                for i in range(spec.nq):
+                    sc = O.index_scores(ocache, int(q_seq[i]), int(q_vis[i]), L.q_idx[i], L.w[i])
+                    check_selection_valid(g["idx"][i], g["cnt"][i], r["idx"][i], r["cnt"][i], sc, spec.k)
+        else:
+            assert np.array_equal(g["idx"], got[0]["idx"])
+        o_ref, lse_ref = O.sparse_attn(ocache, L.q, q_seq, g["idx"], g["cnt"], spec.sm_scale)
+        err = np.abs(g["out"] - o_ref).max()
+        say(f"  layer {li} mode {L.mode}: max|dO| {err:.2e}")
+        assert err <= OUT_ATOL
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(g["lse"]), fin)
+        lerr = np.abs(g["lse"][fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+        assert lerr.size == 0 or lerr.max() <= LSE_RTOL, lerr.max()
+    return dc, got, ref
+
+
+@pytest.mark.parametrize("seed,cached,h_idx,k", [
+    (21, [4096], 4, 512),
+    (22, [600, 37, 2048 + 5, 5000, 511, 0, 1], 8, 512),
+    (23, [3000, 777], 16, 64),
+    (24, [2500, 130], 1, 128),
+    (25, [9000], 8, 2048),
+])
+def test_group_integer_exact(seed, cached, h_idx, k):
+    spec = W.small_case("int_group", seed, cached, n_new=1, h_idx=h_idx, h=16, k=k, integer_indexer=True)
+    _compare_group(spec, exact_topk=True)
+
+
+@pytest.mark.parametrize("seed,cached,h", [
+    (31, [4096, 1500, 700], 64),
+    (32, [3000, 200], 24),
+    (33, [2100], 128),
+])
+def test_group_gaussian(seed, cached, h):
+    spec = W.small_case("gauss_group", seed, cached, n_new=1, h_idx=8, h=h, k=512, integer_indexer=False)
+    _compare_group(spec, exact_topk=False)
+
+
+def test_config0_exact():
+    spec = W.config(0)
+    _compare_group(spec, exact_topk=True)
+
+
+def test_prefill_small_causal():
+    spec = W.small_case("prefill", 41, [1500], n_new=300, h_idx=8, h=32, k=256, modes=(O.FULL,), prefill=True,
+                        integer_indexer=True)
+    _compare_group(spec, exact_topk=True)
+
+
+def test_all_equal_scores_take_lowest_indices():
+    """Zero indexer queries make every score 0: the first k entries win,
+    including the long-tie path (more tied keys than the select kernel parks)."""
+    ops, runner = _ops()
+    for cached in ([20000], [300, 13000]):
+        spec = W.small_case("ties", 51, cached, n_new=1, h_idx=4, h=16, k=512, modes=(O.FULL,), integer_indexer=True)
+        say(f"[ties] cached={cached}")
+        dc = runner.DeviceCase(spec, gen_device="cpu")
+        dc.inputs[0][0].zero_()
+        dc.run_group()
+        got = dc.results_host()[0]
+        for i, s in enumerate(spec.q_seq()):
+            v = spec.seq_len_after(int(s))
+            kp = min(512, v)
+            assert got["cnt"][i] == kp
+            assert list(got["idx"][i, :kp]) == list(range(kp))
+
+
+def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
+    spec = W.small_case("repeat", 61, [3000, 900], n_new=1, h_idx=8, h=16, k=512)
+    _, runner = _ops()
+    dc = runner.DeviceCase(spec, gen_device="cpu")
+    dc.run_group()
+    a = dc.results_host()
+    for _ in range(3):
+        dc.run_group()
+    b = dc.results_host()
+    for x, y in zip(a, b):
+        for key in ("idx", "cnt", "out", "lse"):
+            assert np.array_equal(x[key], y[key]), key
+    assert int(dc.ws[: 2 * 2048 * 4].view(torch.int32).abs().sum().item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# attention alone, on chosen selections
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h,cnts", [(16, [0, 1, 17, 512]), (64, [512, 300]), (40, [33, 512]), (128, [511])])
+def test_sparse_attn_given_selection(h, cnts):
+    ops, _ = _ops()
+    say(f"[attn] h={h} cnts={cnts}")
+    rng = np.random.default_rng(h)
+    n, ps = 3000, 64
+    npg = (n + ps - 1) // ps
+    perm = rng.permutation(npg).astype(np.int32)
+    cache = ops.Cache(npg, ps, torch.from_numpy(perm[None]))
+    ocache = O.Cache.empty(npg, ps, perm[None], [n])
+    kv = (rng.standard_normal((n, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kv[5] = 0                                              # an all-zero row
+    kv[6, :32] = 0x0001                                    # a subnormal block
+    ik = np.zeros((n, 128), dtype=np.uint16)
+    t = np.arange(n)
+    slots = (perm[t // ps].astype(np.int64) * ps + t % ps).astype(np.int32)
+    ops.csa2_append_quant_fp4(cache, torch.from_numpy(slots).cuda(), torch.from_numpy(kv.view(np.int16)).cuda(),
+                              torch.from_numpy(ik.view(np.int16)).cuda())
+    O.append_quant_fp4(ocache, slots, kv, ik)
+    k = 512
+    nq = len(cnts)
+    idx = np.full((nq, k), -1, dtype=np.int32)
+    for i, c in enumerate(cnts):
+        sel = np.sort(rng.choice(n, c, replace=False))
+        if c >= 7:
+            sel[:2] = [5, 6]
+            sel = np.sort(sel)
+        idx[i, :c] = sel
+    q = (rng.standard_normal((nq, h, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q_seq = np.zeros(nq, dtype=np.int32)
+    out, lse = ops.csa2_sparse_attn(cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda(),
+                                    torch.from_numpy(idx).cuda(), torch.tensor(cnts, dtype=torch.int32).cuda(),
+                                    1 / np.sqrt(512))
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = O.sparse_attn(ocache, q, q_seq, idx, np.array(cnts), 1 / np.sqrt(512))
+    err = np.abs(out - o_ref).max()
+    say(f"  max|dO| {err:.2e}")
+    assert err <= OUT_ATOL
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert (np.abs(lse[fin] - lse_ref[fin]) <= LSE_RTOL * np.maximum(1, np.abs(lse_ref[fin]))).all()
+    for i, c in enumerate(cnts):
+        if c == 0:
+            assert (out[i] == 0).all()
+
+
+def test_peaked_softmax_stays_within_tolerance():
+    """Large logits make a near one-hot softmax, the worst case for rounding
+    the probabilities before the P.V product."""
+    ops, _ = _ops()
+    rng = np.random.default_rng(77)
+    n, ps, h = 600, 64, 16
+    npg = (n + ps - 1) // ps
+    cache = ops.Cache(npg, ps, torch.arange(npg, dtype=torch.int32)[None])
+    ocache = O.Cache.empty(npg, ps, np.arange(npg, dtype=np.int32)[None], [n])
+    kv = (rng.standard_normal((n, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ik = np.zeros((n, 128), dtype=np.uint16)
+    slots = np.arange(n, dtype=np.int32)
+    ops.csa2_append_quant_fp4(cache, torch.from_numpy(slots).cuda(), torch.from_numpy(kv.view(np.int16)).cuda(),
+                              torch.from_numpy(ik.view(np.int16)).cuda())
+    O.append_quant_fp4(ocache, slots, kv, ik)
+    x = O.dequantize_kv_rows(ocache.kv.reshape(-1, 272)[:n])
+    idx = np.sort(rng.choice(n, 512, replace=False)).astype(np.int32)[None]
+    q32 = (x[idx[0, 10]] * 4.0)[None, None, :].repeat(h, 1).astype(np.float32)   # aligned with one row
+    q32 *= np.linspace(0.2, 3.0, h, dtype=np.float32)[None, :, None]
+    q = (q32.view(np.uint32) >> 16).astype(np.uint16)
+    out, lse = ops.csa2_sparse_attn(cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.zeros(1, dtype=torch.int32).cuda(),
+                                    torch.from_numpy(idx).cuda(), torch.tensor([512], dtype=torch.int32).cuda(),
+                                    1 / np.sqrt(512))
+    o_ref, lse_ref = O.sparse_attn(ocache, q, [0], idx, [512], 1 / np.sqrt(512))
+    err = np.abs(out.cpu().numpy() - o_ref).max()
+    say(f"[attn peaked] max|dO| {err:.2e}")
+    assert err <= OUT_ATOL
