@@ -1,0 +1,200 @@
+"""CSA2 decode benchmark on one MI355X.
+
+One step = one CSA2 layer group (Full, Reindex, Reuse, Reuse) over a batch of
+32 decode sequences with 65,536 cached entries each plus one entry appended
+by quantize-on-append (indexer 8 x 128 FP8, 64 heads over the 512-wide FP4
+latent, Top-512).  Inputs are synthetic, seeded, and already resident in HBM
+when timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA2 decode tokens/s (B=32, 64K ctx) + % of HBM roofline"
+
+
+def scan_bytes(spec) -> int:
+    """Algorithmic bytes of one indexer-scan launch: every visible indexer-K
+    row (128 B) of every query, plus each query's indexer query (h_idx x 128 B)
+    and head weights (h_idx x 4 B)."""
+    vis = spec.q_vis()
+    return int(vis.sum()) * 128 + spec.nq * spec.h_idx * (128 + 4)
+
+
+def cpu_baseline(spec, dc, budget_s: float = 12.0):
+    """The fp64 oracle timed on this host on a bounded sample of the same
+    workload: whole layer groups for a few sequences, repeated until the
+    budget is spent.  Cache encoding is set-up, outside the timing, as the
+    GPU's resident cache is."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import csa2_oracle as O
+
+    seqs = [0, 1]
+    caches = {}
+    for s in seqs:
+        vis = spec.seq_len_after(s)
+        ps = 64
+        npg = (vis + ps - 1) // ps
+        cache = O.Cache.empty(npg, ps, np.arange(npg, dtype=np.int32)[None], [vis])
+        c = spec.cached[s]
+        kv = W.kv_rows(spec, s, "cuda").cpu().numpy().view(np.uint16)
+        ik = W.idxk_rows(spec, s, "cuda").cpu().numpy().view(np.uint16)
+        O.append_quant_fp4(cache, np.arange(c), kv[:c], ik[:c])
+        caches[s] = (cache, kv[c:c + spec.n_new], ik[c:c + spec.n_new], c)
+    layer_in = [tuple(x.cpu().numpy() for x in li) for li in dc.inputs]
+    tokens = 0
+    t0 = time.perf_counter()
+    while True:
+        for s in seqs:
+            cache, nkv, nik, c = caches[s]
+            idx = cnt = None
+            for li, mode in enumerate(spec.modes):
+                qi, w, q = layer_in[li]
+                args = dict(q_idx=qi[s:s + 1], w=w[s:s + 1]) if mode != O.REUSE else dict(idx=idx, cnt=cnt)
+                if mode == O.FULL:
+                    args.update(new_slots=np.arange(c, c + spec.n_new), new_kv=nkv, new_idxk=nik)
+                i2, c2, _, _ = O.layer_step(mode, cache, q[s:s + 1].view(np.uint16), [0], [spec.seq_len_after(s)],
+                                            spec.k, spec.sm_scale, **args)
+                if mode == O.FULL:
+                    idx, cnt = i2, c2
+            tokens += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()]
+    cores = max(blas) if blas else 1
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(seqs)} of {spec.num_seqs} sequences x full 4-layer group, {tokens} sequence-steps "
+                      f"in {el:.1f} s (fp64 NumPy, host cores {len(os.sched_getaffinity(0))})"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "scan_traffic.json"),
+                    help="HBM traffic per scan launch measured with rocprofv3 counters (optional)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from fp4_kv_cache_layer_amd import ops, runner
+    from fp4_kv_cache_layer_amd import _lib as L
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    spec = W.config(args.config)
+    print(f"[bench] building {spec.name}", file=sys.stderr, flush=True)
+    dc = runner.DeviceCase(spec, gen_device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        dc.run_group()
+    torch.cuda.synchronize()
+
+    # timed region without event hooks
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # timed region with per-kernel device events (dominant kernel: indexer scan)
+    n_scan = sum(1 for m in spec.modes if m != ops.REUSE)
+    n_attn = len(spec.modes)
+    rings = {L.KCLASS_SCAN: ops.TimingRing(L.KCLASS_SCAN, args.steps * n_scan),
+             L.KCLASS_SELECT: ops.TimingRing(L.KCLASS_SELECT, args.steps * n_scan),
+             L.KCLASS_ATTN: ops.TimingRing(L.KCLASS_ATTN, args.steps * n_attn),
+             L.KCLASS_APPEND: ops.TimingRing(L.KCLASS_APPEND, args.steps)}
+    for r in rings.values():
+        r.install()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ms_events = (time.perf_counter() - t0) * 1e3 / args.steps
+    for r in rings.values():
+        r.uninstall()
+    dur = {k: r.durations_ms() for k, r in rings.items()}
+
+    ms = ms_events
+    value = spec.num_seqs * spec.n_new / (ms / 1e3) if spec.n_new else spec.nq / (ms / 1e3)
+    scan_ms = dur[L.KCLASS_SCAN]
+    scan_avg = statistics.mean(scan_ms)
+    sbytes = scan_bytes(spec)
+    achieved = sbytes / (scan_avg / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic))
+            if tr.get("workload") == spec.name:
+                traffic = tr.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    def avg(xs):
+        return round(statistics.mean(xs) * 1e3, 2) if xs else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "global_batch": spec.num_seqs, "seq_len": spec.cached[0] + spec.n_new,
+                   "modes": "full,reindex,reuse,reuse", "topk": spec.k, "heads": spec.h, "indexer_heads": spec.h_idx,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "index_scan_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": sbytes, "avg_launch_us": round(scan_avg * 1e3, 2)},
+        "kernels_avg_us": {"append": avg(dur[L.KCLASS_APPEND]), "scan_full": avg(scan_ms[0::n_scan]),
+                           "scan_reindex": avg(scan_ms[1::n_scan]) if n_scan > 1 else None,
+                           "select": avg(dur[L.KCLASS_SELECT]), "attn": avg(dur[L.KCLASS_ATTN])},
+        "ms_per_step_no_events": round(ms_plain, 5),
+        "group_hbm_frac": None,
+    }
+    # whole-group algorithmic bytes: scans + gathered rows + Q + O + LSE + append
+    attn_b = spec.nq * (spec.k * 272 + spec.h * 512 * 2 + spec.h * 512 * 4 + spec.h * 4 + spec.k * 4)
+    group_b = n_scan * sbytes + n_attn * attn_b + spec.num_seqs * spec.n_new * (1024 + 256 + 272 + 128 + 4)
+    out["group_hbm_frac"] = round(group_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(spec, dc)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

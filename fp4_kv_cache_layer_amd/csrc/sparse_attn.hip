@@ -65,7 +65,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
                    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int h, int k,
                    float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kAttnWaves * kWaveLds];
-  __shared__ float stat_m[kAttnWaves][16], stat_l[kAttnWaves][16], stat_le[kAttnWaves][16];
+  __shared__ float stat_m[kAttnWaves][16], stat_l[kAttnWaves][16];
 
   const int ngroups = (h + 15) >> 4;
   const int qi = blockIdx.x / ngroups;
@@ -90,7 +90,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   floatx4 oacc[32];
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f, le_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
 
   uint8_t* my = lds + wave * kWaveLds;
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
@@ -154,13 +154,13 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     float alpha = 1.0f;
-    float psum = 0.0f, psum_b = 0.0f;
-    float pb[2][4];
+    float psum = 0.0f;
+    float phi[2][4], plo[2][4];                         // p = phi + plo, both bf16
     if (m_new == -INFINITY) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb[mt][i] = 0.0f;
+        for (int i = 0; i < 4; ++i) phi[mt][i] = plo[mt][i] = 0.0f;
     } else {
       alpha = __expf(m_run - m_new);                    // m_run = -inf -> 0
 #pragma unroll
@@ -169,16 +169,13 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
         for (int i = 0; i < 4; ++i) {
           const float p = __expf(v[mt][i] - m_new);     // -inf -> 0
           psum += p;
-          pb[mt][i] = bf16_round(p);
-          psum_b += pb[mt][i];
+          phi[mt][i] = bf16_round(p);
+          plo[mt][i] = bf16_round(p - phi[mt][i]);
         }
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    psum_b += __shfl_xor(psum_b, 16);
-    psum_b += __shfl_xor(psum_b, 32);
-    l_run = l_run * alpha + psum_b;
-    le_run = le_run * alpha + psum;
+    l_run = l_run * alpha + psum;
     m_run = m_new;
     // O rows are heads 4g+i: fetch their alpha from lane 4g+i
     {
@@ -195,12 +192,13 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
           for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
       }
     }
-    // ---- O += P X ----
-    bf16x8 pa;
+    // ---- O += P X, with P split into two bf16 terms (hi + lo) ----
+    bf16x8 pa_hi, pa_lo;
     {
-      const uint32_t w0 = pack_bf16x2(pb[0][0], pb[0][1]), w1 = pack_bf16x2(pb[0][2], pb[0][3]);
-      const uint32_t w2 = pack_bf16x2(pb[1][0], pb[1][1]), w3 = pack_bf16x2(pb[1][2], pb[1][3]);
-      pa = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+      pa_hi = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(phi[0][0], phi[0][1]), pack_bf16x2(phi[0][2], phi[0][3]),
+                                                    pack_bf16x2(phi[1][0], phi[1][1]), pack_bf16x2(phi[1][2], phi[1][3])));
+      pa_lo = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(plo[0][0], plo[0][1]), pack_bf16x2(plo[0][2], plo[0][3]),
+                                                    pack_bf16x2(plo[1][0], plo[1][1]), pack_bf16x2(plo[1][2], plo[1][3])));
     }
     // make this wave's LDS writes visible to its own transposing reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -215,7 +213,9 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       const shortx4 x8lo = lo, x8hi = hi;
       typedef short shortx8 __attribute__((ext_vector_type(8)));
       const shortx8 b8 = {x8lo[0], x8lo[1], x8lo[2], x8lo[3], x8hi[0], x8hi[1], x8hi[2], x8hi[3]};
-      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, b8), oacc[nt], 0, 0, 0);
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, b8);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb, oacc[nt], 0, 0, 0);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb, oacc[nt], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -223,7 +223,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   }
 
   // ---- merge the four waves ----
-  if (g == 0) { stat_m[wave][r] = m_run; stat_l[wave][r] = l_run; stat_le[wave][r] = le_run; }
+  if (g == 0) { stat_m[wave][r] = m_run; stat_l[wave][r] = l_run; }
   __syncthreads();
   float* red = reinterpret_cast<float*>(lds);          // [wave][16 heads][512] fp32 = 32 KB per wave
   {
@@ -266,7 +266,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       for (int w2 = 0; w2 < kAttnWaves; ++w2) M = fmaxf(M, stat_m[w2][tid]);
       float Le = 0.0f;
       for (int w2 = 0; w2 < kAttnWaves; ++w2)
-        if (M != -INFINITY && stat_m[w2][tid] != -INFINITY) Le += __expf(stat_m[w2][tid] - M) * stat_le[w2][tid];
+        if (M != -INFINITY && stat_m[w2][tid] != -INFINITY) Le += __expf(stat_m[w2][tid] - M) * stat_l[w2][tid];
       lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(Le);
     }
   }

@@ -188,7 +188,7 @@ def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
 # attention alone, on chosen selections
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("h,cnts", [(16, [0, 1, 17, 512]), (64, [512, 300]), (40, [33, 512]), (128, [511])])
+@pytest.mark.parametrize("h,cnts", [(16, [0, 1, 2, 3, 17, 512]), (64, [512, 300, 2]), (40, [33, 512]), (128, [511, 5])])
 def test_sparse_attn_given_selection(h, cnts):
     ops, _ = _ops()
     say(f"[attn] h={h} cnts={cnts}")
