@@ -70,7 +70,7 @@ csa2_status validate_index(const csa2_cache_view* c, const uint8_t* q_idx, const
   if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(q_seq, 4) || !aligned(q_vis, 4) ||
       !aligned(out_idx, 16) || !aligned(out_cnt, 4) || !aligned(ws, 16))
     return CSA2_ERR_INVALID_ARG;
-  if (ws_bytes < index_ws_bytes(nq, max_vis)) return CSA2_ERR_WORKSPACE;
+  if (ws_bytes < zero_state_bytes(nq) + index_score_bytes(nq, max_vis)) return CSA2_ERR_WORKSPACE;
   return CSA2_OK;
 }
 
@@ -100,17 +100,27 @@ csa2_status validate_append(const csa2_cache_view* c, const int32_t* slots, cons
   return CSA2_OK;
 }
 
+IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
+  IndexWs r;
+  uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  r.hist = reinterpret_cast<uint32_t*>(p);
+  r.cand_cnt = reinterpret_cast<uint32_t*>(p + (size_t)nq * kHistBins * 4);
+  r.vstride = index_vstride(max_vis);
+  r.scores = reinterpret_cast<float*>(p + score_off);
+  r.cand = reinterpret_cast<int32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
+  return r;
+}
+
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
-                      int32_t* out_cnt, void* ws, hipStream_t s) {
-  const IndexWs iw = index_ws_carve(ws, nq, max_vis);
+                      int32_t* out_cnt, const IndexWs& iw, hipStream_t s) {
   if (max_vis > 0) {
     TimedLaunch t(CSA2_KCLASS_SCAN, s);
     csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s));
     if (st != CSA2_OK) return st;
   }
   TimedLaunch t(CSA2_KCLASS_SELECT, s);
-  return hip_status(launch_topk_select(iw, q_vis, nq, k, out_idx, out_cnt, s));
+  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s));
 }
 
 }  // namespace
@@ -137,10 +147,10 @@ csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring) {
 }
 
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
-  (void)h_idx; (void)h; (void)k;
-  if (nq <= 0 || max_vis < 0) return 0;
-  if (mode == CSA2_REUSE) return 0;
-  return index_ws_bytes(nq, max_vis);
+  (void)h_idx; (void)k;
+  (void)h;
+  if (nq <= 0 || max_vis < 0 || mode == CSA2_REUSE) return 0;
+  return zero_state_bytes(nq) + index_score_bytes(nq, max_vis);
 }
 
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
@@ -164,16 +174,17 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
   CacheArgs ca;
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
-  return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, s);
+  return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), s);
 }
 
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                              const int32_t* cnt, int32_t nq, int32_t h, int32_t k, float sm_scale, float* out,
                              float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
-  (void)ws; (void)ws_bytes;
   CacheArgs ca;
   csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
   if (st != CSA2_OK || nq == 0) return st;
+  (void)ws; (void)ws_bytes;
   TimedLaunch t(CSA2_KCLASS_ATTN, s);
   return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, s));
 }
@@ -205,7 +216,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
   }
   if (a->nq == 0) return CSA2_OK;
   if (mode != CSA2_REUSE) {
-    st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt, a->ws, s);
+    st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt,
+                   index_ws(a->ws, a->nq, a->max_vis, zero_state_bytes(a->nq)), s);
     if (st != CSA2_OK) return st;
   }
   TimedLaunch t(CSA2_KCLASS_ATTN, s);

@@ -22,8 +22,6 @@ constexpr int kLatent = 512;
 constexpr int kIndexDim = 128;
 constexpr int kKvRowBytes = 272;
 constexpr int kCodeBytes = 256;
-constexpr int kHistBits = 11;                 // first radix digit of the score key
-constexpr int kHistBins = 1 << kHistBits;
 
 // ---------------------------------------------------------------------------
 // E8M0 block exponent: the smallest integer e with amax <= 6 * 2^e, read off
@@ -79,6 +77,15 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // E8M0 byte -> fp32 scale 2^(b-127); byte 0 is the subnormal 2^-127.
 __device__ __forceinline__ float e8m0_to_float(uint32_t b) {
   return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// Workgroup barrier that orders LDS only.  A plain __syncthreads() also
+// waits for every global load in flight, which would drain prefetched data
+// at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Physical row of logical entry t of a sequence: page table lookup.

@@ -24,17 +24,11 @@ constexpr int kScanUnroll = 4;          // 16-entry tiles in flight per wave
 
 int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 63) / 64 * 64; }
 
-size_t index_ws_bytes(int32_t nq, int32_t max_vis) {
-  return (size_t)nq * kHistBins * 4 + (size_t)nq * (size_t)index_vstride(max_vis) * 4;
+size_t zero_state_bytes(int32_t nq) {
+  return ((size_t)nq * (kHistBins + 1) * 4 + 255) / 256 * 256;
 }
 
-IndexWs index_ws_carve(void* ws, int32_t nq, int32_t max_vis) {
-  IndexWs r;
-  r.hist = reinterpret_cast<uint32_t*>(ws);
-  r.scores = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + (size_t)nq * kHistBins * 4);
-  r.vstride = index_vstride(max_vis);
-  return r;
-}
+size_t index_score_bytes(int32_t nq, int32_t max_vis) { return 2 * (size_t)nq * (size_t)index_vstride(max_vis) * 4; }
 
 __global__ void __launch_bounds__(kScanWaves * 64)
 index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -62,33 +56,46 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 #pragma unroll
   for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < h_idx) ? w[(int64_t)q * h_idx + 4 * g + i] : 0.0f;
 
+  // Page ids of this chunk (at most kScanChunk / CSA2_MIN_PAGE_SIZE = 32),
+  // one per lane; a tile's page is then a lane read with a uniform index, so
+  // no load waits on a page-table load.
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
+  const int pg0 = t0 >> c.lg_page;
+  const int npg = ((t1 - 1) >> c.lg_page) - pg0 + 1;
+  const int page_of_lane = lane < npg ? pt_row[pg0 + lane] : 0;
   float* srow = ws.scores + (int64_t)q * ws.vstride;
   const int ntiles = (t1 - t0 + 15) >> 4;
-  __syncthreads();
+  lds_barrier();
 
-  for (int base = wave * kScanUnroll; base < ntiles; base += kScanWaves * kScanUnroll) {
-    intx8 b[kScanUnroll];
+  // Tiles j = base + u of this wave; the next group of tiles is loaded while
+  // the current one goes through the matrix core and the epilogue.
+  // Loads are unconditional (a tile past the end re-reads the last tile and
+  // is ignored) so the compiler can count loads in flight instead of waiting
+  // for all of them.
+  auto load = [&](int base, intx8 (&b)[kScanUnroll]) {
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
-      const int j = base + u;
-      if (j < ntiles) {
-        const int t = t0 + 16 * j + r;                // same page as the tile start (< vis)
-        const int64_t row = entry_row(pt_row, t0 + 16 * j, c.lg_page) + r;
-        const intx4* src = reinterpret_cast<const intx4*>(c.idx_k + row * kIndexDim + 32 * g);
-        const intx4 lo = src[0], hi = src[1];
-        b[u] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        (void)t;
-      } else {
-        b[u] = intx8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const int j = min(base + u, ntiles - 1);
+      // rows t0+16j .. +15 share the tile start's page (tiles never straddle pages)
+      const int ts = t0 + 16 * j;
+      const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
+      const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
+      const intx4* src = reinterpret_cast<const intx4*>(c.idx_k + row * kIndexDim + 32 * g);
+      const intx4 lo = src[0], hi = src[1];
+      b[u] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+  };
+  constexpr int kStride = kScanWaves * kScanUnroll;
+  intx8 cur[kScanUnroll], nxt[kScanUnroll];
+  load(wave * kScanUnroll, cur);
+  for (int base = wave * kScanUnroll; base < ntiles; base += kStride) {
+    load(base + kStride, nxt);
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int j = base + u;
       if (j >= ntiles) break;
       floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[u], acc, 0, 0, 0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, cur[u], acc, 0, 0, 0, 0, 0, 0);
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.0f);
@@ -102,8 +109,10 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
         atomicAdd(&hist[score_key(__uint_as_float(u32)) >> (32 - kHistBits)], 1u);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) cur[u] = nxt[u];
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
   for (int i = tid; i < kHistBins; i += kScanWaves * 64) {
     const uint32_t v = hist[i];

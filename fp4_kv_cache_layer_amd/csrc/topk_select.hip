@@ -8,16 +8,22 @@
 //
 // Every entry gets the unique 64-bit key C = (orderable score << 32) |
 // (0xFFFFFFFF - index), so "score descending, index ascending" is "C
-// descending" and no two entries tie.  One 1024-thread workgroup per query:
-//   1. the scan already histogrammed the top 11 bits of C; a block scan over
-//      that histogram fixes the 11-bit prefix P that holds the k-th key;
-//   2. while more than kTieCap keys share the prefix (only for heavily tied
-//      inputs), one more pass over the scores histograms the next digit;
-//   3. one pass over the scores takes every entry whose prefix is above P and
-//      parks the entries equal to P in LDS;
-//   4. radix refinement of the parked keys in LDS finishes the selection;
-//   5. a bitonic sort puts the chosen indices in ascending order.
-// The histogram rows the scan filled are zeroed here, ready for the next call.
+// descending" and no two entries tie.  The indexer scan has already
+// histogrammed the top 11 bits of every key; a block scan over that histogram
+// fixes the 11-bit prefix P holding the k-th key.  Then:
+//
+//  collect (one workgroup per 8K-entry slice of a query, so the score pass is
+//          spread over the whole chip): every entry whose score reaches the
+//          lowest score of prefix P is appended to an LDS list, which is
+//          copied to the query's candidate list after one global atomic
+//          reserves its place;
+//  final   (one workgroup per query): candidates above P are selected, those
+//          equal to P are parked in LDS and refined digit by digit (heavily
+//          tied inputs first refine over the candidate list in global memory),
+//          the chosen indices are marked in an LDS bitmap over the context
+//          and written in index order by a block-wide prefix count (a bitonic
+//          sort when the context is too long for the bitmap).  It leaves the
+//          query's histogram row and candidate counter zeroed for the next call.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -25,183 +31,314 @@ namespace csa2 {
 
 namespace {
 
+constexpr int kSelCap = 2048;
+constexpr int kCollectThreads = 256;
+
 __device__ __forceinline__ uint64_t composite(float s, int t) {
   return ((uint64_t)score_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
 }
 
-constexpr int CSA2_SEL_CAP = 2048;
+// Lowest float whose orderable key is >= key (scores are canonical: no -0, no NaN).
+__device__ __forceinline__ float key_floor_float(uint32_t key) {
+  if (key == 0) return -INFINITY;
+  const uint32_t bits = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(bits);
+}
 
-struct SelShared {
-  uint32_t h[kHistBins];
-  int32_t sel[CSA2_SEL_CAP];
-  uint64_t tie[kTieCap];
-  uint32_t wave_tot[kSelectThreads / 64];
-  int32_t dstar;
-  uint32_t above;
-  int32_t selcnt;
-  int32_t tiecnt;
-};
-
-// Given hist[0..nb) in LDS (nb <= 2048) and need >= 1, finds the largest digit
-// d* whose suffix count reaches need; returns d* and the count strictly above.
-__device__ void find_digit(SelShared& S, int nb, uint32_t need, int& dstar, uint32_t& above) {
+// Block-wide search over a descending-ordered histogram h[0..nb): the largest
+// digit d* whose suffix count reaches need (1 <= need <= total), and the count
+// strictly above it.  scratch holds NT/64 words; result[0..1] receives (d*, above).
+template <int NT>
+__device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* scratch, uint32_t* result) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // thread tid covers descending positions 2*tid, 2*tid+1 -> digits nb-1-2tid, nb-2-2tid
-  const int d0 = nb - 1 - 2 * tid, d1 = nb - 2 - 2 * tid;
-  const uint32_t v0 = d0 >= 0 ? S.h[d0] : 0u;
-  const uint32_t v1 = d1 >= 0 ? S.h[d1] : 0u;
-  uint32_t x = v0 + v1;
+  const int per = (nb + NT - 1) / NT;
+  // thread tid covers descending positions [tid*per, tid*per + per) = digits nb-1-pos
+  uint32_t mine = 0;
+  for (int p = tid * per; p < min(nb, tid * per + per); ++p) mine += h[nb - 1 - p];
+  uint32_t x = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) S.wave_tot[wave] = x;
-  __syncthreads();
-  uint32_t off = 0;
-  for (int i = 0; i < wave; ++i) off += S.wave_tot[i];
-  const uint32_t incl = x + off, excl = incl - v0 - v1;
-  if (d0 >= 0 && excl < need && need <= excl + v0) { S.dstar = d0; S.above = excl; }
-  if (d1 >= 0 && excl + v0 < need && need <= excl + v0 + v1) { S.dstar = d1; S.above = excl + v0; }
-  __syncthreads();
-  dstar = S.dstar;
-  above = S.above;
-  __syncthreads();
+  if (lane == 63) scratch[wave] = x;
+  lds_barrier();
+  uint32_t excl = x - mine;
+  for (int i = 0; i < wave; ++i) excl += scratch[i];
+  if (excl < need && need <= excl + mine) {
+    uint32_t run = excl;
+    for (int p = tid * per; p < min(nb, tid * per + per); ++p) {
+      const uint32_t v = h[nb - 1 - p];
+      if (need <= run + v) { result[0] = (uint32_t)(nb - 1 - p); result[1] = run; break; }
+      run += v;
+    }
+  }
+  lds_barrier();
+}
+
+// Appends value for every lane where flag holds, one atomic per wave.
+template <typename T>
+__device__ __forceinline__ void wave_append(bool flag, T value, int* counter, T* list, int cap) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(flag);
+  if (m == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(m);
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __builtin_popcountll(m));
+  base = __builtin_amdgcn_readlane(base, leader);
+  const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  if (flag && pos < cap) list[pos] = value;
 }
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// collect
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kCollectThreads)
+topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int nslices) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ int32_t list[kCollectSlice];             // this slice's candidates
+  __shared__ uint32_t scratch[kCollectThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ int count, base;
+  const int q = blockIdx.x / nslices;
+  const int slice = blockIdx.x - q * nslices;
+  const int V = q_vis[q];
+  const int t0 = slice * kCollectSlice;
+  if (V <= k || t0 >= V) return;                      // uniform
+  const int tid = threadIdx.x;
+  const int t1 = min(V, t0 + kCollectSlice);
+  // the histogram row first, then the slice's scores (indices clamped, entries past t1 ignored)
+  const uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
+  for (int i = tid; i < kHistBins; i += kCollectThreads) h[i] = gh[i];
+  constexpr int kPer = kCollectSlice / (4 * kCollectThreads);   // float4 loads per thread
+  const float4* sc4 = reinterpret_cast<const float4*>(ws.scores + (int64_t)q * ws.vstride + t0);
+  const int nvec = (t1 - t0 + 3) >> 2;
+  float4 v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) v[u] = sc4[min(u * kCollectThreads + tid, nvec - 1)];
+  if (tid == 0) count = 0;
+  lds_barrier();
+  find_digit<kCollectThreads>(h, kHistBins, (uint32_t)k, scratch, res);
+  const float floor_s = key_floor_float(res[0] << (32 - kHistBits));
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int vi = u * kCollectThreads + tid;
+    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = t0 + 4 * vi + c;
+      wave_append<int32_t>(t < t1 && e[c] >= floor_s, t, &count, list, kCollectSlice);
+    }
+  }
+  lds_barrier();
+  // one global reservation per workgroup, then a coalesced copy of the list
+  const int n = count;
+  if (n == 0) return;
+  if (tid == 0) base = atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
+  lds_barrier();
+  int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
+  for (int i = tid; i < n; i += kCollectThreads) cand[i] = list[i];
+}
+
+// ---------------------------------------------------------------------------
+// final
+// ---------------------------------------------------------------------------
+namespace {
+
+struct SelShared {
+  uint32_t h[kHistBins];
+  int32_t sel[kSelCap];
+  uint64_t tie[kTieCap];                        // parked keys; reused as the output bitmap
+  uint32_t scratch[kSelectThreads / 64];
+  uint32_t res[2];
+  int32_t selcnt;
+  int32_t tiecnt;
+};
+
+}  // namespace
+
 __global__ void __launch_bounds__(kSelectThreads)
-topk_select_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
-                   int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
+topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
+                  int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
   __shared__ SelShared S;
-  const int q = blockIdx.x, tid = threadIdx.x;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = q_vis[q];
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
   const float* sc = ws.scores + (int64_t)q * ws.vstride;
+  const int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
   int32_t* oi = out_idx + (int64_t)q * k;
 
   if (V <= k) {                                       // everything visible is selected
     for (int i = tid; i < kHistBins; i += kSelectThreads) gh[i] = 0;
     for (int i = tid; i < k; i += kSelectThreads) oi[i] = i < V ? i : -1;
-    if (tid == 0) out_cnt[q] = V;
+    if (tid == 0) { out_cnt[q] = V; ws.cand_cnt[q] = 0; }
     return;
   }
+  const int ncand = ws.cand_cnt[q];
   for (int i = tid; i < kHistBins; i += kSelectThreads) { S.h[i] = gh[i]; gh[i] = 0; }
   if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; }
-  __syncthreads();
+  lds_barrier();
 
   uint32_t need = (uint32_t)k;
   int nbits = kHistBits;
-  int dstar;
-  uint32_t above;
-  find_digit(S, kHistBins, need, dstar, above);
+  find_digit<kSelectThreads>(S.h, kHistBins, need, S.scratch, S.res);
+  int dstar = (int)S.res[0];
   uint64_t P = (uint64_t)dstar;
-  need -= above;
+  need -= S.res[1];
   uint32_t cnt_eq = S.h[dstar];
-  __syncthreads();
+  lds_barrier();
 
-  // 2. global refinement while the prefix class is too large for LDS
+  // heavily tied inputs: refine the prefix over the candidate list until its class fits in LDS
   while (cnt_eq > (uint32_t)kTieCap) {
     const int d = min(kHistBits, 64 - nbits);
     for (int i = tid; i < (1 << d); i += kSelectThreads) S.h[i] = 0;
-    __syncthreads();
-    for (int t = tid; t < V; t += kSelectThreads) {
+    lds_barrier();
+    for (int i = tid; i < ncand; i += kSelectThreads) {
+      const int t = cand[i];
       const uint64_t C = composite(sc[t], t);
       if ((C >> (64 - nbits)) == P) atomicAdd(&S.h[(uint32_t)(C >> (64 - nbits - d)) & ((1u << d) - 1)], 1u);
     }
-    __syncthreads();
-    find_digit(S, 1 << d, need, dstar, above);
-    need -= above;
+    lds_barrier();
+    find_digit<kSelectThreads>(S.h, 1 << d, need, S.scratch, S.res);
+    dstar = (int)S.res[0];
+    need -= S.res[1];
     P = (P << d) | (uint64_t)dstar;
     nbits += d;
     cnt_eq = S.h[dstar];
-    __syncthreads();
+    lds_barrier();
   }
 
-  // 3. collect: prefix above P -> selected; prefix equal to P -> parked
-  for (int t = tid; t < V; t += kSelectThreads) {
-    const uint64_t C = composite(sc[t], t);
-    const uint64_t pre = C >> (64 - nbits);
-    if (pre > P) {
-      const int pos = atomicAdd(&S.selcnt, 1);
-      if (pos < CSA2_SEL_CAP) S.sel[pos] = t;
-    } else if (pre == P) {
-      const int pos = atomicAdd(&S.tiecnt, 1);
-      if (pos < kTieCap) S.tie[pos] = C;
+  // candidates: prefix above P -> selected; prefix equal to P -> parked
+  for (int i0 = 0; i0 < ncand; i0 += kSelectThreads) {
+    const int i = i0 + tid;
+    bool up = false, eq = false;
+    uint64_t C = 0;
+    int t = 0;
+    if (i < ncand) {
+      t = cand[i];
+      C = composite(sc[t], t);
+      const uint64_t pre = C >> (64 - nbits);
+      up = pre > P;
+      eq = pre == P;
     }
+    wave_append<int32_t>(up, t, &S.selcnt, S.sel, kSelCap);
+    wave_append<uint64_t>(eq, C, &S.tiecnt, S.tie, kTieCap);
   }
-  __syncthreads();
+  lds_barrier();
   const int ntie = min(S.tiecnt, kTieCap);
 
-  // 4. refine the parked keys (dropped entries become 0, never a valid key)
+  // refine the parked keys (dropped entries become 0, never a valid key)
   while (need > 0) {
     if (cnt_eq == need) {
       for (int i = tid; i < ntie; i += kSelectThreads) {
         const uint64_t C = S.tie[i];
         if (C) {
           const int pos = atomicAdd(&S.selcnt, 1);
-          if (pos < CSA2_SEL_CAP) S.sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)C);
+          if (pos < kSelCap) S.sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)C);
         }
       }
-      __syncthreads();
+      lds_barrier();
       break;
     }
     const int d = min(kHistBits, 64 - nbits);
     if (d <= 0) break;
     const int sh = 64 - nbits - d;
     for (int i = tid; i < (1 << d); i += kSelectThreads) S.h[i] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < ntie; i += kSelectThreads) {
       const uint64_t C = S.tie[i];
       if (C) atomicAdd(&S.h[(uint32_t)(C >> sh) & ((1u << d) - 1)], 1u);
     }
-    __syncthreads();
-    find_digit(S, 1 << d, need, dstar, above);
+    lds_barrier();
+    find_digit<kSelectThreads>(S.h, 1 << d, need, S.scratch, S.res);
+    dstar = (int)S.res[0];
     for (int i = tid; i < ntie; i += kSelectThreads) {
       const uint64_t C = S.tie[i];
       if (!C) continue;
       const int dig = (int)((uint32_t)(C >> sh) & ((1u << d) - 1));
       if (dig > dstar) {
         const int pos = atomicAdd(&S.selcnt, 1);
-        if (pos < CSA2_SEL_CAP) S.sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)C);
+        if (pos < kSelCap) S.sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)C);
         S.tie[i] = 0;
       } else if (dig < dstar) {
         S.tie[i] = 0;
       }
     }
-    need -= above;
+    need -= S.res[1];
     nbits += d;
     P = (P << d) | (uint64_t)dstar;
     cnt_eq = S.h[dstar];
-    __syncthreads();
+    lds_barrier();
   }
 
-  // 5. ascending order: bitonic sort of k indices padded to a power of two
-  int n2 = 1;
-  while (n2 < k) n2 <<= 1;
-  for (int i = tid; i < n2; i += kSelectThreads)
-    if (i >= min(k, S.selcnt)) S.sel[i] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kSelectThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int32_t a = S.sel[lo], b = S.sel[hi];
-        if ((a > b) == up) { S.sel[lo] = b; S.sel[hi] = a; }
-      }
-      __syncthreads();
+  // ascending order
+  const int nsel = min(k, S.selcnt);
+  const int nwords = (V + 31) >> 5;
+  if (nwords <= kTieCap * 2) {
+    // bitmap over the context in the (now free) parking buffer, then an
+    // ordered compaction: thread t owns words [t*W, t*W + W)
+    uint32_t* bm = reinterpret_cast<uint32_t*>(S.tie);
+    for (int i = tid; i < nwords; i += kSelectThreads) bm[i] = 0;
+    lds_barrier();
+    for (int i = tid; i < nsel; i += kSelectThreads) {
+      const int t = S.sel[i];
+      atomicOr(&bm[t >> 5], 1u << (t & 31));
     }
+    lds_barrier();
+    const int W = (nwords + kSelectThreads - 1) / kSelectThreads;
+    const int w0 = min(tid * W, nwords), w1 = min(w0 + W, nwords);
+    uint32_t mine = 0;
+    for (int i = w0; i < w1; ++i) mine += __builtin_popcount(bm[i]);
+    uint32_t x = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) S.scratch[wave] = x;
+    lds_barrier();
+    uint32_t pos = x - mine;
+    for (int i = 0; i < wave; ++i) pos += S.scratch[i];
+    for (int i = w0; i < w1; ++i) {
+      uint32_t bits = bm[i];
+      while (bits) {
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1;
+        oi[pos++] = (i << 5) + b;
+      }
+    }
+  } else {
+    // bitonic sort of the k indices padded to a power of two
+    int n2 = 1;
+    while (n2 < k) n2 <<= 1;
+    for (int i = tid; i < n2; i += kSelectThreads)
+      if (i >= nsel) S.sel[i] = 0x7FFFFFFF;
+    lds_barrier();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < n2 / 2; i += kSelectThreads) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t a = S.sel[lo], b = S.sel[hi];
+          if ((a > b) == up) { S.sel[lo] = b; S.sel[hi] = a; }
+        }
+        lds_barrier();
+      }
+    }
+    for (int i = tid; i < k; i += kSelectThreads) oi[i] = S.sel[i];
   }
-  for (int i = tid; i < k; i += kSelectThreads) oi[i] = S.sel[i];
-  if (tid == 0) out_cnt[q] = k;
+  if (tid == 0) { out_cnt[q] = k; ws.cand_cnt[q] = 0; }
 }
 
-hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
-                              int32_t* out_cnt, hipStream_t s) {
-  hipLaunchKernelGGL(topk_select_kernel, dim3(nq), dim3(kSelectThreads), 0, s, ws, q_vis, k, out_idx, out_cnt);
+hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
+                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s) {
+  const int nslices = max(1, (max_vis + kCollectSlice - 1) / kCollectSlice);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)((int64_t)nq * nslices)), dim3(kCollectThreads), 0, s, ws,
+                     q_vis, k, nslices);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(nq), dim3(kSelectThreads), 0, s, ws, q_vis, k, out_idx, out_cnt);
   return hipGetLastError();
 }
 

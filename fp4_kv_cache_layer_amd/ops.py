@@ -118,7 +118,8 @@ def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: t
 
 def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: torch.Tensor, cnt: torch.Tensor,
                      sm_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     with_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                     with_lse: bool = True, ws: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     _need(q, _BF16, "q")
     nq, h = q.shape[0], q.shape[1]
     k = idx.shape[1]
@@ -128,7 +129,7 @@ def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: to
         lse = torch.empty((nq, h), dtype=torch.float32, device=q.device)
     L.check("csa2_sparse_attn", L.load().csa2_sparse_attn(
         ctypes.byref(cache.view), _ptr(q), _ptr(q_seq), _ptr(idx), _ptr(cnt), nq, h, k, float(sm_scale),
-        _ptr(out), _ptr(lse), None, 0, _stream(stream)))
+        _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
 
 
@@ -151,6 +152,7 @@ class LayerCall:
             a.new_slots, a.new_kv, a.new_idxk, a.n_new = _ptr(new_slots), _ptr(new_kv), _ptr(new_idxk), new_slots.numel()
         if mode in (FULL, REINDEX):
             a.q_idx, a.w, a.h_idx = _ptr(q_idx), _ptr(w), q_idx.shape[1]
+        if ws is not None:
             a.ws, a.ws_bytes = _ptr(ws), ws.numel()
         a.q, a.h, a.sm_scale = _ptr(q), q.shape[1], float(sm_scale)
         a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = _ptr(q_seq), _ptr(q_vis), q.shape[0], k, max_vis

@@ -74,7 +74,7 @@ class DeviceCase:
             if mode == ops.REUSE:
                 idx, cnt = full_idx, full_cnt
                 call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                     idx, cnt, out, lse)
+                                     idx, cnt, out, lse, ws=self.ws)
             else:
                 idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
                 cnt = torch.empty(nq, dtype=torch.int32, device=dev)

@@ -39,7 +39,8 @@ def test_workspace_bytes():
     assert lib.csa2_workspace_bytes(L.CSA2_REUSE, 32, 65537, 8, 64, 512) == 0
     full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
     assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
-    assert full >= 32 * 65537 * 4 + 32 * 2048 * 4
+    assert full >= 32 * 2048 * 4 + 32 * 65537 * 4
+    assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4096, 70000, 8, 64, 512) >= 4096 * 70000 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
 
 

@@ -188,10 +188,11 @@ def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
 # attention alone, on chosen selections
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("h,cnts", [(16, [0, 1, 2, 3, 17, 512]), (64, [512, 300, 2]), (40, [33, 512]), (128, [511, 5])])
-def test_sparse_attn_given_selection(h, cnts):
+def test_sparse_attn_given_selection(h, cnts, with_ws):
     ops, _ = _ops()
-    say(f"[attn] h={h} cnts={cnts}")
+    say(f"[attn] h={h} cnts={cnts} ws={with_ws}")
     rng = np.random.default_rng(h)
     n, ps = 3000, 64
     npg = (n + ps - 1) // ps
@@ -218,9 +219,11 @@ def test_sparse_attn_given_selection(h, cnts):
         idx[i, :c] = sel
     q = (rng.standard_normal((nq, h, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     q_seq = np.zeros(nq, dtype=np.int32)
-    out, lse = ops.csa2_sparse_attn(cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda(),
-                                    torch.from_numpy(idx).cuda(), torch.tensor(cnts, dtype=torch.int32).cuda(),
-                                    1 / np.sqrt(512))
+    ws = ops.workspace(ops.REUSE, nq, 0, 1, h, k) if with_ws else None      # small batch: rows split across workgroups
+    for _ in range(2 if with_ws else 1):                                    # second call reuses the self-cleaned counters
+        out, lse = ops.csa2_sparse_attn(cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda(),
+                                        torch.from_numpy(idx).cuda(), torch.tensor(cnts, dtype=torch.int32).cuda(),
+                                        1 / np.sqrt(512), ws=ws)
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     o_ref, lse_ref = O.sparse_attn(ocache, q, q_seq, idx, np.array(cnts), 1 / np.sqrt(512))
     err = np.abs(out - o_ref).max()
