@@ -111,6 +111,14 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   return r;
 }
 
+// Share buffers of the attention when the workspace holds them (else no split).
+void* attn_part(void* ws, size_t ws_bytes, int32_t nq, int32_t h, int32_t k) {
+  const size_t part = attn_part_bytes(nq, h, k);
+  const size_t z = zero_state_bytes(nq);
+  if (part == 0 || ws == nullptr || ws_bytes < z + part) return nullptr;
+  return reinterpret_cast<uint8_t*>(ws) + z;
+}
+
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
                       int32_t* out_cnt, const IndexWs& iw, hipStream_t s) {
@@ -148,9 +156,10 @@ csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring) {
 
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
   (void)h_idx; (void)k;
-  (void)h;
-  if (nq <= 0 || max_vis < 0 || mode == CSA2_REUSE) return 0;
-  return zero_state_bytes(nq) + index_score_bytes(nq, max_vis);
+  if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;
+  size_t b = zero_state_bytes(nq) + attn_part_bytes(nq, h, k);
+  if (mode != CSA2_REUSE) b += index_score_bytes(nq, max_vis);
+  return b;
 }
 
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
@@ -184,9 +193,10 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
   CacheArgs ca;
   csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
   if (st != CSA2_OK || nq == 0) return st;
-  (void)ws; (void)ws_bytes;
+  if (ws && !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
   TimedLaunch t(CSA2_KCLASS_ATTN, s);
-  return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, s));
+  return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse,
+                                       attn_part(ws, ws_bytes, nq, h, k), s));
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
@@ -215,14 +225,18 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
     if (st != CSA2_OK) return st;
   }
   if (a->nq == 0) return CSA2_OK;
+  const size_t z = zero_state_bytes(a->nq), part = attn_part_bytes(a->nq, a->h, a->k);
   if (mode != CSA2_REUSE) {
+    if (a->ws_bytes < z + part + index_score_bytes(a->nq, a->max_vis)) return CSA2_ERR_WORKSPACE;
     st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt,
-                   index_ws(a->ws, a->nq, a->max_vis, zero_state_bytes(a->nq)), s);
+                   index_ws(a->ws, a->nq, a->max_vis, z + part), s);
     if (st != CSA2_OK) return st;
+  } else if (a->ws && !aligned(a->ws, 16)) {
+    return CSA2_ERR_INVALID_ARG;
   }
   TimedLaunch t(CSA2_KCLASS_ATTN, s);
   return hip_status(launch_sparse_attn(ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
-                                       a->lse, s));
+                                       a->lse, attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k), s));
 }
 
 }  // extern "C"

@@ -79,6 +79,30 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t b) {
   return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
 }
 
+// Reductions across the four 16-lane rows of a wave with the gfx950 lane
+// swaps (plain VALU, no LDS round trip).  V_PERMLANE16_SWAP exchanges odd
+// rows of one operand with even rows of the other, V_PERMLANE32_SWAP the
+// upper half of one with the lower half of the other; with both operands
+// equal to x, the two results hold x and its partner row (half) in every
+// lane, in one order or the other, so a symmetric op of the two is the
+// pairwise reduction.
+__device__ __forceinline__ float rows_pair_max(float x) {        // over lanes l, l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_max(float x) {           // over lanes l, l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroup barrier that orders LDS only.  A plain __syncthreads() also
 // waits for every global load in flight, which would drain prefetched data
 // at each barrier.

@@ -50,8 +50,14 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
                               int32_t* out_idx, int32_t* out_cnt, hipStream_t s);
 
+// Attention shares (small batches split their rows across workgroups):
+// [nq * ceil(h/16)][nsplit][16][512] fp32 partial outputs, then
+// [nq * ceil(h/16)][nsplit][32] fp32 (max, sum); no initial state needed.
+int attn_nsplit(int nq, int h, int k);
+size_t attn_part_bytes(int nq, int h, int k);
+
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              hipStream_t s);
+                              void* part, hipStream_t s);
 
 }  // namespace csa2

@@ -9,12 +9,15 @@
 // by the context length ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
 // Compression", Introduction: near-constant decode FLOPs from 4K to 1M).
 //
-// Work split.  A workgroup serves one query and one group of 16 heads.  It
-// first resolves the physical row of every selected entry into LDS (one round
-// of index and page-table loads for the whole selection), then its eight
-// waves, two row groups x four 128-wide slices of the latent, stream 32-row
-// tiles with the row gathers of the next kPrefetch tiles in flight.  For every
-// tile a wave
+// Work split.  A (query, group of 16 heads) unit is cut into nsplit
+// contiguous shares of its selected rows so that a small decode batch still
+// covers the chip; a workgroup serves one share and writes its unnormalised
+// output with its running max and sum, and a combine kernel merges the shares
+// (nsplit = 1 writes the final output directly).  The four waves of a
+// workgroup own the four 128-wide slices of the latent.  The workgroup first
+// resolves the physical row of every selected entry of its share into LDS,
+// then streams 32-row tiles with the row gathers of the next kPrefetch tiles
+// in flight.  For every tile a wave
 //   - gathers, for two rows per lane, the 16 code bytes of one 32-element
 //     scale block of its slice and dequantises them with
 //     V_CVT_SCALEF32_PK_BF16_FP4 straight into the A operand of
@@ -23,22 +26,24 @@
 //   - publishes its partial S^T (32 rows x 16 heads) and its bf16 slice of the
 //     rows in LDS (row stride 272 B: the 16-byte writes and the transposing
 //     8-byte reads both spread evenly over the 64 banks),
-//   - sums the four partial S^T of its row group (same order in every wave),
-//     runs the online softmax and accumulates O[16 heads][its 128 dims] +=
-//     P X with P split into bf16 hi + lo terms; the B operand (rows as K)
-//     comes from LDS through the transposing read DS_READ_B64_TR_B16.
-// So each latent element is dequantised once per head group, the O
-// accumulator is 32 registers per lane, and the only cross-wave traffic per
-// tile is 2 KB of partial scores per wave.
+//   - sums the four partial S^T (same order in every wave), runs the online
+//     softmax (the output is rescaled only when the running max grows by more
+//     than 8 nats, so probabilities stay below e^8) and accumulates
+//     O[16 heads][its 128 dims] += P X with P split into bf16 hi + lo terms;
+//     the B operand (rows as K) comes from LDS through the transposing read
+//     DS_READ_B64_TR_B16.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
 namespace csa2 {
 
-constexpr int kAttnThreads = 512;
+constexpr int kAttnThreads = 256;
 constexpr int kTileRows = 32;
 constexpr int kSliceStride = 272;                       // bytes per bf16 slice row (128 * 2 + 16 pad)
 constexpr int kSliceBytes = kTileRows * kSliceStride;   // 8,704
+constexpr int kPrefetch = 4;                            // tiles of row gathers in flight per wave
+constexpr float kRescaleSlack = 8.0f;                   // nats the running max may lag the true max
+constexpr int kMaxShareRows = 2048;
 
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
@@ -46,19 +51,6 @@ __device__ __forceinline__ shortx4 lds_read_tr16(const uint8_t* base_generic, in
   const __attribute__((address_space(3))) uint8_t* p =
       (const __attribute__((address_space(3))) uint8_t*)(base_generic) + byte_off;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (a >> 16) | (b & 0xFFFF0000u);
-}
-
-__device__ __forceinline__ float bf16_round(float x) {
-  uint32_t a = __float_as_uint(x);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  return __uint_as_float(a & 0xFFFF0000u);
 }
 
 template <int SEL>
@@ -72,29 +64,31 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-constexpr int kPrefetch = 4;                            // tiles of row gathers in flight per wave
-
 struct AttnShared {
-  uint8_t xs[2][4][kSliceBytes];     // [row group][slice] bf16 rows of the current tile (69,632 B)
-  floatx4 sp[2][4][2][4][16];        // partial S^T per wave: [m-tile][row quad][head] of 4 rows (16,384 B)
-  int64_t rowoff[2048];              // byte offset of every selected row (16,384 B)
-  float st_m[4][16];                 // row-group merge scratch
-  float st_l[4][16];
+  uint8_t xs[4][kSliceBytes];        // [slice] bf16 rows of the current tile (34,816 B)
+  floatx4 sp[4][2][4][16];           // partial S^T per wave: [m-tile][row quad][head] of 4 rows (8,192 B)
+  uint32_t row[kMaxShareRows];       // physical row of every selected entry of the share (8,192 B)
 };
 
-__global__ void __launch_bounds__(kAttnThreads, 1)
+__global__ void __launch_bounds__(kAttnThreads, 2)
 sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
                    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int h, int k,
-                   float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
+                   float sm_scale, float* __restrict__ out, float* __restrict__ lse, int nsplit,
+                   float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ AttnShared S;
   const int ngroups = (h + 15) >> 4;
-  const int qi = blockIdx.x / ngroups;
-  const int hg = blockIdx.x - qi * ngroups;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ds = wave & 3, rg = wave >> 2;
+  const int unit = blockIdx.x / nsplit;                 // (query, head group)
+  const int split = blockIdx.x - unit * nsplit;
+  const int qi = unit / ngroups;
+  const int hg = unit - qi * ngroups;
+  const int tid = threadIdx.x, lane = tid & 63, ds = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int n = cnt[qi];
   const int head = hg * 16 + r;
+  const int n_all = cnt[qi];
+  const int ntiles_all = (n_all + kTileRows - 1) / kTileRows;
+  const int per_split = (ntiles_all + nsplit - 1) / nsplit;
+  const int j0 = split * per_split * kTileRows;         // first selected row of this share
+  const int n = max(0, min(n_all, j0 + per_split * kTileRows) - j0);
 
   // Q^T operand: head r, K-step s holds dims 128*ds + 32*g + 8*s .. +7.
   bf16x8 qop[4];
@@ -104,37 +98,36 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
 #pragma unroll
     for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8, ok ? src[s] : make_uint4(0, 0, 0, 0));
   }
+  // physical rows of the share, resolved once (index loads clamped to the
+  // row of k entries so they need not wait for the count)
+  {
+    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
+    const int32_t* irow = idx + (int64_t)qi * k;
+    for (int j = tid; j < per_split * kTileRows; j += kAttnThreads) {
+      const int t = irow[min(j0 + j, k - 1)];
+      if (j < n) S.row[j] = (uint32_t)entry_row(pt_row, t, c.lg_page);
+    }
+  }
+  lds_barrier();
 
   floatx4 oacc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
-
-  // physical rows of the whole selection, resolved once
-  {
-    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
-    const int32_t* irow = idx + (int64_t)qi * k;
-    for (int j = tid; j < n; j += kAttnThreads) S.rowoff[j] = entry_row(pt_row, irow[j], c.lg_page) * kKvRowBytes;
-  }
-  lds_barrier();
   const int ntiles = (n + kTileRows - 1) / kTileRows;
-  const int iters = (ntiles + 1) >> 1;
+  uint8_t* xs = &S.xs[ds][0];
 
-  uint8_t* xs = &S.xs[rg][ds][0];
-
-  // ring of row gathers: slot u holds iteration it + u's 16 code bytes (one
-  // scale block of this slice) and scale byte, for two rows per lane
+  // Ring of row gathers: slot u holds tile t0+u's 16 code bytes (one scale
+  // block of this slice) and scale byte for two rows per lane.  Loads are
+  // unconditional (a row past the share reads physical row 0, which always
+  // exists) so the compiler counts gathers in flight instead of draining them.
   uint4 cd[kPrefetch][2];
   uint32_t sb[kPrefetch][2];
-  // Loads are unconditional (a row past the selection reads row 0 of page 0,
-  // which always exists) so the compiler can count gathers in flight; the
-  // data of such rows is replaced by zeros at use.
-  auto gather = [&](int iter, uint4 (&c2)[2], uint32_t (&s2)[2]) {
-    const int tile = 2 * iter + rg;
+  auto gather = [&](int tile, uint4 (&c2)[2], uint32_t (&s2)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j = tile * kTileRows + mt * 16 + r;
-      const uint8_t* src = c.kv + ((iter < iters && j < n) ? S.rowoff[j] : 0);
+      const uint8_t* src = c.kv + (size_t)(j < n ? S.row[j] : 0u) * kKvRowBytes;
       c2[mt] = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * g);
       s2[mt] = src[kCodeBytes + 4 * ds + g];
     }
@@ -142,23 +135,23 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u) gather(u, cd[u], sb[u]);
 
-  // The trip count is padded to whole rings (tiles past the selection are
-  // masked), so every ring slot is consumed in a fixed order and the compiler
-  // can keep the younger gathers in flight.
-  const int iters_pad = (iters + kPrefetch - 1) / kPrefetch * kPrefetch;
-  for (int it0 = 0; it0 < iters_pad; it0 += kPrefetch) {
+  // The trip count is padded to whole rings (tiles past the share are masked)
+  // so the ring slots are consumed in a fixed order.
+  const int ntiles_pad = (ntiles + kPrefetch - 1) / kPrefetch * kPrefetch;
+  for (int t0 = 0; t0 < ntiles_pad; t0 += kPrefetch) {
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u) {
-    const int it = it0 + u;
-    const int tile = 2 * it + rg;
+    const int tile = t0 + u;
+    const int lim = n - tile * kTileRows;               // rows of this tile inside the share
     // ---- dequantise into the S^T A operand; partial S^T over this slice ----
     bf16x8 xa[2][4];
     floatx4 st[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const bool ok = tile * kTileRows + mt * 16 + r < n;
-      const float scale = e8m0_to_float(ok ? sb[u][mt] : 127u);
-      const uint32_t wds[4] = {ok ? cd[u][mt].x : 0u, ok ? cd[u][mt].y : 0u, ok ? cd[u][mt].z : 0u, ok ? cd[u][mt].w : 0u};
+      // a row past the share keeps its (finite) codes but gets scale 1: its
+      // logit is masked below, so it only ever meets a zero probability
+      const float scale = e8m0_to_float(mt * 16 + r < lim ? sb[u][mt] : 127u);
+      const uint32_t wds[4] = {cd[u][mt].x, cd[u][mt].y, cd[u][mt].z, cd[u][mt].w};
       st[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -166,77 +159,73 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
         st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt][s], qop[s], st[mt], 0, 0, 0);
       }
     }
-    gather(it + kPrefetch, cd[u], sb[u]);               // refill the slot kPrefetch tiles ahead
+    gather(tile + kPrefetch, cd[u], sb[u]);             // refill the slot kPrefetch tiles ahead
     // ---- publish the bf16 slice rows and the partial scores ----
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       uint8_t* rowp = xs + (mt * 16 + r) * kSliceStride + 64 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(rowp + 16 * s) = xa[mt][s];
-      S.sp[rg][ds][mt][g][r] = st[mt];                  // lanes write consecutive 16 B: no bank conflicts
+      S.sp[ds][mt][g][r] = st[mt];                      // lanes write consecutive 16 B: no bank conflicts
     }
     lds_barrier();
     // ---- full scores of head r, rows mt*16 + 4g + i (fixed summation order) ----
     float v[2][4];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      floatx4 acc = S.sp[rg][0][mt][g][r];
+      floatx4 acc = S.sp[0][mt][g][r];
 #pragma unroll
-      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[rg][d2][mt][g][r];
+      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[d2][mt][g][r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = tile * kTileRows + mt * 16 + 4 * g + i;
-        v[mt][i] = j < n ? acc[i] * sm_scale : -INFINITY;
-        tmax = fmaxf(tmax, v[mt][i]);
-      }
+      for (int i = 0; i < 4; ++i) v[mt][i] = acc[i] * sm_scale;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.0f, psum = 0.0f;
-    float phi[2][4], plo[2][4];                         // p = phi + plo, both bf16
-    if (m_new == -INFINITY) {
+    if (lim < kTileRows) {                              // uniform: only a tile holding the end of the share
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) phi[mt][i] = plo[mt][i] = 0.0f;
-    } else {
-      alpha = __expf(m_run - m_new);                    // m_run = -inf -> 0
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __expf(v[mt][i] - m_new);     // -inf -> 0
-          psum += p;
-          phi[mt][i] = bf16_round(p);
-          plo[mt][i] = bf16_round(p - phi[mt][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (mt * 16 + 4 * g + i >= lim) v[mt][i] = -INFINITY;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    {
-      // O rows are heads 4g+i: their rescale factor lives in lane 4g+i
+    float tmax = fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
+                       fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
+    tmax = halves_max(rows_pair_max(tmax));
+    // rescale only when the max moved by more than the slack
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) {
+      const float m_new = tmax > m_run + kRescaleSlack ? tmax : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);   // m_run = -inf -> 0
+      l_run *= alpha;
+      m_run = m_new;
       float al[4];
-      bool any = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);   // O rows are heads 4g+i
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
+    }
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        al[i] = __shfl(alpha, 4 * g + i);
-        any |= al[i] != 1.0f;
+        p[mt][i] = m_run == -INFINITY ? 0.0f : __expf(v[mt][i] - m_run);   // -inf -> 0
+        psum += p[mt][i];
       }
-      if (__builtin_amdgcn_ballot_w64(any)) {
+    psum = halves_sum(rows_pair_sum(psum));
+    l_run += psum;
+    // p = hi + lo, both bf16 (V_CVT_PK_BF16_F32, round to nearest even)
+    uint32_t whi[4], wlo[4];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
-      }
+    for (int pr = 0; pr < 4; ++pr) {
+      const float a = p[pr >> 1][2 * (pr & 1)], b = p[pr >> 1][2 * (pr & 1) + 1];
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{a, b}), bf16x2));
+      const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);
+      whi[pr] = hi;
+      wlo[pr] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{ra, rb}), bf16x2));
     }
-    const bf16x8 pa_hi = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(phi[0][0], phi[0][1]), pack_bf16x2(phi[0][2], phi[0][3]),
-                                                               pack_bf16x2(phi[1][0], phi[1][1]), pack_bf16x2(phi[1][2], phi[1][3])));
-    const bf16x8 pa_lo = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(plo[0][0], plo[0][1]), pack_bf16x2(plo[0][2], plo[0][3]),
-                                                               pack_bf16x2(plo[1][0], plo[1][1]), pack_bf16x2(plo[1][2], plo[1][3])));
+    const bf16x8 pa_hi = __builtin_bit_cast(bf16x8, make_uint4(whi[0], whi[1], whi[2], whi[3]));
+    const bf16x8 pa_lo = __builtin_bit_cast(bf16x8, make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]));
     // ---- O[16 heads][slice] += P X_slice: rows 4g+j and 16+4g+j through transposing reads ----
     const int off_a = (4 * g + (r >> 2)) * kSliceStride + 8 * (r & 3);
     const int off_b = off_a + 16 * kSliceStride;
@@ -254,34 +243,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   }
   }
 
-  // ---- merge the two row groups (row group 1 hands its state to row group 0) ----
-  float* red = reinterpret_cast<float*>(&S.xs[0][0][0]);   // [slice][16 heads][128] fp32 = 32 KB
-  if (rg == 1) {
-    if (g == 0) { S.st_m[ds][r] = m_run; S.st_l[ds][r] = l_run; }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(ds * 16 + 4 * g + i) * 128 + 16 * nt + r] = oacc[nt][i];
-  }
-  lds_barrier();
-  if (rg == 0) {
-    const float m1 = S.st_m[ds][r], l1 = S.st_l[ds][r];
-    const float M = fmaxf(m_run, m1);
-    const float f0 = (M == -INFINITY || m_run == -INFINITY) ? 0.0f : __expf(m_run - M);
-    const float f1 = (M == -INFINITY || m1 == -INFINITY) ? 0.0f : __expf(m1 - M);
-    const float L = f0 * l_run + f1 * l1;
-    float a0[4], a1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { a0[i] = __shfl(f0, 4 * g + i); a1[i] = __shfl(f1, 4 * g + i); }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        oacc[nt][i] = a0[i] * oacc[nt][i] + a1[i] * red[(ds * 16 + 4 * g + i) * 128 + 16 * nt + r];
-    m_run = M;
-    l_run = L;
-  }
-  if (rg == 0) {
+  if (nsplit == 1) {
     float linv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -297,15 +259,82 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       }
     if (lse != nullptr && ds == 0 && g == 0 && head < h)
       lse[(int64_t)qi * h + head] = (m_run == -INFINITY) ? -INFINITY : m_run + __logf(l_run);
+    return;
   }
+  // share of a split unit: unnormalised output, running max and sum
+  const int64_t pbase = (int64_t)unit * nsplit + split;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      part_o[(pbase * 16 + 4 * g + i) * kLatent + 128 * ds + 16 * nt + r] = oacc[nt][i];
+  if (ds == 0 && g == 0) {
+    part_ml[pbase * 32 + r] = m_run;
+    part_ml[pbase * 32 + 16 + r] = l_run;
+  }
+}
+
+// Merges the nsplit shares of one (query, head): O = sum_s e^(m_s - M) O_s / L,
+// L = sum_s e^(m_s - M) l_s, LSE = M + ln L.  One workgroup per head, one
+// float4 of the output per thread, so every share is read in one round trip.
+__global__ void __launch_bounds__(128)
+attn_combine_kernel(int h, int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                    float* __restrict__ out, float* __restrict__ lse) {
+  const int ngroups = (h + 15) >> 4;
+  const int unit = blockIdx.x >> 4, hh = blockIdx.x & 15;
+  const int qi = unit / ngroups, hg = unit - qi * ngroups;
+  const int hd = hg * 16 + hh;
+  if (hd >= h) return;
+  const int tid = threadIdx.x;
+  const float* ml = part_ml + (int64_t)unit * nsplit * 32;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[sp * 32 + hh]);
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* po = reinterpret_cast<const float4*>(part_o + ((int64_t)unit * nsplit * 16 + hh) * kLatent);
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float ms = ml[sp * 32 + hh];
+    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
+    L += f * ml[sp * 32 + 16 + hh];
+    const float4 x = po[(int64_t)sp * 16 * kLatent / 4 + tid];
+    acc.x += f * x.x; acc.y += f * x.y; acc.z += f * x.z; acc.w += f * x.w;
+  }
+  const float linv = L > 0.0f ? 1.0f / L : 0.0f;
+  acc.x *= linv; acc.y *= linv; acc.z *= linv; acc.w *= linv;
+  reinterpret_cast<float4*>(out + ((int64_t)qi * h + hd) * kLatent)[tid] = acc;
+  if (lse != nullptr && tid == 0) lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+}
+
+int attn_nsplit(int nq, int h, int k) {
+  const int units = nq * ((h + 15) / 16);
+  const int ntiles = (k + kTileRows - 1) / kTileRows;
+  int ns = 1;
+  // aim at >= 512 workgroups with at least two tiles per share; shares must fit the row table
+  while (ns < 16 && units * ns < 512 && ntiles >= 4 * ns) ns *= 2;
+  while ((ntiles + ns - 1) / ns * kTileRows > kMaxShareRows) ns *= 2;
+  return ns;
+}
+
+size_t attn_part_bytes(int nq, int h, int k) {
+  const int ns = attn_nsplit(nq, h, k);
+  if (ns == 1 || nq <= 0) return 0;
+  const size_t units = (size_t)nq * ((h + 15) / 16);
+  return (units * ns * (16 * kLatent + 32) * 4 + 255) / 256 * 256;
 }
 
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              hipStream_t s) {
+                              void* part, hipStream_t s) {
   const int ngroups = (h + 15) / 16;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)((int64_t)nq * ngroups)), dim3(kAttnThreads), 0, s, c, q,
-                     q_seq, idx, cnt, h, k, sm_scale, out, lse);
+  const int ns = part ? attn_nsplit(nq, h, k) : 1;
+  const int64_t units = (int64_t)nq * ngroups;
+  float* part_o = reinterpret_cast<float*>(part);
+  float* part_ml = part_o ? part_o + units * ns * 16 * kLatent : nullptr;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)(units * ns)), dim3(kAttnThreads), 0, s, c, q, q_seq, idx,
+                     cnt, h, k, sm_scale, out, lse, ns, part_o, part_ml);
+  if (ns > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(units * 16)), dim3(128), 0, s, h, ns, part_o, part_ml, out,
+                       lse);
   return hipGetLastError();
 }
 

@@ -114,10 +114,13 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
                                   const uint16_t* kv_rows, const uint16_t* idxk_rows,
                                   int32_t n, hipStream_t s);
 
-/* Bytes of workspace an index_topk / layer_step call needs (0 for Reuse).
- * Layout: per-query histograms [nq][2048] u32 and candidate counters [nq]
- * u32 first, then per-query scores [nq][round_up(max_vis, 64)] fp32 and
- * candidate indices of the same shape.  The histogram part carries state:
+/* Bytes of workspace a layer_step call of this shape needs.  Layout:
+ * per-query histograms [nq][2048] u32 and candidate counters [nq] u32
+ * first; then, for batches small enough that the attention splits each
+ * query's rows across workgroups, the attention shares; then (Full and
+ * Reindex) per-query scores [nq][round_up(max_vis, 64)] fp32 and candidate
+ * indices of the same shape.  csa2_index_topk and csa2_sparse_attn accept a
+ * workspace sized by this call for the same shape.  The histogram part carries state:
  * every call leaves it zeroed for the next one, so zero the whole workspace
  * once after allocating it (csa2_workspace_init does this).  Calls that
  * share one workspace must not run concurrently. */
@@ -147,8 +150,10 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
  *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
  *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq],
  *   out [nq][h][512] fp32, lse [nq][h] fp32 (nullable).
- * 1 <= h <= 128; sm_scale > 0 and finite.  The attention needs no
- * workspace: ws / ws_bytes are ignored (pass NULL / 0). */
+ * 1 <= h <= 128; sm_scale > 0 and finite.  ws may be NULL; with a
+ * workspace of csa2_workspace_bytes(CSA2_REUSE, nq, 0, 1, h, k) bytes, small
+ * batches split each query's rows across workgroups and merge the shares in
+ * a second kernel. */
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq,
                              const int32_t* idx, const int32_t* cnt,
                              int32_t nq, int32_t h, int32_t k, float sm_scale,

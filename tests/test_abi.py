@@ -36,10 +36,12 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = L.load()
-    assert lib.csa2_workspace_bytes(L.CSA2_REUSE, 32, 65537, 8, 64, 512) == 0
+    reuse = lib.csa2_workspace_bytes(L.CSA2_REUSE, 32, 65537, 8, 64, 512)
+    assert reuse >= 32 * 2048 * 4                     # histograms (+ attention shares for small batches)
     full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
     assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
-    assert full >= 32 * 2048 * 4 + 32 * 65537 * 4
+    assert full >= reuse + 2 * 32 * 65537 * 4
+    assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4, 100, 8, 0, 512) == 0          # invalid h
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4096, 70000, 8, 64, 512) >= 4096 * 70000 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
 
