@@ -7,10 +7,13 @@ latent, Top-512).  Inputs are synthetic, seeded, and already resident in HBM
 when timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain device copy of known size, for
+                                           # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -31,6 +34,32 @@ def scan_bytes(spec) -> int:
     and head weights (h_idx x 4 B)."""
     vis = spec.q_vis()
     return int(vis.sum()) * 128 + spec.nq * spec.h_idx * (128 + 4)
+
+
+def scan_source_hash() -> str:
+    """Hash of the indexer-scan kernel source: a stored counter reading
+    applies only to the kernel it was taken on."""
+    src = os.path.join(ROOT, "fp4_kv_cache_layer_amd", "csrc", "index_scan.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+COPY_BYTES = 1 << 30
+SCRUB_BYTES = 512 << 20
+
+
+def copy_calibration(reps: int = 4) -> int:
+    """Device-to-device copies of exactly COPY_BYTES each (torch's copy
+    kernel): FETCH_SIZE and WRITE_SIZE of these launches give the factor that
+    turns counter readings into bytes."""
+    import torch
+    src = torch.full((COPY_BYTES // 4,), 1.0, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": reps}), flush=True)
+    return 0
 
 
 def cpu_baseline(spec, dc, budget_s: float = 12.0):
@@ -92,7 +121,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "scan_traffic.json"),
                     help="HBM traffic per scan launch measured with rocprofv3 counters (optional)")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         return 2
@@ -114,35 +146,63 @@ def main() -> int:
         dc.run_group()
     torch.cuda.synchronize()
 
-    # timed region without event hooks
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dc.run_group()
-    torch.cuda.synchronize()
-    ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # timed region with per-kernel device events (dominant kernel: indexer scan)
+    # Timed region: K steps; the dominant kernel (indexer scan) carries
+    # device timestamps in its dispatches.
     n_scan = sum(1 for m in spec.modes if m != ops.REUSE)
     n_attn = len(spec.modes)
-    rings = {L.KCLASS_SCAN: ops.TimingRing(L.KCLASS_SCAN, args.steps * n_scan),
-             L.KCLASS_SELECT: ops.TimingRing(L.KCLASS_SELECT, args.steps * n_scan),
-             L.KCLASS_ATTN: ops.TimingRing(L.KCLASS_ATTN, args.steps * n_attn),
-             L.KCLASS_APPEND: ops.TimingRing(L.KCLASS_APPEND, args.steps)}
-    for r in rings.values():
-        r.install()
+    scan_ring = ops.TimingRing(L.KCLASS_SCAN, args.steps * n_scan)
+    scan_ring.install()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         dc.run_group()
     torch.cuda.synchronize()
     ms_events = (time.perf_counter() - t0) * 1e3 / args.steps
+    scan_ring.uninstall()
+    scan_ms = scan_ring.durations_ms()
+
+    # Breakdown pass (not the timed region): every kernel class timed.
+    rings = {L.KCLASS_SCAN: ops.TimingRing(L.KCLASS_SCAN, args.steps * n_scan),
+             L.KCLASS_SELECT: ops.TimingRing(L.KCLASS_SELECT, args.steps * n_scan),
+             L.KCLASS_ATTN: ops.TimingRing(L.KCLASS_ATTN, args.steps * n_attn),
+             L.KCLASS_APPEND: ops.TimingRing(L.KCLASS_APPEND, args.steps)}
+    for r in rings.values():
+        r.install()
+    for _ in range(args.steps):
+        dc.run_group()
     for r in rings.values():
         r.uninstall()
     dur = {k: r.durations_ms() for k, r in rings.items()}
 
+    # Scrubbed pass: a 512 MiB read between steps evicts the 256 MB
+    # Infinity Cache and the L2, so no step starts with the cache warm;
+    # each step is bracketed by its own device events.
+    scrub = torch.ones(SCRUB_BYTES // 8, dtype=torch.int64, device="cuda")
+    sink = torch.zeros((), dtype=torch.int64, device="cuda")
+    sring = ops.TimingRing(L.KCLASS_SCAN, args.steps * n_scan)
+    sring.install()
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in step_ev:
+        torch.sum(scrub, dim=0, out=sink)
+        e0.record()
+        dc.run_group()
+        e1.record()
+    sring.uninstall()
+    torch.cuda.synchronize()
+    scrubbed_steps = [a.elapsed_time(b) for a, b in step_ev]
+    scrubbed_scan = sring.durations_ms()
+    del scrub
+
+    # the same K steps with no timestamps, for comparison
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
+
     ms = ms_events
     value = spec.num_seqs * spec.n_new / (ms / 1e3) if spec.n_new else spec.nq / (ms / 1e3)
-    scan_ms = dur[L.KCLASS_SCAN]
     scan_avg = statistics.mean(scan_ms)
     sbytes = scan_bytes(spec)
     achieved = sbytes / (scan_avg / 1e3) / 1e9
@@ -150,7 +210,7 @@ def main() -> int:
     if os.path.exists(args.traffic):
         try:
             tr = json.load(open(args.traffic))
-            if tr.get("workload") == spec.name:
+            if tr.get("workload") == spec.name and tr.get("kernel_source_sha256_16") == scan_source_hash():
                 traffic = tr.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -177,9 +237,14 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "index_scan_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": sbytes, "avg_launch_us": round(scan_avg * 1e3, 2)},
-        "kernels_avg_us": {"append": avg(dur[L.KCLASS_APPEND]), "scan_full": avg(scan_ms[0::n_scan]),
-                           "scan_reindex": avg(scan_ms[1::n_scan]) if n_scan > 1 else None,
+        "kernels_avg_us": {"append": avg(dur[L.KCLASS_APPEND]), "scan_full": avg(dur[L.KCLASS_SCAN][0::n_scan]),
+                           "scan_reindex": avg(dur[L.KCLASS_SCAN][1::n_scan]) if n_scan > 1 else None,
                            "select": avg(dur[L.KCLASS_SELECT]), "attn": avg(dur[L.KCLASS_ATTN])},
+        "cache_scrubbed": {"ms_per_step_median": round(statistics.median(scrubbed_steps), 5),
+                           "scan_avg_us": avg(scrubbed_scan),
+                           "scan_full_us": avg(scrubbed_scan[0::n_scan]),
+                           "scan_reindex_us": avg(scrubbed_scan[1::n_scan]) if n_scan > 1 else None,
+                           "scan_frac": round(sbytes / (statistics.mean(scrubbed_scan) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "ms_per_step_no_events": round(ms_plain, 5),
         "group_hbm_frac": None,
     }

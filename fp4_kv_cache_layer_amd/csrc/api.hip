@@ -12,21 +12,21 @@ namespace {
 
 csa2_timing_ring* g_rings[CSA2_NUM_KCLASSES] = {nullptr, nullptr, nullptr, nullptr};
 
+// Takes the next slot of a kernel class's timing ring, if one is installed;
+// the launch records the slot's events as part of its dispatches.
 struct TimedLaunch {
   csa2_timing_ring* ring;
-  hipStream_t s;
   int slot;
-  TimedLaunch(int cls, hipStream_t st) : ring(g_rings[cls]), s(st), slot(-1) {
+  KEvents ev;
+  explicit TimedLaunch(int cls) : ring(g_rings[cls]), slot(-1) {
     if (ring && ring->count < ring->capacity) {
       slot = ring->count;
-      (void)hipEventRecord(ring->start[slot], s);
+      ev.start = ring->start[slot];
+      ev.stop = ring->stop[slot];
     }
   }
   ~TimedLaunch() {
-    if (slot >= 0) {
-      (void)hipEventRecord(ring->stop[slot], s);
-      ring->count = slot + 1;
-    }
+    if (slot >= 0) ring->count = slot + 1;
   }
 };
 
@@ -123,12 +123,12 @@ csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
                       int32_t* out_cnt, const IndexWs& iw, hipStream_t s) {
   if (max_vis > 0) {
-    TimedLaunch t(CSA2_KCLASS_SCAN, s);
-    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s));
+    TimedLaunch t(CSA2_KCLASS_SCAN);
+    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
     if (st != CSA2_OK) return st;
   }
-  TimedLaunch t(CSA2_KCLASS_SELECT, s);
-  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s));
+  TimedLaunch t(CSA2_KCLASS_SELECT);
+  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s, t.ev));
 }
 
 }  // namespace
@@ -173,8 +173,8 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
   CacheArgs ca;
   csa2_status st = validate_append(c, slots, kv_rows, idxk_rows, n, &ca);
   if (st != CSA2_OK || n == 0) return st;
-  TimedLaunch t(CSA2_KCLASS_APPEND, s);
-  return hip_status(launch_append_quant(ca.kv, ca.idx_k, slots, kv_rows, idxk_rows, n, s));
+  TimedLaunch t(CSA2_KCLASS_APPEND);
+  return hip_status(launch_append_quant(ca.kv, ca.idx_k, slots, kv_rows, idxk_rows, n, s, t.ev));
 }
 
 csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
@@ -194,9 +194,9 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
   csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   if (ws && !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
-  TimedLaunch t(CSA2_KCLASS_ATTN, s);
+  TimedLaunch t(CSA2_KCLASS_ATTN);
   return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse,
-                                       attn_part(ws, ws_bytes, nq, h, k), s));
+                                       attn_part(ws, ws_bytes, nq, h, k), s, t.ev));
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
@@ -220,8 +220,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
   if (st != CSA2_OK) return st;
 
   if (mode == CSA2_FULL && a->n_new > 0) {
-    TimedLaunch t(CSA2_KCLASS_APPEND, s);
-    st = hip_status(launch_append_quant(ca.kv, ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s));
+    TimedLaunch t(CSA2_KCLASS_APPEND);
+    st = hip_status(launch_append_quant(ca.kv, ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
     if (st != CSA2_OK) return st;
   }
   if (a->nq == 0) return CSA2_OK;
@@ -234,9 +234,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;
   }
-  TimedLaunch t(CSA2_KCLASS_ATTN, s);
+  TimedLaunch t(CSA2_KCLASS_ATTN);
   return hip_status(launch_sparse_attn(ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
-                                       a->lse, attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k), s));
+                                       a->lse, attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k), s, t.ev));
 }
 
 }  // extern "C"

@@ -53,9 +53,13 @@ append_quant_kernel(uint8_t* __restrict__ kv, uint8_t* __restrict__ idx_k,
 }
 
 hipError_t launch_append_quant(uint8_t* kv, uint8_t* idx_k, const int32_t* slots, const uint16_t* kv_rows,
-                               const uint16_t* idxk_rows, int n, hipStream_t s) {
+                               const uint16_t* idxk_rows, int n, hipStream_t s, const KEvents& ev) {
   const int blocks = (n + 3) / 4;
-  hipLaunchKernelGGL(append_quant_kernel, dim3(blocks), dim3(256), 0, s, kv, idx_k, slots, kv_rows, idxk_rows, n);
+  if (blocks <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
+  launch(append_quant_kernel, dim3(blocks), dim3(256), s, ev, kv, idx_k, slots, kv_rows, idxk_rows, n);
   return hipGetLastError();
 }
 

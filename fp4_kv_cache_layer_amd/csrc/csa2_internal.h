@@ -1,5 +1,6 @@
 // Internal launchers of the CSA2 kernels (not part of the C ABI).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -28,6 +29,30 @@ struct IndexWs {
   int64_t vstride;
 };
 
+// Optional device timestamps of one launch class: `start` is taken when its
+// first kernel starts, `stop` when its last kernel ends (recorded by the
+// dispatch itself, so timing adds no separate stream operations).
+struct KEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  KEvents first() const { return {start, nullptr}; }
+  KEvents last() const { return {nullptr, stop}; }
+};
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, const KEvents& ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
+// A launch class that dispatches nothing still completes its events.
+inline void record_empty(const KEvents& ev, hipStream_t s) {
+  if (ev.start) (void)hipEventRecord(ev.start, s);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
+}
+
 constexpr int kHistBits = 11;                // first radix digit of the score key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kScanChunk = 2048;             // entries per scan workgroup
@@ -40,15 +65,15 @@ size_t zero_state_bytes(int32_t nq);
 size_t index_score_bytes(int32_t nq, int32_t max_vis);
 
 hipError_t launch_append_quant(uint8_t* kv, uint8_t* idx_k, const int32_t* slots, const uint16_t* kv_rows,
-                               const uint16_t* idxk_rows, int n, hipStream_t s);
+                               const uint16_t* idxk_rows, int n, hipStream_t s, const KEvents& ev = {});
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                              const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
-                             hipStream_t s);
+                             hipStream_t s, const KEvents& ev = {});
 
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
-                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s);
+                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 
 // Attention shares (small batches split their rows across workgroups):
 // [nq * ceil(h/16)][nsplit][16][512] fp32 partial outputs, then
@@ -58,6 +83,6 @@ size_t attn_part_bytes(int nq, int h, int k);
 
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, hipStream_t s);
+                              void* part, hipStream_t s, const KEvents& ev = {});
 
 }  // namespace csa2

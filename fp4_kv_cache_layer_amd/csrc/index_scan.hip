@@ -122,11 +122,15 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                              const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
-                             hipStream_t s) {
+                             hipStream_t s, const KEvents& ev) {
   const int nchunks = (max_vis + kScanChunk - 1) / kScanChunk;
   const int64_t blocks = (int64_t)nq * nchunks;
-  hipLaunchKernelGGL(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), 0, s, c, q_idx, w, q_seq,
-                     q_vis, h_idx, nchunks, ws);
+  if (blocks <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
+  launch(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, h_idx,
+         nchunks, ws);
   return hipGetLastError();
 }
 

@@ -324,17 +324,21 @@ size_t attn_part_bytes(int nq, int h, int k) {
 
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, hipStream_t s) {
+                              void* part, hipStream_t s, const KEvents& ev) {
+  if (nq <= 0 || h <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
   const int ngroups = (h + 15) / 16;
   const int ns = part ? attn_nsplit(nq, h, k) : 1;
   const int64_t units = (int64_t)nq * ngroups;
   float* part_o = reinterpret_cast<float*>(part);
   float* part_ml = part_o ? part_o + units * ns * 16 * kLatent : nullptr;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)(units * ns)), dim3(kAttnThreads), 0, s, c, q, q_seq, idx,
-                     cnt, h, k, sm_scale, out, lse, ns, part_o, part_ml);
+  launch(sparse_attn_kernel, dim3((unsigned)(units * ns)), dim3(kAttnThreads), s, ns > 1 ? ev.first() : ev, c, q,
+         q_seq, idx, cnt, h, k, sm_scale, out, lse, ns, part_o, part_ml);
   if (ns > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(units * 16)), dim3(128), 0, s, h, ns, part_o, part_ml, out,
-                       lse);
+    launch(attn_combine_kernel, dim3((unsigned)(units * 16)), dim3(128), s, ev.last(), h, ns, part_o, part_ml, out,
+           lse);
   return hipGetLastError();
 }
 

@@ -334,11 +334,15 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
 }
 
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
-                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s) {
+                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
+  if (nq <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
   const int nslices = max(1, (max_vis + kCollectSlice - 1) / kCollectSlice);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)((int64_t)nq * nslices)), dim3(kCollectThreads), 0, s, ws,
-                     q_vis, k, nslices);
-  hipLaunchKernelGGL(topk_final_kernel, dim3(nq), dim3(kSelectThreads), 0, s, ws, q_vis, k, out_idx, out_cnt);
+  launch(topk_collect_kernel, dim3((unsigned)((int64_t)nq * nslices)), dim3(kCollectThreads), s, ev.first(), ws,
+         q_vis, k, nslices);
+  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev.last(), ws, q_vis, k, out_idx, out_cnt);
   return hipGetLastError();
 }
 

@@ -196,9 +196,11 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
 const char* csa2_status_string(csa2_status st);
 
 /* Per-kernel device timing for measurement.  While a ring is installed for
- * a kernel class, every launch of that class records hipEvent pairs
- * start[count] / stop[count] on the launch stream around the kernel and
- * increments count, until count reaches capacity.  Events are created and
+ * a kernel class, every launch of that class records the hipEvent pair
+ * start[count] / stop[count] and increments count, until count reaches
+ * capacity.  The events are carried by the kernel dispatches themselves
+ * (start when the class's first kernel begins, stop when its last kernel
+ * ends), so no separate stream operations are added.  Events are created and
  * destroyed by the caller (hipEventCreate); the ring struct must outlive its
  * installation.  Classes: 0 append, 1 indexer scan, 2 Top-K select,
  * 3 attention.  Pass ring = NULL to uninstall.  Process-wide, not
