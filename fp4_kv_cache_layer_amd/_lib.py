@@ -15,6 +15,7 @@ CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ER
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN = 0, 1, 2, 3
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
+STEP_DENSE_INDEX = 1
 
 
 class CacheView(ctypes.Structure):
@@ -29,7 +30,7 @@ class StepArgs(ctypes.Structure):
                 ("q", c_void_p), ("h", c_int32), ("sm_scale", c_float),
                 ("q_seq", c_void_p), ("q_vis", c_void_p), ("nq", c_int32), ("k", c_int32), ("max_vis", c_int32),
                 ("idx", c_void_p), ("cnt", c_void_p), ("out", c_void_p), ("lse", c_void_p),
-                ("ws", c_void_p), ("ws_bytes", c_size_t)]
+                ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32)]
 
 
 class TimingRing(ctypes.Structure):
@@ -55,13 +56,15 @@ def load() -> ctypes.CDLL:
     lib.csa2_workspace_init.argtypes = [c_void_p, c_size_t, c_void_p]
     lib.csa2_index_topk.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                     c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.csa2_prefill_index_topk.argtypes = lib.csa2_index_topk.argtypes
     lib.csa2_sparse_attn.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
     lib.csa2_status_string.argtypes = [c_int32]
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_set_timing.argtypes = [c_int32, P(TimingRing)]
-    for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_sparse_attn",
+    for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
+               "csa2_sparse_attn",
                "csa2_layer_step", "csa2_set_timing"):
         getattr(lib, fn).restype = c_int32
     _lib = lib

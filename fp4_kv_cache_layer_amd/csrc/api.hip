@@ -121,10 +121,12 @@ void* attn_part(void* ws, size_t ws_bytes, int32_t nq, int32_t h, int32_t k) {
 
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
-                      int32_t* out_cnt, const IndexWs& iw, hipStream_t s) {
+                      int32_t* out_cnt, const IndexWs& iw, bool dense, hipStream_t s) {
   if (max_vis > 0) {
     TimedLaunch t(CSA2_KCLASS_SCAN);
-    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
+    csa2_status st = hip_status(
+        dense ? launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev)
+              : launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
     if (st != CSA2_OK) return st;
   }
   TimedLaunch t(CSA2_KCLASS_SELECT);
@@ -184,7 +186,17 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
-                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), s);
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), false, s);
+}
+
+csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                                    const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis,
+                                    int32_t* out_idx, int32_t* out_cnt, void* ws, size_t ws_bytes, hipStream_t s) {
+  CacheArgs ca;
+  csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
+  if (st != CSA2_OK || nq == 0) return st;
+  return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), true, s);
 }
 
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
@@ -201,6 +213,7 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
   if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & ~CSA2_STEP_DENSE_INDEX) return CSA2_ERR_INVALID_ARG;
   CacheArgs ca;
   csa2_status st;
   if (mode == CSA2_FULL) {
@@ -229,7 +242,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
   if (mode != CSA2_REUSE) {
     if (a->ws_bytes < z + part + index_score_bytes(a->nq, a->max_vis)) return CSA2_ERR_WORKSPACE;
     st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt,
-                   index_ws(a->ws, a->nq, a->max_vis, z + part), s);
+                   index_ws(a->ws, a->nq, a->max_vis, z + part), (a->flags & CSA2_STEP_DENSE_INDEX) != 0, s);
     if (st != CSA2_OK) return st;
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;

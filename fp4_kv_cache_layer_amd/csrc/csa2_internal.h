@@ -72,6 +72,12 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
                              const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
                              hipStream_t s, const KEvents& ev = {});
 
+// Dense form for many queries of one sequence (q_seq[0]): same workspace
+// outputs and bit-identical scores.
+hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                               const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                               hipStream_t s, const KEvents& ev = {});
+
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
                               int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 

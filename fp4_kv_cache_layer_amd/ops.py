@@ -102,7 +102,10 @@ def csa2_append_quant_fp4(cache: Cache, slots: torch.Tensor, kv_rows: torch.Tens
 
 def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor,
                     k: int, max_vis: int, ws: torch.Tensor, out_idx: Optional[torch.Tensor] = None,
-                    out_cnt: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    out_cnt: Optional[torch.Tensor] = None, stream=None,
+                    dense: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Indexer scores + Top-K.  dense=True calls csa2_prefill_index_topk (every
+    query in sequence q_seq[0]: one FP8 matrix product with a causal mask)."""
     nq, h_idx = q_idx.shape[0], q_idx.shape[1]
     _need(q_idx, (torch.uint8,), "q_idx")
     _need(w, (torch.float32,), "w")
@@ -110,7 +113,8 @@ def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: t
         out_idx = torch.empty((nq, k), dtype=torch.int32, device=q_idx.device)
     if out_cnt is None:
         out_cnt = torch.empty(nq, dtype=torch.int32, device=q_idx.device)
-    L.check("csa2_index_topk", L.load().csa2_index_topk(
+    name = "csa2_prefill_index_topk" if dense else "csa2_index_topk"
+    L.check(name, getattr(L.load(), name)(
         ctypes.byref(cache.view), _ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(q_vis), nq, h_idx, k, max_vis,
         _ptr(out_idx), _ptr(out_cnt), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_cnt
@@ -142,7 +146,8 @@ class LayerCall:
                  out: torch.Tensor, lse: Optional[torch.Tensor] = None,
                  q_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
                  new_slots: Optional[torch.Tensor] = None, new_kv: Optional[torch.Tensor] = None,
-                 new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+                 new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 dense: bool = False):
         self.mode = mode
         self.cache = cache
         self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws)
@@ -157,6 +162,7 @@ class LayerCall:
         a.q, a.h, a.sm_scale = _ptr(q), q.shape[1], float(sm_scale)
         a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = _ptr(q_seq), _ptr(q_vis), q.shape[0], k, max_vis
         a.idx, a.cnt, a.out, a.lse = _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse)
+        a.flags = L.STEP_DENSE_INDEX if dense else 0
         self.args = a
         self._ref = ctypes.byref(a)
         self._fn = L.load().csa2_layer_step
@@ -170,9 +176,9 @@ class LayerCall:
 def csa2_layer_step(mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor, k: int,
                     max_vis: int, sm_scale: float, idx: torch.Tensor, cnt: torch.Tensor, out: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, q_idx=None, w=None, new_slots=None, new_kv=None,
-                    new_idxk=None, ws=None, stream=None) -> None:
+                    new_idxk=None, ws=None, stream=None, dense: bool = False) -> None:
     LayerCall(mode, cache, q, q_seq, q_vis, k, max_vis, sm_scale, idx, cnt, out, lse, q_idx, w,
-              new_slots, new_kv, new_idxk, ws)(stream)
+              new_slots, new_kv, new_idxk, ws, dense)(stream)
 
 
 class TimingRing:

@@ -18,8 +18,13 @@ APPEND_CHUNK = 1 << 20          # rows per bulk append call
 
 
 class DeviceCase:
-    def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda"):
+    """dense: None -> the dense prefill indexer for prefill workloads (all
+    queries in one sequence), the per-query scan otherwise."""
+
+    def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda",
+                 dense: Optional[bool] = None):
         self.spec = spec
+        self.dense = spec.prefill if dense is None else dense
         self.device = device
         self.gen_device = gen_device
         pt = torch.from_numpy(W.page_table(spec))
@@ -81,11 +86,11 @@ class DeviceCase:
                 if mode == ops.FULL:
                     call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
                                          idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
-                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=self.ws)
+                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=self.ws, dense=self.dense)
                     full_idx, full_cnt = idx, cnt
                 else:
                     call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                         idx, cnt, out, lse, q_idx=qi, w=w, ws=self.ws)
+                                         idx, cnt, out, lse, q_idx=qi, w=w, ws=self.ws, dense=self.dense)
             self.outputs.append(dict(idx=idx, cnt=cnt, out=out, lse=lse))
             self.calls.append(call)
 

@@ -146,6 +146,20 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
                             int32_t* out_idx, int32_t* out_cnt,
                             void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Dense form of csa2_index_topk for a prefill chunk, where every query
+ * belongs to one sequence (q_seq[i] == q_seq[0] for all i; a device value,
+ * trusted like q_vis).  The scoring then runs as one FP8 matrix product
+ * [nq * h_idx x 128] x [128 x max_vis] under the causal mask t < q_vis[i],
+ * prefill being the computationally expensive phase ("DeepSeek-V4.1-Flash"
+ * research-podcast summary, abstract).  Arguments, outputs, workspace and
+ * errors are those of csa2_index_topk, and the scores - so the selection -
+ * are bit-identical to it. */
+csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,
+                                    const int32_t* q_seq, const int32_t* q_vis,
+                                    int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis,
+                                    int32_t* out_idx, int32_t* out_cnt,
+                                    void* ws, size_t ws_bytes, hipStream_t s);
+
 /* Sparse attention over the selected rows (all three modes end here).
  *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
  *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq],
@@ -184,7 +198,12 @@ typedef struct {
   float*          lse;           /* nullable */
   void*           ws;
   size_t          ws_bytes;
+  uint32_t        flags;         /* CSA2_STEP_* bits, 0 by default            */
 } csa2_step_args;
+
+/* Full/Reindex: score as csa2_prefill_index_topk (all queries of the call
+ * belong to the sequence q_seq[0], e.g. one prefill chunk). */
+#define CSA2_STEP_DENSE_INDEX 1u
 
 /* One CSA2 layer in the given mode:
  *   Full    = append (if n_new > 0) -> index_topk -> sparse_attn

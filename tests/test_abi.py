@@ -21,8 +21,9 @@ def _view(**kw):
 def test_exports_every_header_function():
     lib = L.load()
     names = L.header_functions()
-    assert set(names) >= {"csa2_append_quant_fp4", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_step",
-                          "csa2_workspace_bytes", "csa2_workspace_init", "csa2_status_string", "csa2_set_timing"}
+    assert set(names) >= {"csa2_append_quant_fp4", "csa2_index_topk", "csa2_prefill_index_topk", "csa2_sparse_attn",
+                          "csa2_layer_step", "csa2_workspace_bytes", "csa2_workspace_init", "csa2_status_string",
+                          "csa2_set_timing"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -46,31 +47,37 @@ def test_workspace_bytes():
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
 
 
-def _topk(lib, view, **kw):
+def _topk(lib, view, fn="csa2_index_topk", **kw):
     a = dict(q_idx=FAKE, w=FAKE, q_seq=FAKE, q_vis=FAKE, nq=1, h_idx=8, k=512, max_vis=200,
              out_idx=FAKE, out_cnt=FAKE, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
-    return lib.csa2_index_topk(ctypes.byref(view), a["q_idx"], a["w"], a["q_seq"], a["q_vis"], a["nq"], a["h_idx"],
-                               a["k"], a["max_vis"], a["out_idx"], a["out_cnt"], a["ws"], a["ws_bytes"], None)
+    return getattr(lib, fn)(ctypes.byref(view), a["q_idx"], a["w"], a["q_seq"], a["q_vis"], a["nq"], a["h_idx"],
+                            a["k"], a["max_vis"], a["out_idx"], a["out_cnt"], a["ws"], a["ws_bytes"], None)
+
+
+TOPK_FNS = ["csa2_index_topk", "csa2_prefill_index_topk"]
 
 
 @pytest.mark.parametrize("kw", [dict(h_idx=0), dict(h_idx=17), dict(k=0), dict(k=2049), dict(nq=-1),
                                 dict(max_vis=-1), dict(max_vis=257), dict(q_idx=None), dict(w=None),
                                 dict(out_idx=None), dict(ws=None), dict(q_idx=FAKE + 8)])
-def test_index_topk_rejects(kw):
-    assert _topk(L.load(), _view(), **kw) == L.CSA2_ERR_INVALID_ARG
+@pytest.mark.parametrize("fn", TOPK_FNS)
+def test_index_topk_rejects(kw, fn):
+    assert _topk(L.load(), _view(), fn, **kw) == L.CSA2_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("vkw", [dict(page_size=48), dict(page_size=32), dict(page_size=0), dict(kv=None),
                                  dict(page_table=None), dict(num_pages=0), dict(kv=FAKE + 4)])
-def test_cache_view_rejects(vkw):
-    assert _topk(L.load(), _view(**vkw)) == L.CSA2_ERR_INVALID_ARG
+@pytest.mark.parametrize("fn", TOPK_FNS)
+def test_cache_view_rejects(vkw, fn):
+    assert _topk(L.load(), _view(**vkw), fn) == L.CSA2_ERR_INVALID_ARG
 
 
-def test_index_topk_workspace_too_small_and_empty():
+@pytest.mark.parametrize("fn", TOPK_FNS)
+def test_index_topk_workspace_too_small_and_empty(fn):
     lib = L.load()
-    assert _topk(lib, _view(), ws_bytes=100) == L.CSA2_ERR_WORKSPACE
-    assert _topk(lib, _view(), nq=0, q_idx=None, ws=None) == L.CSA2_OK          # nothing enqueued
+    assert _topk(lib, _view(), fn, ws_bytes=100) == L.CSA2_ERR_WORKSPACE
+    assert _topk(lib, _view(), fn, nq=0, q_idx=None, ws=None) == L.CSA2_OK          # nothing enqueued
 
 
 def _attn(lib, view, **kw):
@@ -111,6 +118,10 @@ def test_layer_step_mode_field_rules():
     assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG   # Full needs q_idx/w/ws
     a.nq = 0
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK              # nothing to do
+    a.flags = 2                                          # unknown flag bit
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.flags = L.STEP_DENSE_INDEX
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
     assert lib.csa2_layer_step(L.CSA2_REUSE, None, None) == L.CSA2_ERR_INVALID_ARG
 
 

@@ -74,17 +74,17 @@ def test_append_bit_exact_every_bf16(arrangement):
 # indexer + Top-K
 # ---------------------------------------------------------------------------
 
-def _run_case(spec):
+def _run_case(spec, dense=None):
     _, runner = _ops()
-    dc = runner.DeviceCase(spec, gen_device="cpu")
+    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense)
     dc.run_group()
     return dc, dc.results_host()
 
 
-def _compare_group(spec, exact_topk: bool):
+def _compare_group(spec, exact_topk: bool, dense=None):
     say(f"[group] {spec.name} seed={spec.seed} seqs={spec.num_seqs} cached={spec.cached[:6]} "
-        f"n_new={spec.n_new} h_idx={spec.h_idx} h={spec.h} k={spec.k} int={spec.integer_indexer}")
-    dc, got = _run_case(spec)
+        f"n_new={spec.n_new} h_idx={spec.h_idx} h={spec.h} k={spec.k} int={spec.integer_indexer} dense={dense}")
+    dc, got = _run_case(spec, dense)
     case = CB.build(spec)
     ref = CB.run_group(case)
     # oracle cache after the Full layer's append, to evaluate attention over the GPU's selection
@@ -145,10 +145,46 @@ def test_config0_exact():
     _compare_group(spec, exact_topk=True)
 
 
-def test_prefill_small_causal():
+@pytest.mark.parametrize("dense", [True, False])
+def test_prefill_small_causal(dense):
     spec = W.small_case("prefill", 41, [1500], n_new=300, h_idx=8, h=32, k=256, modes=(O.FULL,), prefill=True,
                         integer_indexer=True)
-    _compare_group(spec, exact_topk=True)
+    _compare_group(spec, exact_topk=True, dense=dense)
+
+
+@pytest.mark.parametrize("seed,cached,n_new,h_idx,k", [
+    (42, [2000], 37, 12, 512),       # one query per A tile, ragged query block
+    (43, [700], 130, 3, 128),        # short context: most entries causal-masked for early queries
+])
+def test_prefill_dense_integer_exact(seed, cached, n_new, h_idx, k):
+    spec = W.small_case("prefill_int", seed, cached, n_new=n_new, h_idx=h_idx, h=16, k=k, modes=(O.FULL,),
+                        prefill=True, integer_indexer=True)
+    _compare_group(spec, exact_topk=True, dense=True)
+
+
+def test_prefill_dense_gaussian():
+    spec = W.small_case("prefill_gauss", 44, [5000], n_new=200, h_idx=8, h=64, k=512, modes=(O.FULL, O.REINDEX),
+                        prefill=True)
+    _compare_group(spec, exact_topk=False, dense=True)
+
+
+@pytest.mark.parametrize("seed,cached,n_new,h_idx,page_size", [
+    (45, [6000], 300, 8, 64),
+    (46, [40000], 45, 8, 64),        # several chunks per XCD (64-entry pages cap a chunk at 63 pages)
+    (47, [3000], 77, 12, 128),
+    (48, [2500], 19, 3, 64),
+])
+def test_prefill_dense_bit_identical_to_scan(seed, cached, n_new, h_idx, page_size):
+    """The dense prefill indexer and the per-query scan produce identical
+    scores, so the whole layer output matches bit for bit."""
+    spec = W.small_case("prefill_same", seed, cached, n_new=n_new, h_idx=h_idx, h=16, k=512,
+                        modes=(O.FULL, O.REINDEX), prefill=True, page_size=page_size)
+    say(f"[dense=scan] seed={seed} cached={cached} n_new={n_new} h_idx={h_idx} page={page_size}")
+    _, a = _run_case(spec, dense=True)
+    _, b = _run_case(spec, dense=False)
+    for li, (x, y) in enumerate(zip(a, b)):
+        for key in ("idx", "cnt", "out", "lse"):
+            assert np.array_equal(x[key], y[key]), (li, key)
 
 
 def test_all_equal_scores_take_lowest_indices():
