@@ -20,6 +20,9 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the epilogues read every
+    # accumulator, and an AGPR result would cost one copy per register
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -108,6 +108,7 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   r.vstride = index_vstride(max_vis);
   r.scores = reinterpret_cast<float*>(p + score_off);
   r.cand = reinterpret_cast<int32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
+  r.mask = reinterpret_cast<uint64_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
   return r;
 }
 
@@ -122,11 +123,19 @@ void* attn_part(void* ws, size_t ws_bytes, int32_t nq, int32_t h, int32_t k) {
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
                       int32_t* out_cnt, const IndexWs& iw, bool dense, hipStream_t s) {
+  if (dense) {
+    // the dense indexer leaves a compacted candidate list: only the final select remains
+    if (max_vis > 0) {
+      TimedLaunch t(CSA2_KCLASS_SCAN);
+      csa2_status st = hip_status(launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, s, t.ev));
+      if (st != CSA2_OK) return st;
+    }
+    TimedLaunch t(CSA2_KCLASS_SELECT);
+    return hip_status(launch_topk_final(iw, q_vis, nq, k, out_idx, out_cnt, s, t.ev));
+  }
   if (max_vis > 0) {
     TimedLaunch t(CSA2_KCLASS_SCAN);
-    csa2_status st = hip_status(
-        dense ? launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev)
-              : launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
+    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
     if (st != CSA2_OK) return st;
   }
   TimedLaunch t(CSA2_KCLASS_SELECT);
@@ -153,6 +162,12 @@ csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring) {
   if (ring && (ring->capacity < 0 || (ring->capacity > 0 && (!ring->start || !ring->stop))))
     return CSA2_ERR_INVALID_ARG;
   g_rings[kernel_class] = ring;
+  return CSA2_OK;
+}
+
+csa2_status csa2_set_prefill_candidate_factor(int32_t factor) {
+  if (factor < 0 || factor > 64) return CSA2_ERR_INVALID_ARG;
+  g_prefill_cand_factor = factor;
   return CSA2_OK;
 }
 

@@ -74,6 +74,33 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One lane's 32-byte MFMA operand (V_MFMA_*_F8F6F4, K = 128) from a 128-byte
+// FP8 row: lanes 16g .. 16g+15 take bytes [16g, +16) and [64 + 16g, +16).
+// This is a fixed permutation of K applied to both operands alike, so the
+// product is unchanged; each 16-lane load then covers one contiguous half of
+// every row it touches.  All indexer paths use it, so their scores agree bit
+// for bit.
+__device__ __forceinline__ intx8 load_fp8_operand(const uint8_t* row, int g) {
+  const intx4 lo = *reinterpret_cast<const intx4*>(row + 16 * g);
+  const intx4 hi = *reinterpret_cast<const intx4*>(row + 64 + 16 * g);
+  return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// max(x, 0) as one integer max on the bit pattern: negative values (sign bit
+// set, -0 included) map to +0; used by every indexer path so their scores
+// agree bit for bit.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// This lane's share sum_i w_i * max(0, acc_i) over its 4 MFMA output rows.
+__device__ __forceinline__ float relu_weighted(const floatx4& acc, const float (&wv)[4]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += wv[i] * relu_bits(acc[i]);
+  return s;
+}
+
 // E8M0 byte -> fp32 scale 2^(b-127); byte 0 is the subnormal 2^-127.
 __device__ __forceinline__ float e8m0_to_float(uint32_t b) {
   return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);

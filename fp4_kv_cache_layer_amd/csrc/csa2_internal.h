@@ -20,12 +20,15 @@ struct CacheArgs {
 //               counters [nq] u32; the final select kernel leaves every row
 //               it used zeroed again.
 //   [Z, ...)    scores [nq][vstride] fp32, then candidate indices
-//               [nq][vstride] i32; no initial state needed.
+//               [nq][vstride] i32, then (dense prefill indexer) candidate
+//               masks, round_up(nq, 16) * vstride / 8 bytes; no initial
+//               state needed.
 struct IndexWs {
   uint32_t* hist;
   uint32_t* cand_cnt;
   float* scores;
   int32_t* cand;
+  uint64_t* mask;
   int64_t vstride;
 };
 
@@ -72,11 +75,19 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
                              const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
                              hipStream_t s, const KEvents& ev = {});
 
-// Dense form for many queries of one sequence (q_seq[0]): same workspace
-// outputs and bit-identical scores.
+// Dense form for many queries of one sequence (q_seq[0]): leaves the same
+// inputs for the final select (candidate list, candidate histogram, scores of
+// the candidates), with scores bit-identical to the per-query scan.  Its events
+// cover the threshold, candidate, full-rescore and compaction kernels.
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
-                               const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                               const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                                hipStream_t s, const KEvents& ev = {});
+// Expected candidates per query of the dense indexer, in units of k (0 sends
+// every query through the full rescore).
+extern int g_prefill_cand_factor;
+// Launches of the final select alone (the dense indexer compacts its own candidates).
+hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
+                             int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
                               int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});

@@ -10,9 +10,8 @@
 // Dot products run on the gfx950 FP8 matrix core: one
 // V_MFMA_F32_16X16X128_F8F6F4 multiplies the (zero-padded to 16) indexer
 // heads by 16 entries over the full 128-wide dimension.  Lane l supplies
-// head / entry (l % 16) and bytes [32*(l/16), +32) of its row, so each lane
-// streams 32 contiguous bytes of one indexer-K row per tile and a wave
-// streams 2 KB.  The result puts entry (l % 16) and heads 4*(l/16)+i in lane
+// head / entry (l % 16) and 32 bytes of its row (load_fp8_operand), so a wave
+// streams one 2 KB tile of 16 indexer-K rows per MFMA.  The result puts entry (l % 16) and heads 4*(l/16)+i in lane
 // l, so the ReLU * w reduction is 4 FMAs and two cross-lane adds.
 #include "csa2_device.h"
 #include "csa2_internal.h"
@@ -22,13 +21,20 @@ namespace csa2 {
 constexpr int kScanWaves = 4;
 constexpr int kScanUnroll = 4;          // 16-entry tiles in flight per wave
 
-int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 63) / 64 * 64; }
+// Row stride of the per-query score and candidate arrays: at least one slot
+// past the longest visible range, which the dense indexer uses as a write
+// sink that is never read.
+int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 1 + 63) / 64 * 64; }
 
 size_t zero_state_bytes(int32_t nq) {
   return ((size_t)nq * (kHistBins + 1) * 4 + 255) / 256 * 256;
 }
 
-size_t index_score_bytes(int32_t nq, int32_t max_vis) { return 2 * (size_t)nq * (size_t)index_vstride(max_vis) * 4; }
+size_t index_score_bytes(int32_t nq, int32_t max_vis) {
+  const size_t v = (size_t)index_vstride(max_vis);
+  const size_t nq16 = ((size_t)nq + 15) / 16 * 16;      // candidate masks cover whole 16-query blocks
+  return (size_t)nq * 8 * v + nq16 * v / 8;
+}
 
 __global__ void __launch_bounds__(kScanWaves * 64)
 index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -48,9 +54,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int g = lane >> 4, r = lane & 15;
   intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
   if (r < h_idx) {
-    const intx4* src = reinterpret_cast<const intx4*>(q_idx + ((int64_t)q * h_idx + r) * kIndexDim + 32 * g);
-    const intx4 lo = src[0], hi = src[1];
-    a = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    a = load_fp8_operand(q_idx + ((int64_t)q * h_idx + r) * kIndexDim, g);
   }
   float wv[4];
 #pragma unroll
@@ -80,9 +84,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       const int ts = t0 + 16 * j;
       const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
       const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
-      const intx4* src = reinterpret_cast<const intx4*>(c.idx_k + row * kIndexDim + 32 * g);
-      const intx4 lo = src[0], hi = src[1];
-      b[u] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      b[u] = load_fp8_operand(c.idx_k + row * kIndexDim, g);
     }
   };
   constexpr int kStride = kScanWaves * kScanUnroll;
@@ -96,9 +98,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       if (j >= ntiles) break;
       floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, cur[u], acc, 0, 0, 0, 0, 0, 0);
-      float part = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part += wv[i] * fmaxf(acc[i], 0.0f);
+      float part = relu_weighted(acc, wv);
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       const int t = t0 + 16 * j + r;

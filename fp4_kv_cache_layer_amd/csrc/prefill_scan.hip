@@ -1,42 +1,69 @@
 // Dense indexer for a prefill chunk: s[i, t] = sum_h w[i, h] * max(0, q[i, h] . k_t)
 // for many query rows of ONE sequence at once, as an FP8 matrix product with a
-// causal mask (query i sees entries t < q_vis[i]).
+// causal mask (query i sees entries t < q_vis[i]), followed by an exact
+// Top-K over the candidates it keeps.
 //
 // Prefill is the computationally expensive phase ("DeepSeek-V4.1-Flash"
 // research-podcast summary, abstract); the indexer scoring it runs is the one
 // of the Full and Reindex modes ("Unlocking Extreme Context Scaling with
 // DeepSeek-V4.1-Flash", section "Compressed Sparse Attention 2 (CSA2)").
 //
-// Shape: A = the queries' indexer heads ([nq * h_idx] x 128 E4M3), B = the
-// sequence's indexer-K rows (128 x V E4M3); every output element needs a
-// ReLU and a weight before the per-query sum over heads, so the epilogue is
-// about as long as the matrix product itself and the two must overlap.
+// Writing every score (4 B per query and entry) would cost more HBM time than
+// the matrix product, so only candidates are kept:
 //
-// Workgroup = 8 waves; it owns 8 A tiles of 16 rows (QPT queries x 16/QPT
-// heads each, held in registers by every wave) and one chunk of entries,
-// which its waves stream as 16-entry B tiles straight from memory into MFMA
-// operands (V_MFMA_F32_16X16X128_F8F6F4: lane l supplies row / entry l % 16,
-// bytes [32*(l/16), +32)).  Each B tile feeds 8 MFMAs.  Workgroups that
-// share a chunk run on the same XCD, so the chunk's indexer-K stays in that
-// XCD's L2 while every query block streams it.
+//  1. threshold (prefill_tau_kernel): each query scores a stratified sample
+//     of 512 visible entries and takes the r-th largest sample score as its
+//     threshold, r chosen so that about factor * k entries are expected to
+//     pass.  Queries with V <= k need no threshold; short contexts keep all.
+//  2. candidates (prefill_scan_kernel, first pass): the product itself; an
+//     entry whose score reaches the threshold has its score stored at its
+//     position and its bit set in a per-(query, 16-entry tile) mask; each
+//     query counts its candidates.
+//  3. exactness (same kernel, second launch): a query with fewer than k
+//     candidates (the sample was unlucky) is rescored in full with every
+//     visible entry a candidate; blocks without such a query exit at once.
+//  4. compaction (prefill_compact_kernel): masks -> ordered candidate list,
+//     plus the 2,048-bin histogram of the candidates' score keys, which is all
+//     the final select needs: every entry at or above the k-th key is a
+//     candidate, so the k-th key and the entries above it are the same as
+//     over all entries.
 //
-// Output: the same workspace as the per-query scan (fp32 scores per query
-// row and a 2,048-bin histogram of the score key's top 11 bits), so the
-// Top-K select is shared.  With QPT = 2 every score is the same fma chain and
-// cross-row add as in the per-query scan, so both produce identical bits.
+// Matrix product: A = the queries' indexer heads ([nq * h_idx] x 128 E4M3),
+// B = the sequence's indexer-K rows (128 x V E4M3).  A workgroup of 4 waves
+// owns 8 A tiles of 16 rows (QPT queries x 16/QPT heads each, held in
+// registers by every wave) and one chunk of entries, which its waves stream as
+// 16-entry B tiles straight into MFMA operands (V_MFMA_F32_16X16X128_F8F6F4:
+// lane l supplies row / entry l % 16 and 32 bytes of it, load_fp8_operand);
+// each B tile feeds 8 MFMAs.  Workgroups sharing a chunk run on the same XCD, so the
+// chunk's indexer-K stays in that XCD's L2.  Every score is the same fma
+// chain and cross-row add as in the per-query scan, so both produce
+// identical bits.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
 namespace csa2 {
 
-constexpr int kPfWaves = 8;
+int g_prefill_cand_factor = 4;
+
+namespace {
+
+constexpr int kPfWaves = 4;
 constexpr int kPfTiles = 8;             // A tiles per workgroup
 constexpr int kPfMaxChunk = 16384;      // entries per workgroup at most
-constexpr int kPfUnroll = 2;            // B tiles in flight per wave
+constexpr int kTauWaves = 4;
+constexpr int kSampleTiles = 32;        // 512 sampled entries per query
+constexpr int kMaxRank = 64;
+constexpr int kCompactThreads = 512;
+constexpr int kSlotRow = 144;           // LDS row pitch of a staged B tile (128 bytes + 16 of padding)
+
+// Per-wave LDS of the candidate pass: the staged B tile.
+struct PfShared {
+  uint8_t tile[kPfWaves][16 * kSlotRow];
+};
 
 // Entries per chunk and chunks per XCD for a given visible range; chunks never
 // span more than 64 pages (one page id per lane).
-static void prefill_chunking(int max_vis, int lg_page, int* chunk, int* per_xcd) {
+void prefill_chunking(int max_vis, int lg_page, int* chunk, int* per_xcd) {
   const int cap = min(kPfMaxChunk, 63 << lg_page);
   int m = 1;
   while ((max_vis + 8 * m - 1) / (8 * m) > cap) ++m;
@@ -45,69 +72,189 @@ static void prefill_chunking(int max_vis, int lg_page, int* chunk, int* per_xcd)
   *per_xcd = m;
 }
 
+// A tile t and the weights of output rows 4g .. 4g+3 for queries q0 + QPT*t ...
 template <int QPT>
+__device__ __forceinline__ void load_a_tile(const uint8_t* q_idx, const float* w, int nq, int h_idx, int qt,
+                                            int r, int g, intx8& a, float (&wv)[4]) {
+  constexpr int kHeadsPerTile = 16 / QPT;
+  const int qa = qt + r / kHeadsPerTile, ha = r % kHeadsPerTile;
+  a = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (qa < nq && ha < h_idx) a = load_fp8_operand(q_idx + ((int64_t)qa * h_idx + ha) * kIndexDim, g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * g + i;
+    const int qw = qt + m / kHeadsPerTile, hw = m % kHeadsPerTile;
+    wv[i] = (qw < nq && hw < h_idx) ? w[(int64_t)qw * h_idx + hw] : 0.0f;
+  }
+}
+
+// Rows 0/1 and 2/3 exchange halves: row 0 gets x_row0 + x_row1, row 1 gets
+// y_row0 + y_row1, row 2 gets x_row2 + x_row3, row 3 gets y_row2 + y_row3.
+__device__ __forceinline__ float pair_rows2(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int row16_sum(int x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. threshold per query from a stratified sample
+// ---------------------------------------------------------------------------
+template <int QPT>
+__global__ void __launch_bounds__(kTauWaves * 64)
+prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis, int nq, int h_idx, int k,
+                   int factor, IndexWs ws) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int qt = (blockIdx.x * kTauWaves + wave) * QPT;       // first query of this wave's A tile
+  if (qt >= nq) return;                                       // wave-uniform; no barriers below
+
+  // the output row of this lane holds query qrow (QPT = 2: rows 0,1 -> qt, rows 2,3 -> qt+1)
+  const int qrow = qt + (QPT == 2 ? (g >> 1) : 0);
+  const bool valid = qrow < nq;
+  const int V = valid ? q_vis[qrow] : 0;
+  int vmin = q_vis[qt];
+  if (QPT == 2 && qt + 1 < nq) vmin = min(vmin, q_vis[qt + 1]);
+  const int ntv = vmin >> 4;                                  // 16-entry tiles visible to the whole tile
+
+  // rank r in the sample; 0 = no sampled threshold for this row
+  float tau;
+  int rank = 0;
+  if (!valid || V <= k || factor == 0) {
+    tau = INFINITY;                                           // nothing to keep (V <= k selects everything)
+  } else {
+    const int64_t rr = ((int64_t)factor * k * (16 * kSampleTiles) + V - 1) / V;
+    if (rr > kMaxRank || ntv < kSampleTiles) tau = -INFINITY; // keep every visible entry
+    else { tau = -INFINITY; rank = (int)rr; }
+  }
+  if (__builtin_amdgcn_ballot_w64(rank > 0)) {
+    intx8 a;
+    float wv[4];
+    load_a_tile<QPT>(q_idx, w, nq, h_idx, qt, r, g, a, wv);
+    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qt] * c.max_pages;
+    float vals[kSampleTiles];
+#pragma unroll
+    for (int j = 0; j < kSampleTiles; ++j) {
+      const int ts = (j * ntv / kSampleTiles) * 16;
+      const int page = pt_row[ts >> c.lg_page];
+      const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
+      const intx8 b = load_fp8_operand(c.idx_k + row * kIndexDim, g);
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+      float s = rows_pair_sum(relu_weighted(acc, wv));
+      if (QPT == 1) s = halves_sum(s);
+      vals[j] = s;
+    }
+    // r-th largest of the row's 16 x 32 values: take out the current maximum
+    // (all copies) until r values have been taken out
+    int left = rank;
+    for (int it = 0; it < kMaxRank && __builtin_amdgcn_ballot_w64(left > 0); ++it) {
+      float m = vals[0];
+#pragma unroll
+      for (int j = 1; j < kSampleTiles; ++j) m = fmaxf(m, vals[j]);
+      m = row16_max(m);
+      int ceq = 0;
+#pragma unroll
+      for (int j = 0; j < kSampleTiles; ++j) ceq += vals[j] == m ? 1 : 0;
+      ceq = row16_sum(ceq);
+      if (left > 0) {
+        if (ceq >= left) { tau = m; left = 0; }
+        else left -= ceq;
+      }
+#pragma unroll
+      for (int j = 0; j < kSampleTiles; ++j) vals[j] = vals[j] == m ? -INFINITY : vals[j];
+    }
+  }
+  const bool writer = r == 0 && (QPT == 1 ? g == 0 : (g & 1) == 0);
+  if (writer && valid) ws.hist[(int64_t)qrow * kHistBins] = __float_as_uint(tau);
+}
+
+// ---------------------------------------------------------------------------
+// 2./3. candidate pass (RESCORE = false) and full rescore of short queries
+// ---------------------------------------------------------------------------
+template <int QPT, bool RESCORE>
 __global__ void __launch_bounds__(kPfWaves * 64)
 prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
-                    int nq, int h_idx, int chunk, int per_xcd, IndexWs ws) {
+                    int nq, int h_idx, int k, int chunk, int per_xcd, IndexWs ws) {
   constexpr int kQ = kPfTiles * QPT;                 // queries per workgroup
-  __shared__ uint32_t hist[kQ * kHistBins];
+  __shared__ PfShared S;
   const int b = blockIdx.x;
   const int chunk_id = (b & 7) + 8 * ((b >> 3) % per_xcd);
   const int q0 = ((b >> 3) / per_xcd) * kQ;
   const int e0 = chunk_id * chunk;
 
-  // visible range of the block's queries (uniform loads)
+  // visible range of the block's queries; the rescore pass only serves
+  // queries left with fewer than k candidates (uniform loads)
   int vmax = 0;
+  bool any_fail = false;
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) vmax = max(vmax, (q0 + j < nq) ? q_vis[q0 + j] : 0);
-  if (e0 >= vmax) return;                            // uniform for the block
+  for (int j = 0; j < kQ; ++j) {
+    const int v = (q0 + j < nq) ? q_vis[q0 + j] : 0;
+    vmax = max(vmax, v);
+    if (RESCORE && v > k && (int)ws.cand_cnt[q0 + j] < k) any_fail = true;
+  }
+  if (RESCORE && !any_fail) return;                  // uniform for the block
+  if (e0 >= vmax) return;
   const int e1 = min(e0 + chunk, vmax);
 
-  const int tid = threadIdx.x;
-  {
-    uint4* h4 = reinterpret_cast<uint4*>(hist);
-    for (int i = tid; i < kQ * kHistBins / 4; i += kPfWaves * 64) h4[i] = make_uint4(0, 0, 0, 0);
-  }
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile indices stay scalar
   const int g = lane >> 4, r = lane & 15;
-
-  // A tiles and head weights: tile t row m is query q0 + QPT*t + m/(16/QPT),
-  // head m % (16/QPT); lane (r, g) holds row r's bytes [32g, +32) and the
-  // weights of output rows 4g .. 4g+3.
-  constexpr int kHeadsPerTile = 16 / QPT;
   intx8 a[kPfTiles];
   float wv[kPfTiles][4];
 #pragma unroll
-  for (int t = 0; t < kPfTiles; ++t) {
-    const int qa = q0 + QPT * t + r / kHeadsPerTile, ha = r % kHeadsPerTile;
-    a[t] = intx8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (qa < nq && ha < h_idx) {
-      const intx4* src = reinterpret_cast<const intx4*>(q_idx + ((int64_t)qa * h_idx + ha) * kIndexDim + 32 * g);
-      const intx4 lo = src[0], hi = src[1];
-      a[t] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      const int qw = q0 + QPT * t + m / kHeadsPerTile, hw = m % kHeadsPerTile;
-      wv[t][i] = (qw < nq && hw < h_idx) ? w[(int64_t)qw * h_idx + hw] : 0.0f;
-    }
-  }
+  for (int t = 0; t < kPfTiles; ++t) load_a_tile<QPT>(q_idx, w, nq, h_idx, q0 + QPT * t, r, g, a[t], wv[t]);
 
   // After the head sums, output set p puts query ql(p, g) in lane row g:
   //   QPT = 2: tiles 2p and 2p+1 -> ql = 4p + 2*(g & 1) + (g >> 1)
   //   QPT = 1: tiles 4p .. 4p+3   -> ql = 4p + g
+  // Candidate masks: per (query block, set, 16-entry tile) one 64-bit word
+  // whose bit 16g + r marks entry 16*tile + r of query ql(p, g).
   constexpr int kSets = kPfTiles * QPT / 4;
   int vis_of[kSets];
-  float* srow[kSets];
+  float tau_of[kSets];
+  uint32_t soff[kSets];                              // byte offset of (query ql, entry r) in the block's score rows
+  uint64_t own_rows[kSets];                          // rows whose query this pass writes
 #pragma unroll
   for (int p = 0; p < kSets; ++p) {
     const int ql = (QPT == 2) ? 4 * p + 2 * (g & 1) + (g >> 1) : 4 * p + g;
     const int qg = q0 + ql;
-    vis_of[p] = qg < nq ? q_vis[qg] : 0;
-    srow[p] = ws.scores + (int64_t)min(qg, nq - 1) * ws.vstride;
+    const bool valid = qg < nq;
+    const int v = valid ? q_vis[qg] : 0;
+    bool own;
+    if (RESCORE) {
+      own = valid && v > k && (int)ws.cand_cnt[qg] < k;
+      tau_of[p] = -INFINITY;
+    } else {
+      own = valid;
+      tau_of[p] = valid ? __uint_as_float(ws.hist[(int64_t)qg * kHistBins]) : INFINITY;
+    }
+    vis_of[p] = own ? v : 0;
+    soff[p] = (uint32_t)(ql * (int)ws.vstride + r) * 4u;
+    own_rows[p] = __builtin_amdgcn_ballot_w64(own);
   }
+  auto own_rows_of = [&](int ps) {
+    uint64_t o = own_rows[0];
+#pragma unroll
+    for (int p = 1; p < kSets; ++p) o = ps == p ? own_rows[p] : o;
+    return o;
+  };
+  float* const sblock = ws.scores + (int64_t)q0 * ws.vstride;
+  const int64_t mtiles = ws.vstride >> 4;
+  uint64_t* const mblock = ws.mask + (int64_t)(q0 / kQ) * mtiles * kSets;
 
   // page ids of the chunk, one per lane
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q0] * c.max_pages;
@@ -115,73 +262,209 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   const int npg = ((e1 - 1) >> c.lg_page) - pg0 + 1;
   const int page_of_lane = lane < npg ? pt_row[pg0 + lane] : 0;
   const int ntiles = (e1 - e0 + 15) >> 4;
-  lds_barrier();
 
-  auto load = [&](int j, intx8& bt) {
-    j = min(j, ntiles - 1);
-    const int ts = e0 + 16 * j;
+  // Every query block streams the same chunk; starting each block at its own
+  // offset keeps the XCD's workgroups from requesting the same tile at the
+  // same moment, so all but the first reader of a tile hit in L2.
+  const int rot = (int)(((int64_t)((b >> 3) / per_xcd) * 37) % ntiles);
+  auto tile_at = [&](int j) {                        // j-th tile of this block's rotated order
+    j = min(j, ntiles - 1) + rot;
+    return j >= ntiles ? j - ntiles : j;
+  };
+  // A tile's 16 rows are 2 KB of contiguous memory; lane l loads bytes
+  // [32l, +32), so every group of four lanes reads one whole 128-byte row.
+  auto load = [&](int j, intx8& lin) {
+    const int ts = e0 + 16 * tile_at(j);
     const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
-    const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
-    const intx4* src = reinterpret_cast<const intx4*>(c.idx_k + row * kIndexDim + 32 * g);
-    const intx4 lo = src[0], hi = src[1];
-    bt = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint8_t* tb = c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim;
+    const intx4 lo = *reinterpret_cast<const intx4*>(tb + 32 * lane);
+    const intx4 hi = *reinterpret_cast<const intx4*>(tb + 32 * lane + 16);
+    lin = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // ... and the wave turns it into the MFMA operand through its own LDS
+  // slot (rows padded to 144 bytes, so both accesses are bank-conflict free).
+  uint8_t* const slot = S.tile[wave];
+  auto to_operand = [&](const intx8& lin) {
+    uint8_t* wr = slot + (lane >> 2) * kSlotRow + 32 * (lane & 3);
+    *reinterpret_cast<intx4*>(wr) = intx4{lin[0], lin[1], lin[2], lin[3]};
+    *reinterpret_cast<intx4*>(wr + 16) = intx4{lin[4], lin[5], lin[6], lin[7]};
+    const uint8_t* rd = slot + r * kSlotRow;
+    const intx4 lo = *reinterpret_cast<const intx4*>(rd + 16 * g);
+    const intx4 hi = *reinterpret_cast<const intx4*>(rd + 64 + 16 * g);
+    return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  intx8 cur[kPfUnroll], nxt[kPfUnroll];
+  // Scores of one tile for output set p (see ql above): the set's matrix
+  // products are issued one set ahead of their epilogue, so the epilogue never
+  // waits on a product that was just issued.
+  constexpr int kPerSet = 4 / QPT;                   // MFMAs per output set
+  auto products = [&](const intx8& bop, int p, floatx4 (&acc)[kPerSet]) {
 #pragma unroll
-  for (int u = 0; u < kPfUnroll; ++u) load(wave + kPfWaves * u, cur[u]);
-  constexpr int kStride = kPfWaves * kPfUnroll;
-  for (int base = wave; base < ntiles; base += kStride) {
-#pragma unroll
-    for (int u = 0; u < kPfUnroll; ++u) load(base + kStride + kPfWaves * u, nxt[u]);
-#pragma unroll
-    for (int u = 0; u < kPfUnroll; ++u) {
-      const int j = base + kPfWaves * u;
-      if (j >= ntiles) break;
-      const int te = e0 + 16 * j;
-      float part[kPfTiles];
-#pragma unroll
-      for (int t = 0; t < kPfTiles; ++t) {
-        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[t], cur[u], acc, 0, 0, 0, 0, 0, 0);
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += wv[t][i] * fmaxf(acc[i], 0.0f);
-        s = rows_pair_sum(s);
-        if (QPT == 1) s = halves_sum(s);
-        part[t] = s;
-      }
-      const int e = te + r;
-#pragma unroll
-      for (int p = 0; p < kSets; ++p) {
-        float s;
-        if (QPT == 2) {
-          s = (g & 1) ? part[2 * p + 1] : part[2 * p];
-        } else {
-          s = g == 0 ? part[4 * p] : g == 1 ? part[4 * p + 1] : g == 2 ? part[4 * p + 2] : part[4 * p + 3];
-        }
-        const int ql = (QPT == 2) ? 4 * p + 2 * (g & 1) + (g >> 1) : 4 * p + g;
-        if (e < vis_of[p]) {                         // causal mask; 0 for padding queries
-          uint32_t u32 = __float_as_uint(s);
-          if ((u32 << 1) == 0) u32 = 0;              // -0 -> +0
-          srow[p][e] = __uint_as_float(u32);
-          atomicAdd(&hist[ql * kHistBins + (score_key(__uint_as_float(u32)) >> (32 - kHistBits))], 1u);
-        }
-      }
+    for (int i = 0; i < kPerSet; ++i) {
+      acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[kPerSet * p + i], bop, acc[i], 0, 0, 0, 0, 0, 0);
     }
+  };
+  auto finish = [&](int p, const floatx4 (&acc)[kPerSet]) {
+    if (QPT == 2) {
+      return pair_rows2(relu_weighted(acc[0], wv[2 * p]), relu_weighted(acc[1], wv[2 * p + 1]));
+    } else {
+      float sq[4];
 #pragma unroll
-    for (int u = 0; u < kPfUnroll; ++u) cur[u] = nxt[u];
+      for (int i = 0; i < 4; ++i) sq[i] = halves_sum(rows_pair_sum(relu_weighted(acc[i], wv[4 * p + i])));
+      return g == 0 ? sq[0] : g == 1 ? sq[1] : g == 2 ? sq[2] : sq[3];
+    }
+  };
+  auto set_scores = [&](const intx8& bop, int p) {
+    floatx4 acc[kPerSet];
+    products(bop, p, acc);
+    return finish(p, acc);
+  };
+
+  uint32_t cnt[kSets][4];                            // candidates per (set, row): wave-uniform
+#pragma unroll
+  for (int p = 0; p < kSets; ++p)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) cnt[p][gg] = 0;
+  // sink: last score slot of the block's first row, never read
+  const uint32_t sink_off = (uint32_t)(ws.vstride - 1) * 4u;
+
+  auto process = [&](int j, const intx8& lin) {
+    const int te = e0 + 16 * tile_at(j);
+    const int e = te + r;
+    const intx8 bop = to_operand(lin);
+    char* const st = reinterpret_cast<char*>(sblock) + (uint32_t)te * 4u;
+    // lanes without a candidate store into the sink slot (last slot of the
+    // block's first row, never read), so every store is unconditional and
+    // the compiler can count the loads in flight past them
+    const uint32_t sink = sink_off - (uint32_t)te * 4u;
+    uint64_t masks[kSets];
+    floatx4 cur[kPerSet], nxt[kPerSet];
+    products(bop, 0, cur);
+#pragma unroll
+    for (int p = 0; p < kSets; ++p) {
+      if (p + 1 < kSets) products(bop, p + 1, nxt);
+      const float sc = finish(p, cur);
+      const bool keep = e < vis_of[p] && sc >= tau_of[p];   // causal mask, threshold
+      const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+      masks[p] = m;
+      *reinterpret_cast<float*>(st + (keep ? soff[p] : sink)) = sc;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) cnt[p][gg] += (uint32_t)__builtin_popcountll(m & (0xFFFFull << (16 * gg)));
+#pragma unroll
+      for (int i = 0; i < kPerSet; ++i) cur[i] = nxt[i];
+    }
+    // one store for the tile's masks: lane l writes the word of set l % kSets
+    uint64_t* const mt = mblock + (te >> 4);
+    const int ps = lane & (kSets - 1);
+    uint64_t mw = masks[0];
+#pragma unroll
+    for (int p = 1; p < kSets; ++p) mw = ps == p ? masks[p] : mw;
+    if (RESCORE) {
+      const uint64_t orow = own_rows_of(ps);
+      mt[ps * mtiles] = (mt[ps * mtiles] & ~orow) | mw;   // every lane of set ps writes the same word
+    } else {
+      mt[ps * mtiles] = mw;
+    }
+  };
+  // B tiles j = wave, wave + 4, ...; two tiles in flight ahead of the one in
+  // use, in three buffers that rotate by name (unrolled by three)
+  intx8 l0, l1, l2;
+  load(wave, l0);
+  load(wave + kPfWaves, l1);
+  for (int j = wave; j < ntiles; j += 3 * kPfWaves) {
+    load(j + 2 * kPfWaves, l2);
+    process(j, l0);
+    if (j + kPfWaves >= ntiles) break;
+    load(j + 3 * kPfWaves, l0);
+    process(j + kPfWaves, l1);
+    if (j + 2 * kPfWaves >= ntiles) break;
+    load(j + 4 * kPfWaves, l1);
+    process(j + 2 * kPfWaves, l2);
   }
-  lds_barrier();
-  for (int i = tid; i < kQ * kHistBins; i += kPfWaves * 64) {
-    const int ql = i / kHistBins;
-    const uint32_t v = hist[i];
-    if (v && q0 + ql < nq) atomicAdd(&ws.hist[(int64_t)(q0 + ql) * kHistBins + (i - ql * kHistBins)], v);
+  if (!RESCORE && lane == 0) {
+#pragma unroll
+    for (int p = 0; p < kSets; ++p)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int ql = (QPT == 2) ? 4 * p + 2 * (gg & 1) + (gg >> 1) : 4 * p + gg;
+        if (cnt[p][gg]) atomicAdd(&ws.cand_cnt[q0 + ql], cnt[p][gg]);
+      }
   }
 }
 
+// ---------------------------------------------------------------------------
+// 4. compaction: masks -> candidate list + key histogram (list order is free:
+//    the final select orders its output itself)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kCompactThreads)
+prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, IndexWs ws) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t total;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int V = q_vis[q];
+  if (V <= k) return;                                // the final select needs no candidates
+  for (int i = tid; i < kHistBins; i += kCompactThreads) h[i] = 0;
+  if (tid == 0) total = 0;
+  const int kq = kPfTiles * qpt, nsets = kPfTiles * qpt / 4;
+  const int ql = q % kq, p = ql >> 2;
+  const int g = qpt == 2 ? (((ql & 1) << 1) | ((ql >> 1) & 1)) : (ql & 3);
+  const int64_t mtiles = ws.vstride >> 4;
+  const uint64_t* mq = ws.mask + ((int64_t)(q / kq) * nsets + p) * mtiles;
+  const float* sc = ws.scores + (int64_t)q * ws.vstride;
+  int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
+  const int nt = (V + 15) >> 4;
+  lds_barrier();
+  constexpr int kBatch = 4;
+  for (int j0 = 0; j0 < nt; j0 += kCompactThreads * kBatch) {
+    uint32_t bits[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u * kCompactThreads + tid;
+      bits[u] = j < nt ? (uint32_t)(mq[j] >> (16 * g)) & 0xFFFFu : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t n = __builtin_popcount(bits[u]);
+      uint32_t x = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      uint32_t wbase = 0;
+      if (lane == 63 && x) wbase = atomicAdd(&total, x);
+      wbase = __shfl(wbase, 63);
+      uint32_t pos = wbase + x - n;
+      const int j = j0 + u * kCompactThreads + tid;
+      uint32_t b = bits[u];
+      while (b) {
+        cand[pos++] = (j << 4) + __builtin_ctz(b);
+        b &= b - 1;
+      }
+    }
+  }
+  __syncthreads();                                   // the list is complete (global writes included)
+  const uint32_t n = total;
+  for (uint32_t i0 = 0; i0 < n; i0 += kCompactThreads * kBatch) {
+    float sv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = i0 + u * kCompactThreads + tid;
+      sv[u] = i < n ? sc[cand[i]] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (i0 + u * kCompactThreads + tid < n) atomicAdd(&h[score_key(sv[u]) >> (32 - kHistBits)], 1u);
+  }
+  lds_barrier();
+  uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
+  for (int i = tid; i < kHistBins; i += kCompactThreads) gh[i] = h[i];
+  if (tid == 0) ws.cand_cnt[q] = n;
+}
+
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
-                               const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                               const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                                hipStream_t s, const KEvents& ev) {
   if (nq <= 0 || max_vis <= 0) {
     record_empty(ev, s);
@@ -191,13 +474,23 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
   prefill_chunking(max_vis, c.lg_page, &chunk, &per_xcd);
   const int qpt = h_idx <= 8 ? 2 : 1;
   const int64_t nqb = (nq + kPfTiles * qpt - 1) / (kPfTiles * qpt);
-  const dim3 grid((unsigned)(8 * per_xcd * nqb));
-  if (qpt == 2)
-    launch(prefill_scan_kernel<2>, grid, dim3(kPfWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, nq, h_idx, chunk,
+  const dim3 grid((unsigned)(8 * per_xcd * nqb)), block(kPfWaves * 64);
+  const dim3 tgrid((unsigned)((nq + kTauWaves * qpt - 1) / (kTauWaves * qpt))), tblock(kTauWaves * 64);
+  const int factor = g_prefill_cand_factor;
+  if (qpt == 2) {
+    launch(prefill_tau_kernel<2>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
+    launch(prefill_scan_kernel<2, false>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
-  else
-    launch(prefill_scan_kernel<1>, grid, dim3(kPfWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, nq, h_idx, chunk,
+    launch(prefill_scan_kernel<2, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
+  } else {
+    launch(prefill_tau_kernel<1>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
+    launch(prefill_scan_kernel<1, false>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+           per_xcd, ws);
+    launch(prefill_scan_kernel<1, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+           per_xcd, ws);
+  }
+  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, ev.last(), q_vis, k, qpt, ws);
   return hipGetLastError();
 }
 

@@ -346,4 +346,14 @@ hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, i
   return hipGetLastError();
 }
 
+hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
+                             int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
+  if (nq <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
+  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev, ws, q_vis, k, out_idx, out_cnt);
+  return hipGetLastError();
+}
+
 }  // namespace csa2

@@ -137,6 +137,10 @@ def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: to
     return out, lse
 
 
+def csa2_set_prefill_candidate_factor(factor: int) -> None:
+    L.check("csa2_set_prefill_candidate_factor", L.load().csa2_set_prefill_candidate_factor(int(factor)))
+
+
 class LayerCall:
     """Prepared arguments of one csa2_layer_step call (pointers fixed at
     construction, so repeated launches cost one ctypes call each)."""

@@ -160,6 +160,15 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
                                     int32_t* out_idx, int32_t* out_cnt,
                                     void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Candidate target of the dense indexer, in units of k: each query keeps the
+ * entries whose score reaches a threshold estimated from a 512-entry sample
+ * so that about factor * k of them are expected to pass (default 4; the
+ * selection is exact for every factor, queries left with fewer than k
+ * candidates are rescored in full).  0 sends every query with more than k
+ * visible entries through the full rescore.  Process-wide, not thread-safe:
+ * meant for tuning and tests.  Returns CSA2_ERR_INVALID_ARG outside [0, 64]. */
+csa2_status csa2_set_prefill_candidate_factor(int32_t factor);
+
 /* Sparse attention over the selected rows (all three modes end here).
  *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
  *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq],

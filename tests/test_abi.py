@@ -125,6 +125,14 @@ def test_layer_step_mode_field_rules():
     assert lib.csa2_layer_step(L.CSA2_REUSE, None, None) == L.CSA2_ERR_INVALID_ARG
 
 
+def test_prefill_candidate_factor_range():
+    lib = L.load()
+    assert lib.csa2_set_prefill_candidate_factor(-1) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_set_prefill_candidate_factor(65) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_set_prefill_candidate_factor(0) == L.CSA2_OK
+    assert lib.csa2_set_prefill_candidate_factor(4) == L.CSA2_OK
+
+
 def test_set_timing_validation():
     lib = L.load()
     assert lib.csa2_set_timing(9, None) == L.CSA2_ERR_INVALID_ARG

@@ -168,23 +168,45 @@ def test_prefill_dense_gaussian():
     _compare_group(spec, exact_topk=False, dense=True)
 
 
-@pytest.mark.parametrize("seed,cached,n_new,h_idx,page_size", [
-    (45, [6000], 300, 8, 64),
-    (46, [40000], 45, 8, 64),        # several chunks per XCD (64-entry pages cap a chunk at 63 pages)
-    (47, [3000], 77, 12, 128),
-    (48, [2500], 19, 3, 64),
+@pytest.mark.parametrize("seed,cached,n_new,h_idx,page_size,k", [
+    (45, [6000], 300, 8, 64, 512),
+    (46, [40000], 45, 8, 64, 512),   # several chunks per XCD (64-entry pages cap a chunk at 63 pages)
+    (47, [3000], 77, 12, 128, 512),
+    (48, [2500], 19, 3, 64, 512),
+    (49, [20000], 64, 8, 256, 128),   # sampled threshold with k = 128
+    (50, [30000], 40, 12, 1024, 512),
 ])
-def test_prefill_dense_bit_identical_to_scan(seed, cached, n_new, h_idx, page_size):
-    """The dense prefill indexer and the per-query scan produce identical
-    scores, so the whole layer output matches bit for bit."""
-    spec = W.small_case("prefill_same", seed, cached, n_new=n_new, h_idx=h_idx, h=16, k=512,
+def test_prefill_dense_bit_identical_to_scan(seed, cached, n_new, h_idx, page_size, k):
+    """The dense prefill indexer (sampled threshold, candidates, exact select)
+    and the per-query scan select identically, so the whole layer output
+    matches bit for bit."""
+    spec = W.small_case("prefill_same", seed, cached, n_new=n_new, h_idx=h_idx, h=16, k=k,
                         modes=(O.FULL, O.REINDEX), prefill=True, page_size=page_size)
-    say(f"[dense=scan] seed={seed} cached={cached} n_new={n_new} h_idx={h_idx} page={page_size}")
+    say(f"[dense=scan] seed={seed} cached={cached} n_new={n_new} h_idx={h_idx} page={page_size} k={k}")
     _, a = _run_case(spec, dense=True)
     _, b = _run_case(spec, dense=False)
     for li, (x, y) in enumerate(zip(a, b)):
         for key in ("idx", "cnt", "out", "lse"):
             assert np.array_equal(x[key], y[key]), (li, key)
+
+
+@pytest.mark.parametrize("factor", [0, 1, 64])
+def test_prefill_dense_candidate_factor(factor):
+    """Candidate factor 0 sends every query through the full rescore, 1 makes
+    short candidate lists (some queries rescored), 64 keeps every entry; the
+    selection is the same in all cases."""
+    ops, _ = _ops()
+    spec = W.small_case("prefill_factor", 52, [24000], n_new=48, h_idx=8, h=16, k=256,
+                        modes=(O.FULL,), prefill=True, page_size=128)
+    say(f"[dense factor] factor={factor}")
+    _, ref = _run_case(spec, dense=False)
+    try:
+        ops.csa2_set_prefill_candidate_factor(factor)
+        _, got = _run_case(spec, dense=True)
+    finally:
+        ops.csa2_set_prefill_candidate_factor(4)
+    for key in ("idx", "cnt", "out", "lse"):
+        assert np.array_equal(got[0][key], ref[0][key]), key
 
 
 def test_all_equal_scores_take_lowest_indices():
