@@ -86,6 +86,27 @@ __device__ __forceinline__ intx8 load_fp8_operand(const uint8_t* row, int g) {
   return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// A 16-row x 128-byte FP8 tile in contiguous memory reaches its MFMA
+// operand layout through LDS: lane l loads bytes [32l, +32) (four lanes per
+// 128-byte row, so loads are fully coalesced), writes them to the wave's LDS
+// slot (rows padded to kFp8SlotRow bytes, conflict-free both ways) and reads
+// back the load_fp8_operand layout of row l % 16.
+constexpr int kFp8SlotRow = 144;
+constexpr int kFp8SlotBytes = 16 * kFp8SlotRow;
+
+__device__ __forceinline__ intx8 load_fp8_tile_linear(const uint8_t* tile, int lane) {
+  const intx4 lo = *reinterpret_cast<const intx4*>(tile + 32 * lane);
+  const intx4 hi = *reinterpret_cast<const intx4*>(tile + 32 * lane + 16);
+  return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ intx8 fp8_tile_operand(uint8_t* slot, const intx8& lin, int lane) {
+  uint8_t* wr = slot + (lane >> 2) * kFp8SlotRow + 32 * (lane & 3);
+  *reinterpret_cast<intx4*>(wr) = intx4{lin[0], lin[1], lin[2], lin[3]};
+  *reinterpret_cast<intx4*>(wr + 16) = intx4{lin[4], lin[5], lin[6], lin[7]};
+  return load_fp8_operand(slot + (lane & 15) * kFp8SlotRow, lane >> 4);
+}
+
 // max(x, 0) as one integer max on the bit pattern: negative values (sign bit
 // set, -0 included) map to +0; used by every indexer path so their scores
 // agree bit for bit.

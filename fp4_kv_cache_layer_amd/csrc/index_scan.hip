@@ -9,17 +9,18 @@
 //
 // Dot products run on the gfx950 FP8 matrix core: one
 // V_MFMA_F32_16X16X128_F8F6F4 multiplies the (zero-padded to 16) indexer
-// heads by 16 entries over the full 128-wide dimension.  Lane l supplies
-// head / entry (l % 16) and 32 bytes of its row (load_fp8_operand), so a wave
-// streams one 2 KB tile of 16 indexer-K rows per MFMA.  The result puts entry (l % 16) and heads 4*(l/16)+i in lane
-// l, so the ReLU * w reduction is 4 FMAs and two cross-lane adds.
+// heads by a tile of 16 entries over the full 128-wide dimension.  Each
+// 2 KB tile is read with fully coalesced loads and reaches the operand
+// layout through the wave's LDS slot.  The result puts entry (l % 16) and
+// heads 4*(l/16)+i in lane l, so the ReLU * w reduction is 4 FMAs and two
+// lane-swap adds.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
 namespace csa2 {
 
 constexpr int kScanWaves = 4;
-constexpr int kScanUnroll = 4;          // 16-entry tiles in flight per wave
+constexpr int kScanDepth = 6;           // tiles per wave in the load ring
 
 // Row stride of the per-query score and candidate arrays: at least one slot
 // past the longest visible range, which the dense indexer uses as a write
@@ -39,10 +40,13 @@ size_t index_score_bytes(int32_t nq, int32_t max_vis) {
 __global__ void __launch_bounds__(kScanWaves * 64)
 index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
-                  int h_idx, int nchunks, IndexWs ws) {
+                  int nq, int h_idx, IndexWs ws) {
   __shared__ uint32_t hist[kHistBins];
-  const int q = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x - q * nchunks;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];
+  // chunk-major: the short last chunks of equal-length queries come last, so
+  // a grid larger than one round leaves only short work for the second round
+  const int chunk = blockIdx.x / nq;
+  const int q = blockIdx.x - chunk * nq;
   const int vis = q_vis[q];
   const int t0 = chunk * kScanChunk;
   if (t0 >= vis) return;                              // uniform for the block
@@ -50,7 +54,8 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int tid = threadIdx.x;
   for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
   if (r < h_idx) {
@@ -71,46 +76,53 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int ntiles = (t1 - t0 + 15) >> 4;
   lds_barrier();
 
-  // Tiles j = base + u of this wave; the next group of tiles is loaded while
-  // the current one goes through the matrix core and the epilogue.
-  // Loads are unconditional (a tile past the end re-reads the last tile and
-  // is ignored) so the compiler can count loads in flight instead of waiting
-  // for all of them.
-  auto load = [&](int base, intx8 (&b)[kScanUnroll]) {
-#pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      const int j = min(base + u, ntiles - 1);
-      // rows t0+16j .. +15 share the tile start's page (tiles never straddle pages)
-      const int ts = t0 + 16 * j;
-      const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
-      const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
-      b[u] = load_fp8_operand(c.idx_k + row * kIndexDim, g);
-    }
+  // Tiles j = wave, wave + 4, ... of this wave, kScanDepth - 1 in flight ahead
+  // of the one in use (a ring of buffers addressed by name after unrolling).  A tile's 16 rows are 2 KB of
+  // contiguous memory: loaded coalesced, turned into the MFMA operand through
+  // the wave's LDS slot.  Loads past the end re-read the last tile; stores are
+  // unconditional (lanes with nothing to write use the sink slot past every
+  // visible entry), so the compiler can count loads in flight past them.
+  uint8_t* const slot = stage[wave];
+  auto load = [&](int j, intx8& lin) {
+    j = min(j, ntiles - 1);
+    const int ts = t0 + 16 * j;                       // tiles never straddle pages
+    const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
+    lin = load_fp8_tile_linear(c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim,
+                               lane);
   };
-  constexpr int kStride = kScanWaves * kScanUnroll;
-  intx8 cur[kScanUnroll], nxt[kScanUnroll];
-  load(wave * kScanUnroll, cur);
-  for (int base = wave * kScanUnroll; base < ntiles; base += kStride) {
-    load(base + kStride, nxt);
+  const int sink = (int)ws.vstride - 1;
+  auto process = [&](int j, const intx8& lin) {
+    const intx8 b = fp8_tile_operand(slot, lin, lane);
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+    const float part = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));   // every lane: entry r's score
+    const int t = t0 + 16 * j + r;
+    uint32_t u32 = __float_as_uint(part);
+    if ((u32 << 1) == 0) u32 = 0;                     // -0 -> +0
+    srow[t < t1 ? t : sink] = __uint_as_float(u32);
+    if (g == 0 && t < t1) atomicAdd(&hist[score_key(__uint_as_float(u32)) >> (32 - kHistBits)], 1u);
+  };
+  intx8 buf[kScanDepth];
 #pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) {
-      const int j = base + u;
-      if (j >= ntiles) break;
-      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, cur[u], acc, 0, 0, 0, 0, 0, 0);
-      float part = relu_weighted(acc, wv);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      const int t = t0 + 16 * j + r;
-      if (g == 0 && t < t1) {
-        uint32_t u32 = __float_as_uint(part);
-        if ((u32 << 1) == 0) u32 = 0;                 // -0 -> +0
-        srow[t] = __uint_as_float(u32);
-        atomicAdd(&hist[score_key(__uint_as_float(u32)) >> (32 - kHistBits)], 1u);
+  for (int d = 0; d + 1 < kScanDepth; ++d) load(wave + d * kScanWaves, buf[d]);
+  if (ntiles == kScanChunk / 16) {
+    // full chunk: a fixed schedule, unrolled, so every wait on the ring is exact
+    constexpr int kSteps = kScanChunk / 16 / kScanWaves;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      if (u + kScanDepth - 1 < kSteps)
+        load(wave + (u + kScanDepth - 1) * kScanWaves, buf[(u + kScanDepth - 1) % kScanDepth]);
+      process(wave + u * kScanWaves, buf[u % kScanDepth]);
+    }
+  } else {
+    for (int j = wave; j < ntiles; j += kScanDepth * kScanWaves) {
+#pragma unroll
+      for (int u = 0; u < kScanDepth; ++u) {
+        load(j + (u + kScanDepth - 1) * kScanWaves, buf[(u + kScanDepth - 1) % kScanDepth]);
+        if (j + u * kScanWaves >= ntiles) break;
+        process(j + u * kScanWaves, buf[u]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) cur[u] = nxt[u];
   }
   lds_barrier();
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
@@ -129,8 +141,8 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
     record_empty(ev, s);
     return hipSuccess;
   }
-  launch(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, h_idx,
-         nchunks, ws);
+  launch(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, nq,
+         h_idx, ws);
   return hipGetLastError();
 }
 

@@ -54,11 +54,10 @@ constexpr int kTauWaves = 4;
 constexpr int kSampleTiles = 32;        // 512 sampled entries per query
 constexpr int kMaxRank = 64;
 constexpr int kCompactThreads = 512;
-constexpr int kSlotRow = 144;           // LDS row pitch of a staged B tile (128 bytes + 16 of padding)
 
 // Per-wave LDS of the candidate pass: the staged B tile.
 struct PfShared {
-  uint8_t tile[kPfWaves][16 * kSlotRow];
+  uint8_t tile[kPfWaves][kFp8SlotBytes];
 };
 
 // Entries per chunk and chunks per XCD for a given visible range; chunks never
@@ -271,28 +270,16 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     j = min(j, ntiles - 1) + rot;
     return j >= ntiles ? j - ntiles : j;
   };
-  // A tile's 16 rows are 2 KB of contiguous memory; lane l loads bytes
-  // [32l, +32), so every group of four lanes reads one whole 128-byte row.
+  // A tile's 16 rows are 2 KB of contiguous memory, loaded coalesced and
+  // turned into the MFMA operand through the wave's LDS slot.
   auto load = [&](int j, intx8& lin) {
     const int ts = e0 + 16 * tile_at(j);
     const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
-    const uint8_t* tb = c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim;
-    const intx4 lo = *reinterpret_cast<const intx4*>(tb + 32 * lane);
-    const intx4 hi = *reinterpret_cast<const intx4*>(tb + 32 * lane + 16);
-    lin = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    lin = load_fp8_tile_linear(
+        c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim, lane);
   };
-  // ... and the wave turns it into the MFMA operand through its own LDS
-  // slot (rows padded to 144 bytes, so both accesses are bank-conflict free).
   uint8_t* const slot = S.tile[wave];
-  auto to_operand = [&](const intx8& lin) {
-    uint8_t* wr = slot + (lane >> 2) * kSlotRow + 32 * (lane & 3);
-    *reinterpret_cast<intx4*>(wr) = intx4{lin[0], lin[1], lin[2], lin[3]};
-    *reinterpret_cast<intx4*>(wr + 16) = intx4{lin[4], lin[5], lin[6], lin[7]};
-    const uint8_t* rd = slot + r * kSlotRow;
-    const intx4 lo = *reinterpret_cast<const intx4*>(rd + 16 * g);
-    const intx4 hi = *reinterpret_cast<const intx4*>(rd + 64 + 16 * g);
-    return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
+  auto to_operand = [&](const intx8& lin) { return fp8_tile_operand(slot, lin, lane); };
 
   // Scores of one tile for output set p (see ql above): the set's matrix
   // products are issued one set ahead of their epilogue, so the epilogue never
