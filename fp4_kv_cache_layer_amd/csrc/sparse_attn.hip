@@ -9,23 +9,24 @@
 // by the context length ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
 // Compression", Introduction: near-constant decode FLOPs from 4K to 1M).
 //
-// Work split.  A (query, group of 16 heads) unit is cut into nsplit
-// contiguous shares of its selected rows so that a small decode batch still
-// covers the chip; a workgroup serves one share and writes its unnormalised
-// output with its running max and sum, and a combine kernel merges the shares
-// (nsplit = 1 writes the final output directly).  The four waves of a
-// workgroup own the four 128-wide slices of the latent.  The workgroup first
-// resolves the physical row of every selected entry of its share into LDS,
-// then streams 32-row tiles with the row gathers of the next kPrefetch tiles
-// in flight.  For every tile a wave
-//   - gathers, for two rows per lane, the 16 code bytes of one 32-element
-//     scale block of its slice and dequantises them with
-//     V_CVT_SCALEF32_PK_BF16_FP4 straight into the A operand of
-//     S^T = X Q^T (bf16 MFMA 16x16x32, K = its 128 dims, permuted alike in
-//     the Q operand),
-//   - publishes its partial S^T (32 rows x 16 heads) and its bf16 slice of the
-//     rows in LDS (row stride 272 B: the 16-byte writes and the transposing
-//     8-byte reads both spread evenly over the 64 banks),
+// Work split.  A workgroup serves one (query, group of 16 heads) unit, or a
+// share of its selected rows.  Its waves form RG row groups of four: the four
+// waves of a row group own the four 128-wide slices of the latent, and row
+// group g takes tiles g, g + RG, ...; at the end row groups merge their
+// (output, running max, running sum) through LDS.  Small decode batches use
+// RG = 2; a share split across workgroups (small batches) writes its
+// unnormalised output with its running max and sum and a combine kernel
+// merges the shares.  The workgroup first resolves the physical
+// row of every selected entry of its share into LDS, then streams 32-row
+// tiles with the row gathers of the next kPrefetch tiles in flight.  For every
+// tile a wave
+//   - gathers whole 64-byte row segments of its slice (four lanes per row)
+//     with their scale bytes, dequantises them with
+//     V_CVT_SCALEF32_PK_BF16_FP4 into its bf16 slice rows in LDS (row stride
+//     272 B: the 16-byte accesses and the transposing 8-byte reads both spread
+//     evenly over the banks), and reads back the A operand of S^T = X Q^T
+//     (bf16 MFMA 16x16x32, K = its 128 dims, permuted alike in the Q operand),
+//   - publishes its partial S^T (32 rows x 16 heads) in LDS,
 //   - sums the four partial S^T (same order in every wave), runs the online
 //     softmax (the output is rescaled only when the running max grows by more
 //     than 8 nats, so probabilities stay below e^8) and accumulates
@@ -37,7 +38,6 @@
 
 namespace csa2 {
 
-constexpr int kAttnThreads = 256;
 constexpr int kTileRows = 32;
 constexpr int kSliceStride = 272;                       // bytes per bf16 slice row (128 * 2 + 16 pad)
 constexpr int kSliceBytes = kTileRows * kSliceStride;   // 8,704
@@ -64,24 +64,35 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float scale) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+template <int RG>
 struct AttnShared {
-  uint8_t xs[4][kSliceBytes];        // [slice] bf16 rows of the current tile (34,816 B)
-  floatx4 sp[4][2][4][16];           // partial S^T per wave: [m-tile][row quad][head] of 4 rows (8,192 B)
+  uint8_t xs[4 * RG][kSliceBytes];   // [wave] bf16 slice rows of its current tile (8,704 B each)
+  floatx4 sp[RG][4][2][4][16];       // partial S^T per row group and wave: [m-tile][row quad][head] of 4 rows
   uint32_t row[kMaxShareRows];       // physical row of every selected entry of the share (8,192 B)
 };
 
-__global__ void __launch_bounds__(kAttnThreads, 2)
+template <int RG>
+__global__ void __launch_bounds__(256 * RG, RG == 1 ? 2 : 1)
 sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
                    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int h, int k,
-                   float sm_scale, float* __restrict__ out, float* __restrict__ lse, int nsplit,
+                   float sm_scale, float* __restrict__ out, float* __restrict__ lse, int nsplit, int npairs,
                    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ AttnShared S;
+  constexpr int kThreads = 256 * RG;
+  __shared__ AttnShared<RG> S;
+  // Block order: the head groups of one (query, share) are 8 blocks apart,
+  // so they run on the same XCD (blocks go to XCDs round-robin) and gather
+  // the same rows through one L2.
   const int ngroups = (h + 15) >> 4;
-  const int unit = blockIdx.x / nsplit;                 // (query, head group)
-  const int split = blockIdx.x - unit * nsplit;
-  const int qi = unit / ngroups;
-  const int hg = unit - qi * ngroups;
-  const int tid = threadIdx.x, lane = tid & 63, ds = tid >> 6;
+  const int b = blockIdx.x;
+  const int hg = (b >> 3) % ngroups;
+  const int pair = (b / (8 * ngroups)) * 8 + (b & 7);    // (query, share)
+  if (pair >= npairs) return;                            // uniform: padding of the last group of 8
+  const int qi = pair / nsplit;
+  const int split = pair - qi * nsplit;
+  const int unit = qi * ngroups + hg;                    // (query, head group)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ds = wv & 3, rg = wv >> 2;                  // latent slice, row group
   const int g = lane >> 4, r = lane & 15;
   const int head = hg * 16 + r;
   const int n_all = cnt[qi];
@@ -103,7 +114,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   {
     const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
     const int32_t* irow = idx + (int64_t)qi * k;
-    for (int j = tid; j < per_split * kTileRows; j += kAttnThreads) {
+    for (int j = tid; j < per_split * kTileRows; j += kThreads) {
       const int t = irow[min(j0 + j, k - 1)];
       if (j < n) S.row[j] = (uint32_t)entry_row(pt_row, t, c.lg_page);
     }
@@ -115,67 +126,71 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
   const int ntiles = (n + kTileRows - 1) / kTileRows;
-  uint8_t* xs = &S.xs[ds][0];
+  const int ntiles_rg = (ntiles + RG - 1) / RG;          // tiles rg, rg + RG, ... of this row group
+  uint8_t* xs = &S.xs[wv][0];
 
-  // Ring of row gathers: slot u holds tile t0+u's 16 code bytes (one scale
-  // block of this slice) and scale byte for two rows per lane.  Loads are
-  // unconditional (a row past the share reads physical row 0, which always
-  // exists) so the compiler counts gathers in flight instead of draining them.
+  // Ring of row gathers.  Lanes 4i .. 4i+3 read row i's 64 code bytes of
+  // this slice (one 32-value scale block each) and its 4 scale bytes, so a
+  // load covers whole row segments; slot u holds tile t0+u (two groups of 16
+  // rows).  Loads are unconditional (a row past the share reads physical row
+  // 0, which always exists) so the compiler counts gathers in flight instead
+  // of draining them.
+  const int grow = lane >> 2, gblk = lane & 3;          // gather layout: row, scale block
   uint4 cd[kPrefetch][2];
   uint32_t sb[kPrefetch][2];
-  auto gather = [&](int tile, uint4 (&c2)[2], uint32_t (&s2)[2]) {
+  auto gather = [&](int tt, uint4 (&c2)[2], uint32_t (&s2)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int j = tile * kTileRows + mt * 16 + r;
+      const int j = (rg + RG * tt) * kTileRows + mt * 16 + grow;
       const uint8_t* src = c.kv + (size_t)(j < n ? S.row[j] : 0u) * kKvRowBytes;
-      c2[mt] = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * g);
-      s2[mt] = src[kCodeBytes + 4 * ds + g];
+      c2[mt] = *reinterpret_cast<const uint4*>(src + 64 * ds + 16 * gblk);
+      s2[mt] = src[kCodeBytes + 4 * ds + gblk];
     }
   };
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u) gather(u, cd[u], sb[u]);
 
   // The trip count is padded to whole rings (tiles past the share are masked)
-  // so the ring slots are consumed in a fixed order.
-  const int ntiles_pad = (ntiles + kPrefetch - 1) / kPrefetch * kPrefetch;
+  // so the ring slots are consumed in a fixed order; it is the same for every
+  // row group, so all waves meet the same barriers.
+  const int ntiles_pad = (ntiles_rg + kPrefetch - 1) / kPrefetch * kPrefetch;
   for (int t0 = 0; t0 < ntiles_pad; t0 += kPrefetch) {
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u) {
-    const int tile = t0 + u;
-    const int lim = n - tile * kTileRows;               // rows of this tile inside the share
-    // ---- dequantise into the S^T A operand; partial S^T over this slice ----
-    bf16x8 xa[2][4];
-    floatx4 st[2];
+    const int tt = t0 + u;
+    const int lim = n - (rg + RG * tt) * kTileRows;     // rows of this tile inside the share
+    // ---- dequantise (gather layout) into this wave's bf16 slice rows ----
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       // a row past the share keeps its (finite) codes but gets scale 1: its
       // logit is masked below, so it only ever meets a zero probability
-      const float scale = e8m0_to_float(mt * 16 + r < lim ? sb[u][mt] : 127u);
+      const float scale = e8m0_to_float(mt * 16 + grow < lim ? sb[u][mt] : 127u);
       const uint32_t wds[4] = {cd[u][mt].x, cd[u][mt].y, cd[u][mt].z, cd[u][mt].w};
-      st[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      uint8_t* rowp = xs + (mt * 16 + grow) * kSliceStride + 64 * gblk;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        xa[mt][s] = dequant8(wds[s], scale);
-        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt][s], qop[s], st[mt], 0, 0, 0);
-      }
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(rowp + 16 * s) = dequant8(wds[s], scale);
     }
-    gather(tile + kPrefetch, cd[u], sb[u]);             // refill the slot kPrefetch tiles ahead
-    // ---- publish the bf16 slice rows and the partial scores ----
+    gather(tt + kPrefetch, cd[u], sb[u]);               // refill the slot kPrefetch tiles ahead
+    // ---- partial S^T over this slice: the A operand (row r, dims 32g + 8s)
+    //      read back from the slice rows ----
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      uint8_t* rowp = xs + (mt * 16 + r) * kSliceStride + 64 * g;
+      const uint8_t* rowp = xs + (mt * 16 + r) * kSliceStride + 64 * g;
+      floatx4 st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(rowp + 16 * s) = xa[mt][s];
-      S.sp[ds][mt][g][r] = st[mt];                      // lanes write consecutive 16 B: no bank conflicts
+      for (int s = 0; s < 4; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(rowp + 16 * s), qop[s], st,
+                                                     0, 0, 0);
+      S.sp[rg][ds][mt][g][r] = st;                      // lanes write consecutive 16 B: no bank conflicts
     }
     lds_barrier();
     // ---- full scores of head r, rows mt*16 + 4g + i (fixed summation order) ----
     float v[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      floatx4 acc = S.sp[0][mt][g][r];
+      floatx4 acc = S.sp[rg][0][mt][g][r];
 #pragma unroll
-      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[d2][mt][g][r];
+      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[rg][d2][mt][g][r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[mt][i] = acc[i] * sm_scale;
     }
@@ -243,6 +258,45 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   }
   }
 
+  if (RG > 1) {
+    // Row groups 1 .. RG-1 hand their (O, running max, running sum) to row
+    // group 0 through the freed slice-row buffers; row group 0 merges them.
+    constexpr int kMergeFloats = 64 * 34;                 // per wave: 32 outputs + max + sum per lane
+    float* mbuf = reinterpret_cast<float*>(&S.xs[0][0]);
+    lds_barrier();                                        // every wave is done with its slice rows
+    if (rg > 0) {
+      float* mine = mbuf + ((rg - 1) * 4 + ds) * kMergeFloats + lane * 34;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[4 * nt + i] = oacc[nt][i];
+      mine[32] = m_run;
+      mine[33] = l_run;
+    }
+    lds_barrier();
+    if (rg > 0) return;                                   // no barrier follows
+#pragma unroll
+    for (int o = 1; o < RG; ++o) {
+      const float* other = mbuf + ((o - 1) * 4 + ds) * kMergeFloats + lane * 34;
+      const float m_o = other[32], l_o = other[33];
+      const float m_new = fmaxf(m_run, m_o);
+      const float a_me = m_run == -INFINITY ? 0.0f : __expf(m_run - m_new);
+      const float a_o = m_o == -INFINITY ? 0.0f : __expf(m_o - m_new);
+      l_run = a_me * l_run + a_o * l_o;
+      m_run = m_new;
+      float am[4], ao[4];                                 // O rows are heads 4g+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        am[i] = __shfl(a_me, 4 * g + i);
+        ao[i] = __shfl(a_o, 4 * g + i);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nt][i] = am[i] * oacc[nt][i] + ao[i] * other[4 * nt + i];
+    }
+  }
+
   if (nsplit == 1) {
     float linv[4];
 #pragma unroll
@@ -305,13 +359,23 @@ attn_combine_kernel(int h, int nsplit, const float* __restrict__ part_o, const f
   if (lse != nullptr && tid == 0) lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
 }
 
+// Row groups per workgroup: small batches (decode) split each query's rows
+// among 2 row groups of 4 waves inside one workgroup, merged through LDS;
+// large batches already cover the chip with one 4-wave workgroup per unit.
+static int attn_rgroups(int nq, int h) {
+  const int units = nq * ((h + 15) / 16);
+  return units < 256 ? 2 : 1;
+}
+
 int attn_nsplit(int nq, int h, int k) {
   const int units = nq * ((h + 15) / 16);
   const int ntiles = (k + kTileRows - 1) / kTileRows;
+  const int rg = attn_rgroups(nq, h);
+  const int target = rg > 1 ? 256 : 512;                 // workgroups that fill the chip
   int ns = 1;
-  // aim at >= 512 workgroups with at least two tiles per share; shares must fit the row table
-  while (ns < 16 && units * ns < 512 && ntiles >= 4 * ns) ns *= 2;
-  while ((ntiles + ns - 1) / ns * kTileRows > kMaxShareRows) ns *= 2;
+  // split across workgroups only while every row group keeps two tiles per share
+  while (ns < 16 && units * ns < target && ntiles >= 2 * rg * 2 * ns) ns *= 2;
+  while ((ntiles + ns - 1) / ns * kTileRows > kMaxShareRows) ns *= 2;   // shares must fit the row table
   return ns;
 }
 
@@ -334,8 +398,14 @@ hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32
   const int64_t units = (int64_t)nq * ngroups;
   float* part_o = reinterpret_cast<float*>(part);
   float* part_ml = part_o ? part_o + units * ns * 16 * kLatent : nullptr;
-  launch(sparse_attn_kernel, dim3((unsigned)(units * ns)), dim3(kAttnThreads), s, ns > 1 ? ev.first() : ev, c, q,
-         q_seq, idx, cnt, h, k, sm_scale, out, lse, ns, part_o, part_ml);
+  const int64_t npairs = (int64_t)nq * ns;
+  const int64_t blocks = (npairs + 7) / 8 * 8 * ngroups;
+  if (attn_rgroups(nq, h) == 2)
+    launch(sparse_attn_kernel<2>, dim3((unsigned)blocks), dim3(256 * 2), s, ns > 1 ? ev.first() : ev, c, q, q_seq,
+           idx, cnt, h, k, sm_scale, out, lse, ns, (int)npairs, part_o, part_ml);
+  else
+    launch(sparse_attn_kernel<1>, dim3((unsigned)blocks), dim3(256), s, ns > 1 ? ev.first() : ev, c, q, q_seq, idx,
+           cnt, h, k, sm_scale, out, lse, ns, (int)npairs, part_o, part_ml);
   if (ns > 1)
     launch(attn_combine_kernel, dim3((unsigned)(units * 16)), dim3(128), s, ev.last(), h, ns, part_o, part_ml, out,
            lse);
