@@ -121,6 +121,10 @@ __device__ __forceinline__ float relu_weighted(const floatx4& acc, const float (
   for (int i = 0; i < 4; ++i) s += wv[i] * relu_bits(acc[i]);
   return s;
 }
+__device__ __forceinline__ float relu_weighted4(const floatx4& acc, const float4 wv) {
+  const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+  return relu_weighted(acc, w4);
+}
 
 // E8M0 byte -> fp32 scale 2^(b-127); byte 0 is the subnormal 2^-127.
 __device__ __forceinline__ float e8m0_to_float(uint32_t b) {

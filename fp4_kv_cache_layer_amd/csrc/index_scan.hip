@@ -22,10 +22,10 @@ namespace csa2 {
 constexpr int kScanWaves = 4;
 constexpr int kScanDepth = 6;           // tiles per wave in the load ring
 
-// Row stride of the per-query score and candidate arrays: at least one slot
-// past the longest visible range, which the dense indexer uses as a write
-// sink that is never read.
-int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 1 + 63) / 64 * 64; }
+// Row stride of the per-query score and candidate arrays: at least two slots
+// past the longest visible range, which the indexer kernels use as write
+// sinks that are never read.
+int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 2 + 63) / 64 * 64; }
 
 size_t zero_state_bytes(int32_t nq) {
   return ((size_t)nq * (kHistBins + 1) * 4 + 255) / 256 * 256;

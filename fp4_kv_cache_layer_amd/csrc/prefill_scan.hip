@@ -58,6 +58,7 @@ constexpr int kCompactThreads = 512;
 // Per-wave LDS of the candidate pass: the staged B tile.
 struct PfShared {
   uint8_t tile[kPfWaves][kFp8SlotBytes];
+  float4 w[kPfTiles][4];             // head weights of A tile t's output rows 4g .. 4g+3 (row group g)
 };
 
 // Entries per chunk and chunks per XCD for a given visible range; chunks never
@@ -184,7 +185,7 @@ prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* 
 // 2./3. candidate pass (RESCORE = false) and full rescore of short queries
 // ---------------------------------------------------------------------------
 template <int QPT, bool RESCORE>
-__global__ void __launch_bounds__(kPfWaves * 64)
+__global__ void __launch_bounds__(kPfWaves * 64, 4)
 prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
                     int nq, int h_idx, int k, int chunk, int per_xcd, IndexWs ws) {
@@ -212,10 +213,17 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile indices stay scalar
   const int g = lane >> 4, r = lane & 15;
+  // A tiles in registers; their head weights, the same for all 16 lanes of a
+  // row group, in LDS (read back as one broadcast per use)
   intx8 a[kPfTiles];
-  float wv[kPfTiles][4];
 #pragma unroll
-  for (int t = 0; t < kPfTiles; ++t) load_a_tile<QPT>(q_idx, w, nq, h_idx, q0 + QPT * t, r, g, a[t], wv[t]);
+  for (int t = 0; t < kPfTiles; ++t) {
+    float wv[4];
+    load_a_tile<QPT>(q_idx, w, nq, h_idx, q0 + QPT * t, r, g, a[t], wv);
+    if (wave == 0 && r == 0) S.w[t][g] = make_float4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  lds_barrier();
+
 
   // After the head sums, output set p puts query ql(p, g) in lane row g:
   //   QPT = 2: tiles 2p and 2p+1 -> ql = 4p + 2*(g & 1) + (g >> 1)
@@ -294,11 +302,11 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   };
   auto finish = [&](int p, const floatx4 (&acc)[kPerSet]) {
     if (QPT == 2) {
-      return pair_rows2(relu_weighted(acc[0], wv[2 * p]), relu_weighted(acc[1], wv[2 * p + 1]));
+      return pair_rows2(relu_weighted4(acc[0], S.w[2 * p][g]), relu_weighted4(acc[1], S.w[2 * p + 1][g]));
     } else {
       float sq[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sq[i] = halves_sum(rows_pair_sum(relu_weighted(acc[i], wv[4 * p + i])));
+      for (int i = 0; i < 4; ++i) sq[i] = halves_sum(rows_pair_sum(relu_weighted4(acc[i], S.w[4 * p + i][g])));
       return g == 0 ? sq[0] : g == 1 ? sq[1] : g == 2 ? sq[2] : sq[3];
     }
   };
@@ -356,9 +364,20 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   };
   // B tiles j = wave, wave + 4, ...; two tiles in flight ahead of the one in
   // use, in three buffers that rotate by name (unrolled by three)
+  // Before the loop, each ring load is followed by the stores of one tile
+  // (into sink slots), as in the loop, so the loop entry and back edge carry
+  // the same memory operations and the compiler's waits stay exact.
+  char* const sink2 = reinterpret_cast<char*>(sblock) + (uint32_t)(ws.vstride - 2) * 4u;
+  auto sink_stores = [&]() {
+#pragma unroll
+    for (int p = 0; p < kSets; ++p) *reinterpret_cast<float*>(sink2 + 4) = 0.0f;
+    *reinterpret_cast<uint64_t*>(sink2) = 0ull;
+  };
   intx8 l0, l1, l2;
   load(wave, l0);
+  sink_stores();
   load(wave + kPfWaves, l1);
+  sink_stores();
   for (int j = wave; j < ntiles; j += 3 * kPfWaves) {
     load(j + 2 * kPfWaves, l2);
     process(j, l0);
