@@ -7,6 +7,9 @@ latent, Top-512).  Inputs are synthetic, seeded, and already resident in HBM
 when timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --config 2             # causal prefill of 4,096 rows against
+                                           # 65,536 cached: one Full layer, dense
+                                           # FP8 indexer, MFMA roofline
     python bench.py --copy-calibration     # plain device copy of known size, for
                                            # scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
 """
@@ -25,7 +28,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
 METRIC = "CSA2 decode tokens/s (B=32, 64K ctx) + % of HBM roofline"
+PREFILL_METRIC = "CSA2 prefill tokens/s (4,096 rows vs 64K ctx) + % of FP8 MFMA roofline (dense indexer)"
 
 
 def scan_bytes(spec) -> int:
@@ -34,6 +39,18 @@ def scan_bytes(spec) -> int:
     and head weights (h_idx x 4 B)."""
     vis = spec.q_vis()
     return int(vis.sum()) * 128 + spec.nq * spec.h_idx * (128 + 4)
+
+
+def dense_flops(spec) -> int:
+    """Algorithmic FLOP of the dense prefill indexer: every causal
+    (query, visible entry) pair costs h_idx dot products of length 128."""
+    return int(spec.q_vis().sum()) * 2 * spec.h_idx * 128
+
+
+def attn_bytes(spec) -> int:
+    """Algorithmic bytes of one attention layer: k gathered rows (272 B) and
+    their indices per query, bf16 Q, fp32 O and LSE."""
+    return spec.nq * (spec.k * 272 + spec.k * 4 + spec.h * 512 * 2 + spec.h * 512 * 4 + spec.h * 4)
 
 
 def scan_source_hash() -> str:
@@ -112,6 +129,137 @@ def cpu_baseline(spec, dc, budget_s: float = 12.0):
                       f"in {el:.1f} s (fp64 NumPy, host cores {len(os.sched_getaffinity(0))})"}
 
 
+def cpu_baseline_prefill(spec, dc, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the prefill step: the append of
+    all new rows once, then index + select + attend for evenly spaced query
+    rows (first and last included) until the budget is spent; the step time is
+    extrapolated linearly to every row."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as W
+    from oracle import csa2_oracle as O
+
+    vis_all = spec.q_vis()
+    ps = 64
+    npg = (int(vis_all.max()) + ps - 1) // ps
+    cache = O.Cache.empty(npg, ps, np.arange(npg, dtype=np.int32)[None], [spec.seq_len_after(0)])
+    c = spec.cached[0]
+    kv = W.kv_rows(spec, 0, "cuda").cpu().numpy().view(np.uint16)
+    ik = W.idxk_rows(spec, 0, "cuda").cpu().numpy().view(np.uint16)
+    O.append_quant_fp4(cache, np.arange(c), kv[:c], ik[:c])
+    qi, w, q = (x.cpu().numpy() for x in dc.inputs[0])
+    q = q.view(np.uint16)
+    t0 = time.perf_counter()
+    O.append_quant_fp4(cache, np.arange(c, c + spec.n_new), kv[c:], ik[c:])
+    t_append = time.perf_counter() - t0
+    rows = np.unique(np.linspace(0, spec.nq - 1, 64).round().astype(np.int64))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        i = int(rows[done % len(rows)])
+        O.layer_step(O.REINDEX, cache, q[i:i + 1], [0], [int(vis_all[i])], spec.k, spec.sm_scale,
+                     q_idx=qi[i:i + 1], w=w[i:i + 1])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and done >= len(rows):
+            break
+    per_row = el / done
+    step_s = t_append + per_row * spec.nq
+    blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()]
+    cores = max(blas) if blas else 1
+    return {"value": spec.nq / step_s, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"append of all {spec.n_new} rows ({t_append:.2f} s) + {done} query rows of {spec.nq} "
+                      f"(64 evenly spaced incl. first and last) in {el:.1f} s, extrapolated linearly to "
+                      f"{spec.nq} rows (fp64 NumPy, host cores {len(os.sched_getaffinity(0))})"}
+
+
+def bench_prefill(args, spec, dc) -> int:
+    """One step = one Full layer over the prefill chunk: append of the new
+    rows, dense indexer, Top-K, attention.  The dominant contraction is the
+    dense indexer's candidate kernel (FP8 MFMA); the roofline is reported on it."""
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    from fp4_kv_cache_layer_amd import _lib as L
+
+    for _ in range(args.warmup):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ring = ops.TimingRing(L.KCLASS_DENSE, args.steps)
+    ring.install()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ring.uninstall()
+    prod_ms = ring.durations_ms()
+
+    classes = (L.KCLASS_APPEND, L.KCLASS_SCAN, L.KCLASS_SELECT, L.KCLASS_ATTN, L.KCLASS_DENSE)
+    rings = {k: ops.TimingRing(k, args.steps) for k in classes}
+    for r in rings.values():
+        r.install()
+    for _ in range(args.steps):
+        dc.run_group()
+    for r in rings.values():
+        r.uninstall()
+    dur = {k: r.durations_ms() for k, r in rings.items()}
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dc.run_group()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def avg(xs):
+        return round(statistics.mean(xs) * 1e3, 2) if xs else None
+
+    flops = dense_flops(spec)
+    prod_avg_s = statistics.mean(prod_ms) / 1e3
+    achieved = flops / prod_avg_s / 1e12
+    index_s = statistics.mean(dur[L.KCLASS_SCAN]) / 1e3
+    ab = attn_bytes(spec)
+    attn_s = statistics.mean(dur[L.KCLASS_ATTN]) / 1e3
+    out = {
+        "metric": PREFILL_METRIC,
+        "value": round(spec.nq / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "global_batch": 1, "seq_len": spec.cached[0] + spec.n_new,
+                   "prefill_rows": spec.nq, "modes": "full", "topk": spec.k, "heads": spec.h,
+                   "indexer_heads": spec.h_idx, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_scan_kernel", "achieved": round(achieved, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": flops, "avg_launch_us": round(prod_avg_s * 1e6, 2)},
+        "indexer_all_kernels": {"avg_us": round(index_s * 1e6, 2),
+                                "mfma_frac": round(flops / index_s / 1e12 / FP8_PEAK_TFLOPS, 4)},
+        "attention": {"avg_us": round(attn_s * 1e6, 2), "bytes": ab,
+                      "GBps": round(ab / attn_s / 1e9, 1), "hbm_frac": round(ab / attn_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernels_avg_us": {"append": avg(dur[L.KCLASS_APPEND]), "indexer": avg(dur[L.KCLASS_SCAN]),
+                           "indexer_product": avg(dur[L.KCLASS_DENSE]), "select": avg(dur[L.KCLASS_SELECT]),
+                           "attn": avg(dur[L.KCLASS_ATTN])},
+        "ms_per_step_no_events": round(ms_plain, 5),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_prefill(spec, dc)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,7 +288,8 @@ def main() -> int:
     print(f"[bench] building {spec.name}", file=sys.stderr, flush=True)
     dc = runner.DeviceCase(spec, gen_device="cuda")
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    if spec.prefill:
+        return bench_prefill(args, spec, dc)
 
     for _ in range(args.warmup):
         dc.run_group()
@@ -249,7 +398,7 @@ def main() -> int:
         "group_hbm_frac": None,
     }
     # whole-group algorithmic bytes: scans + gathered rows + Q + O + LSE + append
-    attn_b = spec.nq * (spec.k * 272 + spec.h * 512 * 2 + spec.h * 512 * 4 + spec.h * 4 + spec.k * 4)
+    attn_b = attn_bytes(spec)
     group_b = n_scan * sbytes + n_attn * attn_b + spec.num_seqs * spec.n_new * (1024 + 256 + 272 + 128 + 4)
     out["group_hbm_frac"] = round(group_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline:

@@ -13,7 +13,7 @@ c_int32, c_void_p, c_float, c_size_t = ctypes.c_int32, ctypes.c_void_p, ctypes.c
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
-KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN = 0, 1, 2, 3
+KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE = 0, 1, 2, 3, 4
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
 STEP_DENSE_INDEX = 1
 

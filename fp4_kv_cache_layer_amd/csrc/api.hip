@@ -10,7 +10,7 @@ using namespace csa2;
 
 namespace {
 
-csa2_timing_ring* g_rings[CSA2_NUM_KCLASSES] = {nullptr, nullptr, nullptr, nullptr};
+csa2_timing_ring* g_rings[CSA2_NUM_KCLASSES] = {};
 
 // Takes the next slot of a kernel class's timing ring, if one is installed;
 // the launch records the slot's events as part of its dispatches.
@@ -126,8 +126,9 @@ csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w,
   if (dense) {
     // the dense indexer leaves a compacted candidate list: only the final select remains
     if (max_vis > 0) {
-      TimedLaunch t(CSA2_KCLASS_SCAN);
-      csa2_status st = hip_status(launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, s, t.ev));
+      TimedLaunch t(CSA2_KCLASS_SCAN), tp(CSA2_KCLASS_DENSE);
+      csa2_status st =
+          hip_status(launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, s, t.ev, tp.ev));
       if (st != CSA2_OK) return st;
     }
     TimedLaunch t(CSA2_KCLASS_SELECT);

@@ -77,11 +77,12 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
 
 // Dense form for many queries of one sequence (q_seq[0]): leaves the same
 // inputs for the final select (candidate list, candidate histogram, scores of
-// the candidates), with scores bit-identical to the per-query scan.  Its events
-// cover the threshold, candidate, full-rescore and compaction kernels.
+// the candidates), with scores bit-identical to the per-query scan.  ev covers
+// the threshold, candidate, full-rescore and compaction kernels, ev_product
+// the candidate (matrix-product) kernel alone.
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                               hipStream_t s, const KEvents& ev = {});
+                               hipStream_t s, const KEvents& ev = {}, const KEvents& ev_product = {});
 // Expected candidates per query of the dense indexer, in units of k (0 sends
 // every query through the full rescore).
 extern int g_prefill_cand_factor;

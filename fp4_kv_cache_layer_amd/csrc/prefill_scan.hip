@@ -471,9 +471,10 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, IndexW
 
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                               hipStream_t s, const KEvents& ev) {
+                               hipStream_t s, const KEvents& ev, const KEvents& ev_product) {
   if (nq <= 0 || max_vis <= 0) {
     record_empty(ev, s);
+    record_empty(ev_product, s);
     return hipSuccess;
   }
   int chunk, per_xcd;
@@ -485,13 +486,13 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
   const int factor = g_prefill_cand_factor;
   if (qpt == 2) {
     launch(prefill_tau_kernel<2>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
-    launch(prefill_scan_kernel<2, false>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+    launch(prefill_scan_kernel<2, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
     launch(prefill_scan_kernel<2, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
   } else {
     launch(prefill_tau_kernel<1>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
-    launch(prefill_scan_kernel<1, false>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+    launch(prefill_scan_kernel<1, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
     launch(prefill_scan_kernel<1, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);

@@ -230,8 +230,10 @@ const char* csa2_status_string(csa2_status st);
  * (start when the class's first kernel begins, stop when its last kernel
  * ends), so no separate stream operations are added.  Events are created and
  * destroyed by the caller (hipEventCreate); the ring struct must outlive its
- * installation.  Classes: 0 append, 1 indexer scan, 2 Top-K select,
- * 3 attention.  Pass ring = NULL to uninstall.  Process-wide, not
+ * installation.  Classes: 0 append, 1 indexer scan (for the dense indexer:
+ * threshold, candidates, full rescore and compaction), 2 Top-K select,
+ * 3 attention, 4 the dense indexer's matrix-product (candidate) kernel
+ * alone.  Pass ring = NULL to uninstall.  Process-wide, not
  * thread-safe: meant for benchmarks. */
 typedef struct {
   hipEvent_t* start;     /* [capacity] */
@@ -244,7 +246,8 @@ typedef struct {
 #define CSA2_KCLASS_SCAN   1
 #define CSA2_KCLASS_SELECT 2
 #define CSA2_KCLASS_ATTN   3
-#define CSA2_NUM_KCLASSES  4
+#define CSA2_KCLASS_DENSE  4
+#define CSA2_NUM_KCLASSES  5
 csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
 
 #ifdef __cplusplus
