@@ -16,7 +16,7 @@ SOURCES = ["api.hip", "append_quant.hip", "index_scan.hip", "prefill_scan.hip", 
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     f"--offload-arch={ARCH}",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,6 +25,8 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
+SOURCE_FLAGS = {s: [] for s in SOURCES}
+BUILD_DIR = os.path.join(ROOT, "_build")
 
 
 def hipcc() -> str:
@@ -34,20 +36,37 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into one shared library; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose: bool):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(proc, verbose: bool, what: str) -> None:
+    text, _ = proc.communicate()
+    out = "\n".join(l for l in text.splitlines()
                     if "packed-fp32-ops" not in l and "unknown target feature" not in l.lower())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every HIP source (in parallel, each with its own flags) and
+    links them into one shared library; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs, procs = [], []
+    for s in SOURCES:
+        obj = os.path.join(BUILD_DIR, s.replace(".hip", ".o"))
+        objs.append(obj)
+        procs.append((s, _run([hipcc(), *FLAGS, *SOURCE_FLAGS[s], *inc, "-c", os.path.join(CSRC, s), "-o", obj],
+                              verbose)))
+    for s, p in procs:
+        _finish(p, verbose, s)
+    tmp = LIB + ".tmp"
+    _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose), verbose, "link")
     os.replace(tmp, LIB)
     return LIB
 

@@ -310,11 +310,6 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
       return g == 0 ? sq[0] : g == 1 ? sq[1] : g == 2 ? sq[2] : sq[3];
     }
   };
-  auto set_scores = [&](const intx8& bop, int p) {
-    floatx4 acc[kPerSet];
-    products(bop, p, acc);
-    return finish(p, acc);
-  };
 
   uint32_t cnt[kSets][4];                            // candidates per (set, row): wave-uniform
 #pragma unroll

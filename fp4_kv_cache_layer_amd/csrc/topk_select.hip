@@ -45,32 +45,70 @@ __device__ __forceinline__ float key_floor_float(uint32_t key) {
   return __uint_as_float(bits);
 }
 
-// Block-wide search over a descending-ordered histogram h[0..nb): the largest
-// digit d* whose suffix count reaches need (1 <= need <= total), and the count
-// strictly above it.  scratch holds NT/64 words; result[0..1] receives (d*, above).
-template <int NT>
-__device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* scratch, uint32_t* result) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (nb + NT - 1) / NT;
-  // thread tid covers descending positions [tid*per, tid*per + per) = digits nb-1-pos
-  uint32_t mine = 0;
-  for (int p = tid * per; p < min(nb, tid * per + per); ++p) mine += h[nb - 1 - p];
-  uint32_t x = mine;
+// Search over a descending-ordered histogram h[0..nb) (nb <= 2048): the
+// largest digit d* whose suffix count reaches need (1 <= need <= total), and
+// the count strictly above it, written to result[0..1].  One wave does the
+// search (lane l sums the digits at descending positions [l*per, l*per + per),
+// then a wave scan finds the lane holding d*); the workgroup barrier at the
+// end publishes the result.  Callers have h complete (a barrier) first.
+__device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* result) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    if (nb == kHistBins) {
+      // lane l holds digits [base, base + 32), base = nb - 32 (l + 1), read as
+      // eight 16-byte vectors; descending position i is digit base + 31 - i
+      const int base = nb - 32 * (lane + 1);
+      uint32_t v[32];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) scratch[wave] = x;
-  lds_barrier();
-  uint32_t excl = x - mine;
-  for (int i = 0; i < wave; ++i) excl += scratch[i];
-  if (excl < need && need <= excl + mine) {
-    uint32_t run = excl;
-    for (int p = tid * per; p < min(nb, tid * per + per); ++p) {
-      const uint32_t v = h[nb - 1 - p];
-      if (need <= run + v) { result[0] = (uint32_t)(nb - 1 - p); result[1] = run; break; }
-      run += v;
+      for (int j = 0; j < 8; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(h + base + 4 * j);
+        v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
+      }
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) mine += v[i];
+      uint32_t x = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      const uint32_t excl = x - mine;
+      if (excl < need && need <= x) {
+        uint32_t run = excl, dig = 0, above = 0;
+        bool done = false;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t c = v[31 - i];
+          const bool hit = !done && need <= run + c;
+          dig = hit ? (uint32_t)(base + 31 - i) : dig;
+          above = hit ? run : above;
+          done = done || hit;
+          run += c;
+        }
+        result[0] = dig;
+        result[1] = above;
+      }
+    } else {
+      const int per = (nb + 63) >> 6;
+      const int p0 = min(nb, lane * per), p1 = min(nb, p0 + per);
+      uint32_t mine = 0;
+      for (int p = p0; p < p1; ++p) mine += h[nb - 1 - p];
+      uint32_t x = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      const uint32_t excl = x - mine;
+      if (excl < need && need <= x) {
+        uint32_t run = excl;
+        for (int p = p0; p < p1; ++p) {
+          const uint32_t c = h[nb - 1 - p];
+          if (need <= run + c) { result[0] = (uint32_t)(nb - 1 - p); result[1] = run; break; }
+          run += c;
+        }
+      }
     }
   }
   lds_barrier();
@@ -97,9 +135,8 @@ __device__ __forceinline__ void wave_append(bool flag, T value, int* counter, T*
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kCollectThreads)
 topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int nslices) {
-  __shared__ uint32_t h[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kHistBins];
   __shared__ int32_t list[kCollectSlice];             // this slice's candidates
-  __shared__ uint32_t scratch[kCollectThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ int count, base;
   const int q = blockIdx.x / nslices;
@@ -120,16 +157,38 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
   for (int u = 0; u < kPer; ++u) v[u] = sc4[min(u * kCollectThreads + tid, nvec - 1)];
   if (tid == 0) count = 0;
   lds_barrier();
-  find_digit<kCollectThreads>(h, kHistBins, (uint32_t)k, scratch, res);
+  find_digit(h, kHistBins, (uint32_t)k, res);
   const float floor_s = key_floor_float(res[0] << (32 - kHistBits));
+  // count this thread's candidates, one scan and one reservation per wave,
+  // then write them in order
+  uint32_t mine = 0;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int vi = u * kCollectThreads + tid;
     const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int t = t0 + 4 * vi + c;
-      wave_append<int32_t>(t < t1 && e[c] >= floor_s, t, &count, list, kCollectSlice);
+    for (int c = 0; c < 4; ++c) mine += (t0 + 4 * vi + c < t1 && e[c] >= floor_s) ? 1u : 0u;
+  }
+  const int lane = tid & 63;
+  uint32_t x = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  int wbase = 0;
+  if (lane == 63 && x) wbase = atomicAdd(&count, (int)x);
+  int pos = __shfl(wbase, 63) + (int)(x - mine);
+  if (mine) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int vi = u * kCollectThreads + tid;
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = t0 + 4 * vi + c;
+        if (t < t1 && e[c] >= floor_s) list[pos++] = t;   // at most kCollectSlice entries in all
+      }
     }
   }
   lds_barrier();
@@ -148,7 +207,7 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
 namespace {
 
 struct SelShared {
-  uint32_t h[kHistBins];
+  alignas(16) uint32_t h[kHistBins];
   int32_t sel[kSelCap];
   uint64_t tie[kTieCap];                        // parked keys; reused as the output bitmap
   uint32_t scratch[kSelectThreads / 64];
@@ -183,7 +242,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
 
   uint32_t need = (uint32_t)k;
   int nbits = kHistBits;
-  find_digit<kSelectThreads>(S.h, kHistBins, need, S.scratch, S.res);
+  find_digit(S.h, kHistBins, need, S.res);
   int dstar = (int)S.res[0];
   uint64_t P = (uint64_t)dstar;
   need -= S.res[1];
@@ -201,7 +260,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
       if ((C >> (64 - nbits)) == P) atomicAdd(&S.h[(uint32_t)(C >> (64 - nbits - d)) & ((1u << d) - 1)], 1u);
     }
     lds_barrier();
-    find_digit<kSelectThreads>(S.h, 1 << d, need, S.scratch, S.res);
+    find_digit(S.h, 1 << d, need, S.res);
     dstar = (int)S.res[0];
     need -= S.res[1];
     P = (P << d) | (uint64_t)dstar;
@@ -210,21 +269,25 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
     lds_barrier();
   }
 
-  // candidates: prefix above P -> selected; prefix equal to P -> parked
-  for (int i0 = 0; i0 < ncand; i0 += kSelectThreads) {
-    const int i = i0 + tid;
-    bool up = false, eq = false;
-    uint64_t C = 0;
-    int t = 0;
-    if (i < ncand) {
-      t = cand[i];
-      C = composite(sc[t], t);
+  // candidates: prefix above P -> selected; prefix equal to P -> parked.
+  // Batches of kCandBatch per thread: all their indices, then all their
+  // scores, are in flight together.
+  constexpr int kCandBatch = 4;
+  for (int i0 = 0; i0 < ncand; i0 += kCandBatch * kSelectThreads) {
+    int t[kCandBatch];
+    float sv[kCandBatch];
+#pragma unroll
+    for (int b = 0; b < kCandBatch; ++b) t[b] = cand[min(i0 + b * kSelectThreads + tid, ncand - 1)];
+#pragma unroll
+    for (int b = 0; b < kCandBatch; ++b) sv[b] = sc[t[b]];
+#pragma unroll
+    for (int b = 0; b < kCandBatch; ++b) {
+      const bool valid = i0 + b * kSelectThreads + tid < ncand;
+      const uint64_t C = composite(sv[b], t[b]);
       const uint64_t pre = C >> (64 - nbits);
-      up = pre > P;
-      eq = pre == P;
+      wave_append<int32_t>(valid && pre > P, t[b], &S.selcnt, S.sel, kSelCap);
+      wave_append<uint64_t>(valid && pre == P, C, &S.tiecnt, S.tie, kTieCap);
     }
-    wave_append<int32_t>(up, t, &S.selcnt, S.sel, kSelCap);
-    wave_append<uint64_t>(eq, C, &S.tiecnt, S.tie, kTieCap);
   }
   lds_barrier();
   const int ntie = min(S.tiecnt, kTieCap);
@@ -252,7 +315,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
       if (C) atomicAdd(&S.h[(uint32_t)(C >> sh) & ((1u << d) - 1)], 1u);
     }
     lds_barrier();
-    find_digit<kSelectThreads>(S.h, 1 << d, need, S.scratch, S.res);
+    find_digit(S.h, 1 << d, need, S.res);
     dstar = (int)S.res[0];
     for (int i = tid; i < ntie; i += kSelectThreads) {
       const uint64_t C = S.tie[i];
