@@ -267,6 +267,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--aux-streams", type=int, default=0,
+                    help="run the timed multi-layer group as one csa2_group_step with this many auxiliary "
+                         "streams (0: one csa2_layer_step call per layer); the other mode is timed too")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "scan_traffic.json"),
                     help="HBM traffic per scan launch measured with rocprofv3 counters (optional)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -286,13 +289,16 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     spec = W.config(args.config)
     print(f"[bench] building {spec.name}", file=sys.stderr, flush=True)
-    dc = runner.DeviceCase(spec, gen_device="cuda")
+    aux = args.aux_streams if len(spec.modes) > 1 else 0
+    # the case carries one workspace per layer, so both execution modes can run on it
+    dc = runner.DeviceCase(spec, gen_device="cuda", group=max(aux, 1) if len(spec.modes) > 1 else 0)
+    step = dc.run_group if aux else dc.run_layers
     torch.cuda.synchronize()
     if spec.prefill:
         return bench_prefill(args, spec, dc)
 
     for _ in range(args.warmup):
-        dc.run_group()
+        step()
     torch.cuda.synchronize()
 
     # Timed region: K steps; the dominant kernel (indexer scan) carries
@@ -304,7 +310,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        dc.run_group()
+        step()
     torch.cuda.synchronize()
     ms_events = (time.perf_counter() - t0) * 1e3 / args.steps
     scan_ring.uninstall()
@@ -318,7 +324,7 @@ def main() -> int:
     for r in rings.values():
         r.install()
     for _ in range(args.steps):
-        dc.run_group()
+        step()
     for r in rings.values():
         r.uninstall()
     dur = {k: r.durations_ms() for k, r in rings.items()}
@@ -334,7 +340,7 @@ def main() -> int:
     for e0, e1 in step_ev:
         torch.sum(scrub, dim=0, out=sink)
         e0.record()
-        dc.run_group()
+        step()
         e1.record()
     sring.uninstall()
     torch.cuda.synchronize()
@@ -346,9 +352,22 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        dc.run_group()
+        step()
     torch.cuda.synchronize()
     ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the other execution mode, no timestamps: one csa2_group_step per step
+    # (Reuse attentions on an auxiliary stream beside the next layers) or
+    # per-layer calls
+    other = dc.run_layers if aux else dc.run_group
+    for _ in range(3):
+        other()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        other()
+    torch.cuda.synchronize()
+    ms_other = (time.perf_counter() - t0) * 1e3 / args.steps
 
     ms = ms_events
     value = spec.num_seqs * spec.n_new / (ms / 1e3) if spec.n_new else spec.nq / (ms / 1e3)
@@ -382,6 +401,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": spec.name, "global_batch": spec.num_seqs, "seq_len": spec.cached[0] + spec.n_new,
                    "modes": "full,reindex,reuse,reuse", "topk": spec.k, "heads": spec.h, "indexer_heads": spec.h_idx,
+                   "execution": (f"csa2_group_step, Reuse attentions on {aux} auxiliary stream(s)" if aux
+                                 else "one csa2_layer_step call per layer"),
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "index_scan_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -395,6 +416,10 @@ def main() -> int:
                            "scan_reindex_us": avg(scrubbed_scan[1::n_scan]) if n_scan > 1 else None,
                            "scan_frac": round(sbytes / (statistics.mean(scrubbed_scan) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "ms_per_step_no_events": round(ms_plain, 5),
+        "other_execution": {"execution": ("one csa2_layer_step call per layer" if aux else
+                                          "csa2_group_step, Reuse attentions on 1 auxiliary stream"),
+                            "ms_per_step_no_events": round(ms_other, 5),
+                            "tokens_per_s": round(spec.num_seqs * spec.n_new / (ms_other / 1e3), 1)},
         "group_hbm_frac": None,
     }
     # whole-group algorithmic bytes: scans + gathered rows + Q + O + LSE + append

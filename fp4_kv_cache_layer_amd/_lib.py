@@ -33,6 +33,14 @@ class StepArgs(ctypes.Structure):
                 ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32)]
 
 
+GROUP_MAX_LAYERS, GROUP_MAX_AUX = 64, 4
+
+
+class GroupExec(ctypes.Structure):
+    _fields_ = [("aux", c_void_p * GROUP_MAX_AUX), ("n_aux", c_int32),
+                ("events", ctypes.POINTER(c_void_p)), ("n_events", c_int32)]
+
+
 class TimingRing(ctypes.Structure):
     _fields_ = [("start", ctypes.POINTER(c_void_p)), ("stop", ctypes.POINTER(c_void_p)),
                 ("capacity", c_int32), ("count", c_int32)]
@@ -60,13 +68,16 @@ def load() -> ctypes.CDLL:
     lib.csa2_sparse_attn.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
+    lib.csa2_group_events.argtypes = [c_int32, c_int32]
+    lib.csa2_group_events.restype = c_int32
+    lib.csa2_group_step.argtypes = [c_int32, P(c_int32), P(StepArgs), c_void_p, P(GroupExec)]
     lib.csa2_status_string.argtypes = [c_int32]
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_set_timing.argtypes = [c_int32, P(TimingRing)]
     lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_set_timing", "csa2_set_prefill_candidate_factor"):
+               "csa2_layer_step", "csa2_group_step", "csa2_set_timing", "csa2_set_prefill_candidate_factor"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

@@ -143,6 +143,115 @@ csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w,
   return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s, t.ev));
 }
 
+// One layer of a step, validated, split into the stages that the group
+// scheduler places on streams: append, indexer scan, Top-K select, attention.
+struct Step {
+  csa2_mode mode;
+  const csa2_step_args* a;
+  CacheArgs ca;
+  bool dense;
+  IndexWs iw;
+  void* part;
+};
+
+// Every check of csa2_layer_step, before anything is launched.
+csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
+  if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & ~CSA2_STEP_DENSE_INDEX) return CSA2_ERR_INVALID_ARG;
+  csa2_status st;
+  if (mode == CSA2_FULL) {
+    st = validate_append(a->cache, a->new_slots, a->new_kv, a->new_idxk, a->n_new, &p->ca);
+    if (st != CSA2_OK) return st;
+  } else if (a->n_new != 0 || a->new_slots || a->new_kv || a->new_idxk) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  if (mode != CSA2_REUSE) {
+    st = validate_index(a->cache, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx,
+                        a->cnt, a->ws, a->ws_bytes, &p->ca);
+    if (st != CSA2_OK) return st;
+  } else if (a->q_idx || a->w || a->h_idx != 0) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  st = validate_attn(a->cache, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out, a->lse, &p->ca);
+  if (st != CSA2_OK) return st;
+  p->mode = mode;
+  p->a = a;
+  p->dense = (a->flags & CSA2_STEP_DENSE_INDEX) != 0;
+  p->iw = IndexWs{};
+  p->part = nullptr;
+  if (a->nq == 0) return CSA2_OK;
+  const size_t z = zero_state_bytes(a->nq), part = attn_part_bytes(a->nq, a->h, a->k);
+  if (mode != CSA2_REUSE) {
+    if (a->ws_bytes < z + part + index_score_bytes(a->nq, a->max_vis)) return CSA2_ERR_WORKSPACE;
+    p->iw = index_ws(a->ws, a->nq, a->max_vis, z + part);
+  } else if (a->ws && !aligned(a->ws, 16)) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  p->part = attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k);
+  return CSA2_OK;
+}
+
+csa2_status stage_append(const Step& p, hipStream_t s) {
+  const csa2_step_args* a = p.a;
+  if (p.mode != CSA2_FULL || a->n_new == 0) return CSA2_OK;
+  TimedLaunch t(CSA2_KCLASS_APPEND);
+  return hip_status(launch_append_quant(p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
+}
+
+csa2_status stage_scan(const Step& p, hipStream_t s) {
+  const csa2_step_args* a = p.a;
+  if (p.mode == CSA2_REUSE || a->nq == 0 || a->max_vis == 0) return CSA2_OK;
+  if (p.dense) {
+    TimedLaunch t(CSA2_KCLASS_SCAN), tp(CSA2_KCLASS_DENSE);
+    return hip_status(launch_prefill_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k,
+                                          a->max_vis, p.iw, s, t.ev, tp.ev));
+  }
+  TimedLaunch t(CSA2_KCLASS_SCAN);
+  return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->max_vis, p.iw, s,
+                                      t.ev));
+}
+
+csa2_status stage_select(const Step& p, hipStream_t s) {
+  const csa2_step_args* a = p.a;
+  if (p.mode == CSA2_REUSE || a->nq == 0) return CSA2_OK;
+  TimedLaunch t(CSA2_KCLASS_SELECT);
+  if (p.dense) return hip_status(launch_topk_final(p.iw, a->q_vis, a->nq, a->k, a->idx, a->cnt, s, t.ev));
+  return hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, a->k, a->max_vis, a->idx, a->cnt, s, t.ev));
+}
+
+csa2_status stage_attn(const Step& p, hipStream_t s) {
+  const csa2_step_args* a = p.a;
+  if (a->nq == 0) return CSA2_OK;
+  TimedLaunch t(CSA2_KCLASS_ATTN);
+  return hip_status(launch_sparse_attn(p.ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
+                                       a->lse, p.part, s, t.ev));
+}
+
+csa2_status run_step(const Step& p, hipStream_t s) {
+  csa2_status st = stage_append(p, s);
+  if (st == CSA2_OK) st = stage_scan(p, s);
+  if (st == CSA2_OK) st = stage_select(p, s);
+  if (st == CSA2_OK) st = stage_attn(p, s);
+  return st;
+}
+
+// Layer j must not overlap layer i (i < j) when they share memory that
+// either writes: a workspace, index/count buffers one of them writes, an
+// output, or (a Full layer j appending) a cache that layer i reads.
+bool layers_conflict(const Step& i, const Step& j) {
+  const csa2_step_args *a = i.a, *b = j.a;
+  auto same = [](const void* x, const void* y) { return x != nullptr && x == y; };
+  if (same(a->ws, b->ws)) return true;
+  if (same(a->out, b->out) || same(a->lse, b->lse)) return true;
+  const bool iw = i.mode != CSA2_REUSE, jw = j.mode != CSA2_REUSE;   // writes idx/cnt
+  if ((iw || jw) && (same(a->idx, b->idx) || same(a->cnt, b->cnt))) {
+    // the one case ordered by stream placement: j reuses what i selected
+    if (!(iw && !jw)) return true;
+  }
+  if (j.mode == CSA2_FULL && b->n_new > 0 && same(i.ca.kv, j.ca.kv)) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,44 +337,160 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
-  if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
-  if (a->flags & ~CSA2_STEP_DENSE_INDEX) return CSA2_ERR_INVALID_ARG;
-  CacheArgs ca;
-  csa2_status st;
-  if (mode == CSA2_FULL) {
-    st = validate_append(a->cache, a->new_slots, a->new_kv, a->new_idxk, a->n_new, &ca);
-    if (st != CSA2_OK) return st;
-  } else if (a->n_new != 0 || a->new_slots || a->new_kv || a->new_idxk) {
-    return CSA2_ERR_INVALID_ARG;
-  }
-  if (mode != CSA2_REUSE) {
-    st = validate_index(a->cache, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx,
-                        a->cnt, a->ws, a->ws_bytes, &ca);
-    if (st != CSA2_OK) return st;
-  } else if (a->q_idx || a->w || a->h_idx != 0) {
-    return CSA2_ERR_INVALID_ARG;
-  }
-  st = validate_attn(a->cache, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out, a->lse, &ca);
+  Step p;
+  csa2_status st = prepare_step(mode, a, &p);
   if (st != CSA2_OK) return st;
+  return run_step(p, s);
+}
 
-  if (mode == CSA2_FULL && a->n_new > 0) {
-    TimedLaunch t(CSA2_KCLASS_APPEND);
-    st = hip_status(launch_append_quant(ca.kv, ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
+int32_t csa2_group_events(int32_t n_layers, int32_t n_aux) {
+  if (n_layers < 0 || n_layers > CSA2_GROUP_MAX_LAYERS || n_aux < 0 || n_aux > CSA2_GROUP_MAX_AUX) return -1;
+  return 1 + 3 * n_layers + n_aux;
+}
+
+csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_args* layers, hipStream_t s,
+                            const csa2_group_exec* ex) {
+  if (n < 0 || n > CSA2_GROUP_MAX_LAYERS) return CSA2_ERR_INVALID_ARG;
+  if (n == 0) return CSA2_OK;
+  if (!modes || !layers) return CSA2_ERR_INVALID_ARG;
+  const int n_aux = ex ? ex->n_aux : 0;
+  if (n_aux < 0 || n_aux > CSA2_GROUP_MAX_AUX) return CSA2_ERR_INVALID_ARG;
+  if (n_aux > 0) {
+    if (!ex->events || ex->n_events < csa2_group_events(n, n_aux)) return CSA2_ERR_INVALID_ARG;
+    for (int j = 0; j < n_aux; ++j) {
+      if (!ex->aux[j] || ex->aux[j] == s) return CSA2_ERR_INVALID_ARG;
+      for (int j2 = 0; j2 < j; ++j2)
+        if (ex->aux[j2] == ex->aux[j]) return CSA2_ERR_INVALID_ARG;
+    }
+    for (int e = 0; e < csa2_group_events(n, n_aux); ++e)
+      if (!ex->events[e]) return CSA2_ERR_INVALID_ARG;
+  }
+  Step steps[CSA2_GROUP_MAX_LAYERS];
+  for (int i = 0; i < n; ++i) {
+    csa2_status st = prepare_step(modes[i], &layers[i], &steps[i]);
     if (st != CSA2_OK) return st;
   }
-  if (a->nq == 0) return CSA2_OK;
-  const size_t z = zero_state_bytes(a->nq), part = attn_part_bytes(a->nq, a->h, a->k);
-  if (mode != CSA2_REUSE) {
-    if (a->ws_bytes < z + part + index_score_bytes(a->nq, a->max_vis)) return CSA2_ERR_WORKSPACE;
-    st = run_index(ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx, a->cnt,
-                   index_ws(a->ws, a->nq, a->max_vis, z + part), (a->flags & CSA2_STEP_DENSE_INDEX) != 0, s);
-    if (st != CSA2_OK) return st;
-  } else if (a->ws && !aligned(a->ws, 16)) {
-    return CSA2_ERR_INVALID_ARG;
+  if (n_aux == 0) {
+    for (int i = 0; i < n; ++i) {
+      csa2_status st = run_step(steps[i], s);
+      if (st != CSA2_OK) return st;
+    }
+    return CSA2_OK;
   }
-  TimedLaunch t(CSA2_KCLASS_ATTN);
-  return hip_status(launch_sparse_attn(ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
-                                       a->lse, attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k), s, t.ev));
+
+  // Full and Reindex layers run whole on s, in layer order.  A Reuse layer
+  // (attention only) runs on an auxiliary stream, round-robin, as soon as
+  // the select it reuses is done, beside the layers after it on s.  Events
+  // carry the cross-stream order, and only the edges that stream order does
+  // not already imply are enqueued (each record or wait costs host time).
+  hipEvent_t* const ev = ex->events;
+  auto ev_sel = [&](int i) { return ev[1 + i]; };
+  auto ev_done = [&](int i) { return ev[1 + n + i]; };
+  auto ev_append = [&](int i) { return ev[1 + 2 * n + i]; };
+  auto ev_aux = [&](int j) { return ev[1 + 3 * n + j]; };
+  auto hip = [](hipError_t e) { return e == hipSuccess; };
+
+  int aux_of[CSA2_GROUP_MAX_LAYERS], src_of[CSA2_GROUP_MAX_LAYERS], app_of[CSA2_GROUP_MAX_LAYERS];
+  bool need_sel[CSA2_GROUP_MAX_LAYERS] = {}, need_done[CSA2_GROUP_MAX_LAYERS] = {};
+  bool need_append[CSA2_GROUP_MAX_LAYERS] = {};
+  int rr = 0;
+  for (int i = 0; i < n; ++i) {
+    const Step& p = steps[i];
+    src_of[i] = -1;
+    app_of[i] = -1;                                   // latest in-group append to this layer's cache before it
+    for (int j = i - 1; j >= 0 && app_of[i] < 0; --j)
+      if (steps[j].mode == CSA2_FULL && steps[j].a->n_new > 0 && steps[j].ca.kv == p.ca.kv) app_of[i] = j;
+    if (p.mode == CSA2_REUSE) {
+      for (int j = i - 1; j >= 0 && src_of[i] < 0; --j)
+        if (steps[j].mode != CSA2_REUSE && steps[j].a->idx == p.a->idx && steps[j].a->cnt == p.a->cnt) src_of[i] = j;
+      aux_of[i] = rr++ % n_aux;
+      if (src_of[i] >= 0) need_sel[src_of[i]] = true;
+      // the source's select comes after the append on s, else wait for it
+      if (app_of[i] >= 0 && !(src_of[i] >= app_of[i])) need_append[app_of[i]] = true;
+    } else {
+      aux_of[i] = -1;
+    }
+    // conflicts that stream order does not cover
+    for (int j = 0; j < i; ++j)
+      if ((aux_of[j] >= 0 || aux_of[i] >= 0) && aux_of[j] != aux_of[i] && layers_conflict(steps[j], p))
+        need_done[j] = true;
+  }
+
+  // s-side events are numbered in record order; an auxiliary stream that has
+  // waited on event m is ordered after everything on s up to m
+  int s_seq = 0;
+  int aux_seen[CSA2_GROUP_MAX_AUX];
+  bool aux_used[CSA2_GROUP_MAX_AUX] = {};
+  for (int j = 0; j < n_aux; ++j) aux_seen[j] = 0;
+  int seq_of_sel[CSA2_GROUP_MAX_LAYERS], seq_of_done[CSA2_GROUP_MAX_LAYERS], seq_of_append[CSA2_GROUP_MAX_LAYERS];
+  bool start_recorded = false;
+  auto record_s = [&](hipEvent_t e, int* seq) {
+    *seq = 2 + s_seq++;
+    return hip(hipEventRecord(e, s));
+  };
+  auto wait_s_event = [&](int x, hipEvent_t e, int seq) {
+    if (aux_seen[x] >= seq) return true;
+    aux_seen[x] = seq;
+    return hip(hipStreamWaitEvent(ex->aux[x], e, 0));
+  };
+  auto ensure_start = [&](int x) {                   // x after the work on s before the call
+    if (aux_seen[x] > 0) return true;
+    if (!start_recorded) {
+      if (!hip(hipEventRecord(ev[0], s))) return false;
+      start_recorded = true;
+    }
+    aux_seen[x] = 1;
+    return hip(hipStreamWaitEvent(ex->aux[x], ev[0], 0));
+  };
+  // A Reuse layer on its auxiliary stream (every event it waits on has been
+  // recorded earlier in this call).
+  auto enqueue_reuse = [&](int i) {
+    const Step& p = steps[i];
+    const int x = aux_of[i];
+    hipStream_t ls = ex->aux[x];
+    aux_used[x] = true;
+    if (src_of[i] >= 0 && !wait_s_event(x, ev_sel(src_of[i]), seq_of_sel[src_of[i]])) return CSA2_ERR_HIP;
+    const int ap = app_of[i];
+    if (ap >= 0 && need_append[ap] && !wait_s_event(x, ev_append(ap), seq_of_append[ap])) return CSA2_ERR_HIP;
+    if (!ensure_start(x)) return CSA2_ERR_HIP;
+    for (int j = 0; j < i; ++j) {
+      if (aux_of[j] == x || !need_done[j] || !layers_conflict(steps[j], p)) continue;
+      const bool ok = aux_of[j] < 0 ? wait_s_event(x, ev_done(j), seq_of_done[j])
+                                    : hip(hipStreamWaitEvent(ls, ev_done(j), 0));
+      if (!ok) return CSA2_ERR_HIP;
+    }
+    csa2_status st = stage_attn(p, ls);
+    if (st != CSA2_OK) return st;
+    if (need_done[i] && !hip(hipEventRecord(ev_done(i), ls))) return CSA2_ERR_HIP;
+    return CSA2_OK;
+  };
+  for (int i = 0; i < n; ++i) {
+    const Step& p = steps[i];
+    csa2_status st = CSA2_OK;
+    if (aux_of[i] < 0) {
+      for (int j = 0; j < i; ++j)                    // earlier auxiliary layers it conflicts with
+        if (aux_of[j] >= 0 && need_done[j] && layers_conflict(steps[j], p) &&
+            !hip(hipStreamWaitEvent(s, ev_done(j), 0)))
+          return CSA2_ERR_HIP;
+      st = stage_append(p, s);
+      if (st == CSA2_OK && need_append[i] && !record_s(ev_append(i), &seq_of_append[i])) st = CSA2_ERR_HIP;
+      if (st == CSA2_OK) st = stage_scan(p, s);
+      if (st == CSA2_OK) st = stage_select(p, s);
+      if (st == CSA2_OK && need_sel[i] && !record_s(ev_sel(i), &seq_of_sel[i])) st = CSA2_ERR_HIP;
+      if (st == CSA2_OK) st = stage_attn(p, s);
+      if (st == CSA2_OK && need_done[i] && !record_s(ev_done(i), &seq_of_done[i])) st = CSA2_ERR_HIP;
+      if (st != CSA2_OK) return st;
+      continue;
+    }
+    st = enqueue_reuse(i);
+    if (st != CSA2_OK) return st;
+  }
+  for (int j = 0; j < n_aux; ++j) {
+    if (!aux_used[j]) continue;
+    if (!hip(hipEventRecord(ev_aux(j), ex->aux[j])) || !hip(hipStreamWaitEvent(s, ev_aux(j), 0)))
+      return CSA2_ERR_HIP;
+  }
+  return CSA2_OK;
 }
 
 }  // extern "C"

@@ -185,6 +185,62 @@ def csa2_layer_step(mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tenso
               new_slots, new_kv, new_idxk, ws, dense)(stream)
 
 
+class GroupCall:
+    """Prepared csa2_group_step over LayerCalls: appends and indexer scans on
+    the calling stream, selects and attentions on n_aux auxiliary streams
+    (default priority) with caller-owned events (see include/csa2.h).  With
+    n_aux = 0 the layers run in order on the calling stream."""
+
+    def __init__(self, calls, n_aux: int = 2, event_sets: int = 4):
+        lib = L.load()
+        n = len(calls)
+        self.calls = list(calls)
+        self.modes = (ctypes.c_int32 * n)(*[c.mode for c in calls])
+        self.args = (L.StepArgs * n)()
+        for i, c in enumerate(calls):
+            ctypes.memmove(ctypes.byref(self.args[i]), ctypes.byref(c.args), ctypes.sizeof(L.StepArgs))
+        # Several event sets, used in turn: re-recording an event whose last
+        # record the device has not reached yet would hold the host back, so
+        # rotating sets lets the host enqueue a few groups ahead.
+        self.exs = []
+        if n_aux > 0:
+            self.streams = [torch.cuda.Stream() for _ in range(n_aux)]
+            ne = lib.csa2_group_events(n, n_aux)
+            if ne < 0:
+                raise ValueError("group too large")
+            self.events, self._ev = [], []
+            for _ in range(max(1, event_sets)):
+                evs = [torch.cuda.Event() for _ in range(ne)]
+                for e in evs:              # materialise the hipEvent handles
+                    e.record()
+                self.events.append(evs)
+                arr = (ctypes.c_void_p * ne)(*[0] * ne)
+                self._ev.append(arr)
+            torch.cuda.synchronize()
+            for evs, arr in zip(self.events, self._ev):
+                for i, e in enumerate(evs):
+                    arr[i] = e.cuda_event
+                ex = L.GroupExec()
+                for j, st in enumerate(self.streams):
+                    ex.aux[j] = st.cuda_stream
+                ex.n_aux = n_aux
+                ex.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+                ex.n_events = ne
+                self.exs.append(ex)
+        self._turn = 0
+        self._n = n
+        self._fn = lib.csa2_group_step
+
+    def __call__(self, stream=None) -> None:
+        ex = None
+        if self.exs:
+            ex = ctypes.byref(self.exs[self._turn])
+            self._turn = (self._turn + 1) % len(self.exs)
+        st = self._fn(self._n, self.modes, self.args, _stream(stream), ex)
+        if st:
+            L.check("csa2_group_step", st)
+
+
 class TimingRing:
     """Device-event ring for one kernel class (see csa2_set_timing)."""
 

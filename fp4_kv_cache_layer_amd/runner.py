@@ -19,12 +19,17 @@ APPEND_CHUNK = 1 << 20          # rows per bulk append call
 
 class DeviceCase:
     """dense: None -> the dense prefill indexer for prefill workloads (all
-    queries in one sequence), the per-query scan otherwise."""
+    queries in one sequence), the per-query scan otherwise.  group: 0 runs
+    the layers as separate csa2_layer_step calls; n > 0 runs them as one
+    csa2_group_step with n auxiliary streams, with a workspace of their own
+    for the Reuse layers so they overlap the layers after them."""
 
     def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda",
-                 dense: Optional[bool] = None):
+                 dense: Optional[bool] = None, group: int = 0, shared_ws: bool = False):
         self.spec = spec
         self.dense = spec.prefill if dense is None else dense
+        self.group_aux = group
+        self.shared_ws = shared_ws
         self.device = device
         self.gen_device = gen_device
         pt = torch.from_numpy(W.page_table(spec))
@@ -66,9 +71,16 @@ class DeviceCase:
         spec, dev = self.spec, self.device
         nq, k = spec.nq, spec.k
         self.ws = ops.workspace(ops.FULL, nq, self.max_vis, spec.h_idx, spec.h, k, device=dev)
+        # Per-layer calls share one workspace.  A group step runs Full and
+        # Reindex layers in order on the calling stream, so they keep sharing
+        # it, while each Reuse layer, which runs beside them, gets its own.
+        self.group_ws = [self.ws if (mode != ops.REUSE or self.shared_ws) else
+                         ops.workspace(ops.REUSE, nq, self.max_vis, spec.h_idx, spec.h, k, device=dev)
+                         for li, mode in enumerate(spec.modes)] if self.group_aux > 0 else None
         self.inputs = []
         self.outputs = []
         self.calls: List[ops.LayerCall] = []
+        group_calls: List[ops.LayerCall] = []
         full_idx = full_cnt = None
         for li, mode in enumerate(spec.modes):
             qi, w, q = W.layer_queries(spec, li, self.gen_device)
@@ -78,23 +90,38 @@ class DeviceCase:
             lse = torch.empty((nq, spec.h), dtype=torch.float32, device=dev)
             if mode == ops.REUSE:
                 idx, cnt = full_idx, full_cnt
-                call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                     idx, cnt, out, lse, ws=self.ws)
             else:
                 idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
                 cnt = torch.empty(nq, dtype=torch.int32, device=dev)
                 if mode == ops.FULL:
-                    call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                         idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
-                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=self.ws, dense=self.dense)
                     full_idx, full_cnt = idx, cnt
-                else:
-                    call = ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                         idx, cnt, out, lse, q_idx=qi, w=w, ws=self.ws, dense=self.dense)
+
+            def make(ws, mode=mode, qi=qi, w=w, q=q, idx=idx, cnt=cnt, out=out, lse=lse):
+                if mode == ops.REUSE:
+                    return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                         idx, cnt, out, lse, ws=ws)
+                if mode == ops.FULL:
+                    return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                         idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
+                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=ws, dense=self.dense)
+                return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
+                                     idx, cnt, out, lse, q_idx=qi, w=w, ws=ws, dense=self.dense)
+            call = make(self.ws)
+            if self.group_ws is not None:
+                group_calls.append(make(self.group_ws[li]))
             self.outputs.append(dict(idx=idx, cnt=cnt, out=out, lse=lse))
             self.calls.append(call)
 
+        self.group = ops.GroupCall(group_calls, n_aux=self.group_aux) if self.group_aux > 0 else None
+
     def run_group(self, stream=None) -> None:
+        if self.group is not None:
+            self.group(stream)
+            return
+        self.run_layers(stream)
+
+    def run_layers(self, stream=None) -> None:
+        """The layers as separate csa2_layer_step calls, whatever `group` is."""
         for c in self.calls:
             c(stream)
 

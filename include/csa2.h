@@ -220,6 +220,52 @@ typedef struct {
  *   Reuse   = sparse_attn with the given idx/cnt */
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s);
 
+/* A group of layers that share caches and indices, run as one call.  The
+ * layers' results are exactly those of calling csa2_layer_step on each in
+ * order on s (same kernels, same inputs); the group only overlaps work that
+ * does not depend on each other.  The modes' composition is the one of
+ * "Unlocking Extreme Context Scaling with DeepSeek-V4.1-Flash", section
+ * "Compressed Sparse Attention 2 (CSA2)": Reindex and Reuse layers read an
+ * earlier Full layer's cache, Reuse layers its indices; a Reuse layer skips
+ * indexing altogether, so its attention can run beside the layers after it.
+ *
+ * Execution (ex): with ex == NULL or n_aux == 0 the layers run one after the
+ * other on s.  Otherwise Full and Reindex layers still run whole on s in
+ * layer order, and each Reuse layer runs on one of the caller's auxiliary
+ * streams (round-robin) as soon as the select whose idx/cnt it reads is done,
+ * beside the layers that follow it on s.  Layers that share a workspace, an
+ * output, an idx/cnt buffer one of them writes, or a cache a later Full layer
+ * appends to are ordered with events, so sharing buffers is always correct
+ * but removes overlap: give concurrent layers their own workspaces.  All work
+ * is ordered after what was enqueued on s before the call, and everything
+ * enqueued on s afterwards runs after all of it (s waits for every auxiliary
+ * stream used).
+ *
+ * Ownership: the caller creates the auxiliary streams (default priority,
+ * same device, none equal to s) and at least csa2_group_events(n, n_aux)
+ * events (flags without timing suffice); the call records and waits on them
+ * and keeps no reference after it returns.  Calls that overlap in time must
+ * not share events.  Errors: CSA2_ERR_INVALID_ARG for n outside
+ * [0, CSA2_GROUP_MAX_LAYERS], null arrays, n_aux outside
+ * [0, CSA2_GROUP_MAX_AUX], a null or repeated stream, too few or null
+ * events; every layer is validated as by csa2_layer_step before anything is
+ * enqueued, and the first failing layer's status is returned. */
+#define CSA2_GROUP_MAX_LAYERS 64
+#define CSA2_GROUP_MAX_AUX 4
+typedef struct {
+  hipStream_t aux[CSA2_GROUP_MAX_AUX];
+  int32_t     n_aux;
+  hipEvent_t* events;
+  int32_t     n_events;
+} csa2_group_exec;
+
+/* Events a csa2_group_step call needs: 1 + 3 n_layers + n_aux; -1 for
+ * arguments outside the limits above. */
+int32_t csa2_group_events(int32_t n_layers, int32_t n_aux);
+
+csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_args* layers, hipStream_t s,
+                            const csa2_group_exec* ex);
+
 /* Static description of a status code. */
 const char* csa2_status_string(csa2_status st);
 

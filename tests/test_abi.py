@@ -139,3 +139,33 @@ def test_set_timing_validation():
     r = L.TimingRing(None, None, 4, 0)
     assert lib.csa2_set_timing(1, ctypes.byref(r)) == L.CSA2_ERR_INVALID_ARG
     assert lib.csa2_set_timing(1, None) == L.CSA2_OK
+
+
+def test_group_step_validation():
+    lib = L.load()
+    assert lib.csa2_group_events(4, 2) == 15
+    assert lib.csa2_group_events(0, 0) == 1
+    assert lib.csa2_group_events(-1, 0) == -1
+    assert lib.csa2_group_events(L.GROUP_MAX_LAYERS + 1, 0) == -1
+    assert lib.csa2_group_events(1, L.GROUP_MAX_AUX + 1) == -1
+    modes = (ctypes.c_int32 * 1)(0)
+    args = (L.StepArgs * 1)()
+    assert lib.csa2_group_step(0, None, None, None, None) == L.CSA2_OK
+    assert lib.csa2_group_step(-1, modes, args, None, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_group_step(L.GROUP_MAX_LAYERS + 1, modes, args, None, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_group_step(1, None, args, None, None) == L.CSA2_ERR_INVALID_ARG
+    ex = L.GroupExec()
+    ex.n_aux = L.GROUP_MAX_AUX + 1
+    assert lib.csa2_group_step(1, modes, args, None, ctypes.byref(ex)) == L.CSA2_ERR_INVALID_ARG
+    ex.n_aux = 1
+    ex.aux[0] = 0x1234
+    ev = (ctypes.c_void_p * 6)(1, 2, 3, 4, 5, 6)
+    ex.events, ex.n_events = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), 4   # needs 5
+    assert lib.csa2_group_step(1, modes, args, None, ctypes.byref(ex)) == L.CSA2_ERR_INVALID_ARG
+    ex.aux[0] = 0                                                                 # null stream
+    ex.n_events = 5
+    assert lib.csa2_group_step(1, modes, args, None, ctypes.byref(ex)) == L.CSA2_ERR_INVALID_ARG
+    ex.n_aux, ex.aux[0], ex.aux[1], ex.n_events = 2, 0x1234, 0x1234, 6            # repeated stream
+    assert lib.csa2_group_step(1, modes, args, None, ctypes.byref(ex)) == L.CSA2_ERR_INVALID_ARG
+    # a layer that fails validation (no cache) is reported before anything is enqueued
+    assert lib.csa2_group_step(1, modes, args, None, None) == L.CSA2_ERR_INVALID_ARG

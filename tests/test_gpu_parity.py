@@ -190,6 +190,44 @@ def test_prefill_dense_bit_identical_to_scan(seed, cached, n_new, h_idx, page_si
             assert np.array_equal(x[key], y[key]), (li, key)
 
 
+def _group_vs_layers(spec, n_aux, dense=None, shared_ws=False, reps=2):
+    _, runner = _ops()
+    say(f"[group step] {spec.name} seed={spec.seed} modes={spec.modes} n_aux={n_aux} shared_ws={shared_ws}")
+    ref = runner.DeviceCase(spec, gen_device="cpu", dense=dense)
+    ref.run_group()
+    want = ref.results_host()
+    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense, group=n_aux, shared_ws=shared_ws)
+    for rep in range(reps):
+        dc.run_group()
+        got = dc.results_host()
+        for li, (x, y) in enumerate(zip(got, want)):
+            for key in ("idx", "cnt", "out", "lse"):
+                assert np.array_equal(x[key], y[key]), (rep, li, key)
+
+
+@pytest.mark.parametrize("n_aux", [1, 2, 3])
+def test_group_step_matches_layer_calls(n_aux):
+    """One csa2_group_step (selects and attentions on auxiliary streams)
+    gives exactly the results of the layers called one by one."""
+    spec = W.small_case("group_step", 61, [4096, 1500, 700, 3000], n_new=1, h_idx=8, h=64, k=512)
+    _group_vs_layers(spec, n_aux)
+
+
+def test_group_step_mixed_order_and_shared_workspace():
+    """Reuse before Reindex, and every layer on one workspace (the group then
+    orders the layers itself)."""
+    spec = W.small_case("group_mixed", 62, [2048, 900], n_new=1, h_idx=4, h=32, k=256,
+                        modes=(O.FULL, O.REUSE, O.REINDEX, O.REUSE), integer_indexer=True)
+    _group_vs_layers(spec, 2)
+    _group_vs_layers(spec, 2, shared_ws=True)
+
+
+def test_group_step_prefill_dense():
+    spec = W.small_case("group_prefill", 63, [3000], n_new=150, h_idx=8, h=16, k=256,
+                        modes=(O.FULL, O.REINDEX, O.REUSE), prefill=True)
+    _group_vs_layers(spec, 2, dense=True)
+
+
 @pytest.mark.parametrize("factor", [0, 1, 64])
 def test_prefill_dense_candidate_factor(factor):
     """Candidate factor 0 sends every query through the full rescore, 1 makes
