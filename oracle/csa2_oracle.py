@@ -32,6 +32,13 @@ What is computed, and where it comes from:
     index ascending), returned in ascending index order, padded with -1;
   - attention: softmax(sm_scale * q_h . X_t) over the selected rows, output
     sum_j p_j X_tj per head, plus the natural-log LSE.
+* The global (CSA2) branch sits beside a local sliding-window branch: "DeepSeek-
+  V4.1-Flash: Pushing the Limits of KV Cache Compression" (global attention
+  over the full context together with local sliding-window attention) and the
+  research-podcast summary (global context decoupled from local
+  sliding-window attention).  No combination formula is given; the reading
+  used is one softmax over the union of the two branches' keys, which the two
+  branches' (output, LSE) pairs give exactly (lse_merge).
 
 All arithmetic is float64.  Parity pins live in the tests (closed-form format
 tables, brute-force selection, a textbook dense attention, exact integer
@@ -308,6 +315,29 @@ def sparse_attn(cache: Cache, q, q_seq, idx, cnt, sm_scale: float):
     for i in range(nq):
         out[i], lse[i] = attend(cache, int(q_seq[i]), q[i], idx[i], int(cnt[i]), sm_scale)
     return out, lse
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Output and LSE of one softmax over the union of two disjoint key sets,
+    from each set's own softmax output O [..][d] and natural-log LSE [..]
+    (the global branch and the local sliding-window branch).  Exactly: with
+    Z = e^lse_a + e^lse_b, O = (e^lse_a O_a + e^lse_b O_b) / Z and LSE = ln Z.
+    A side with no keys has LSE = -inf and counts for nothing; both empty
+    gives O = 0 and LSE = -inf, the convention of attend()."""
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(la, lb)
+    empty = np.isneginf(m)
+    ms = np.where(empty, 0.0, m)
+    wa = np.where(np.isneginf(la), 0.0, np.exp(la - ms))
+    wb = np.where(np.isneginf(lb), 0.0, np.exp(lb - ms))
+    z = wa + wb
+    zs = np.where(empty, 1.0, z)
+    o = (wa[..., None] * o_a + wb[..., None] * o_b) / zs[..., None]
+    lse = np.where(empty, -np.inf, ms + np.log(zs))
+    return o, lse
 
 
 def layer_step(mode: int, cache: Cache, q, q_seq, q_vis, k: int, sm_scale: float,
