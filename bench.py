@@ -53,6 +53,38 @@ def attn_bytes(spec) -> int:
     return spec.nq * (spec.k * 272 + spec.k * 4 + spec.h * 512 * 2 + spec.h * 512 * 4 + spec.h * 4)
 
 
+def merge_bytes(rows: int, dim: int = 512) -> int:
+    """Algorithmic bytes of one branch merge: both branches' outputs and LSEs
+    in, the merged output and LSE out."""
+    return rows * (3 * dim * 4 + 3 * 4)
+
+
+def time_lse_merge(o_a, lse_a, reps: int = 20):
+    """Times csa2_lse_merge of the CSA2 output with a synthetic local-branch
+    output of the same shape (device timestamps of the merge's dispatches)."""
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    from fp4_kv_cache_layer_amd import _lib as L
+    g = torch.Generator(device="cuda").manual_seed(5)
+    o_b = torch.randn(o_a.shape, generator=g, device="cuda", dtype=torch.float32)
+    lse_b = torch.randn(lse_a.shape, generator=g, device="cuda", dtype=torch.float32) * 4
+    out, lse = torch.empty_like(o_a), torch.empty_like(lse_a)
+    for _ in range(3):
+        ops.csa2_lse_merge(o_a, lse_a, o_b, lse_b, out, lse)
+    ring = ops.TimingRing(L.KCLASS_MERGE, reps)
+    ring.install()
+    for _ in range(reps):
+        ops.csa2_lse_merge(o_a, lse_a, o_b, lse_b, out, lse)
+    ring.uninstall()
+    avg_s = statistics.mean(ring.durations_ms()) / 1e3
+    rows = lse_a.numel()
+    b = merge_bytes(rows, o_a.shape[-1])
+    return {"kernel": "lse_merge_kernel", "rows": rows, "dim": int(o_a.shape[-1]), "bytes": b,
+            "avg_us": round(avg_s * 1e6, 2), "GBps": round(b / avg_s / 1e9, 1),
+            "hbm_frac": round(b / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def scan_source_hash() -> str:
     """Hash of the indexer-scan kernel source: a stored counter reading
     applies only to the kernel it was taken on."""
@@ -250,6 +282,7 @@ def bench_prefill(args, spec, dc) -> int:
                            "indexer_product": avg(dur[L.KCLASS_DENSE]), "select": avg(dur[L.KCLASS_SELECT]),
                            "attn": avg(dur[L.KCLASS_ATTN])},
         "ms_per_step_no_events": round(ms_plain, 5),
+        "lse_merge": time_lse_merge(dc.outputs[0]["out"], dc.outputs[0]["lse"]),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -421,6 +454,7 @@ def main() -> int:
                             "ms_per_step_no_events": round(ms_other, 5),
                             "tokens_per_s": round(spec.num_seqs * spec.n_new / (ms_other / 1e3), 1)},
         "group_hbm_frac": None,
+        "lse_merge": time_lse_merge(dc.outputs[0]["out"], dc.outputs[0]["lse"]),
     }
     # whole-group algorithmic bytes: scans + gathered rows + Q + O + LSE + append
     attn_b = attn_bytes(spec)

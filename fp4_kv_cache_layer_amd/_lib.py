@@ -13,7 +13,7 @@ c_int32, c_void_p, c_float, c_size_t = ctypes.c_int32, ctypes.c_void_p, ctypes.c
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
-KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE = 0, 1, 2, 3, 4
+KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE, KCLASS_MERGE = 0, 1, 2, 3, 4, 5
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
 STEP_DENSE_INDEX = 1
 
@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.csa2_sparse_attn.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
+    lib.csa2_lse_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                   c_void_p]
     lib.csa2_group_events.argtypes = [c_int32, c_int32]
     lib.csa2_group_events.restype = c_int32
     lib.csa2_group_step.argtypes = [c_int32, P(c_int32), P(StepArgs), c_void_p, P(GroupExec)]
@@ -77,7 +79,8 @@ def load() -> ctypes.CDLL:
     lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_group_step", "csa2_set_timing", "csa2_set_prefill_candidate_factor"):
+               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_set_timing",
+               "csa2_set_prefill_candidate_factor"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

@@ -343,6 +343,19 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t
   return run_step(p, s);
 }
 
+csa2_status csa2_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                           int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s) {
+  if (rows < 0 || dim < 4 || dim % 4 != 0) return CSA2_ERR_INVALID_ARG;
+  if (rows == 0) return CSA2_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16) || !aligned(lse_a, 4) || !aligned(lse_b, 4) ||
+      (lse && !aligned(lse, 4)))
+    return CSA2_ERR_INVALID_ARG;
+  if (lse && (lse == lse_a || lse == lse_b)) return CSA2_ERR_INVALID_ARG;
+  TimedLaunch t(CSA2_KCLASS_MERGE);
+  return hip_status(launch_lse_merge(o_a, lse_a, o_b, lse_b, rows, dim, o, lse, s, t.ev));
+}
+
 int32_t csa2_group_events(int32_t n_layers, int32_t n_aux) {
   if (n_layers < 0 || n_layers > CSA2_GROUP_MAX_LAYERS || n_aux < 0 || n_aux > CSA2_GROUP_MAX_AUX) return -1;
   return 1 + 3 * n_layers + n_aux;

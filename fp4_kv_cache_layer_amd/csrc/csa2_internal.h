@@ -1,5 +1,6 @@
 // Internal launchers of the CSA2 kernels (not part of the C ABI).
 #pragma once
+#include <algorithm>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -102,5 +103,10 @@ size_t attn_part_bytes(int nq, int h, int k);
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
                               void* part, hipStream_t s, const KEvents& ev = {});
+
+// Branch merge: O and LSE of one softmax over the union of two key sets
+// ([rows][dim] fp32 outputs, [rows] LSEs; dim a multiple of 4).
+hipError_t launch_lse_merge(const float* oa, const float* la, const float* ob, const float* lb, int rows, int dim,
+                            float* o, float* lse, hipStream_t s, const KEvents& ev = {});
 
 }  // namespace csa2

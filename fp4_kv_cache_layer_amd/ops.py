@@ -185,6 +185,28 @@ def csa2_layer_step(mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tenso
               new_slots, new_kv, new_idxk, ws, dense)(stream)
 
 
+def csa2_lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Merge of two attention branches' (O, LSE) over disjoint key sets (see
+    csa2_lse_merge in include/csa2.h).  O tensors [..., dim] fp32, LSEs [...]
+    fp32; returns (out, lse), allocating them when not given."""
+    for t, n in ((o_a, "o_a"), (o_b, "o_b"), (lse_a, "lse_a"), (lse_b, "lse_b")):
+        _need(t, (torch.float32,), n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dim = o_a.shape[-1]
+    rows = o_a.numel() // dim if dim else 0
+    if o_b.shape != o_a.shape or lse_a.numel() != rows or lse_b.numel() != rows:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    L.check("csa2_lse_merge", L.load().csa2_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), rows, dim,
+                                                      _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
 class GroupCall:
     """Prepared csa2_group_step over LayerCalls: appends and indexer scans on
     the calling stream, selects and attentions on n_aux auxiliary streams

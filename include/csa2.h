@@ -266,6 +266,28 @@ int32_t csa2_group_events(int32_t n_layers, int32_t n_aux);
 csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_args* layers, hipStream_t s,
                             const csa2_group_exec* ex);
 
+/* Merge of the global (CSA2) branch with the local sliding-window branch of
+ * the same queries and heads: the output and LSE of one softmax over the
+ * union of the two branches' keys.  The pages place a global attention branch
+ * over the full context beside local sliding-window attention ("DeepSeek-
+ * V4.1-Flash: Pushing the Limits of KV Cache Compression"; the
+ * research-podcast summary: global context decoupled from local
+ * sliding-window attention) and give no combination formula; this is the
+ * plainest reading.  Per row r (e.g. r = query * h + head):
+ *   M = max(lse_a[r], lse_b[r]), w_x = e^(lse_x[r] - M),
+ *   o[r][:] = (w_a o_a[r][:] + w_b o_b[r][:]) / (w_a + w_b),
+ *   lse[r] = M + ln(w_a + w_b)   (natural log, like csa2_sparse_attn's LSE);
+ * a branch with lse = -inf has no keys and counts for nothing; both empty
+ * give o = 0, lse = -inf.
+ * Layout: o_a, o_b, o [rows][dim] fp32 (16-byte aligned, dim a multiple of 4,
+ * 4 <= dim), lse_a, lse_b, lse [rows] fp32 (lse nullable).  o may be o_a or
+ * o_b (in place); lse must not be lse_a or lse_b.  All device memory owned
+ * by the caller.  rows = 0 enqueues nothing.  Errors: CSA2_ERR_INVALID_ARG for
+ * rows < 0, a bad dim, null or misaligned pointers, or lse aliasing an input
+ * LSE; CSA2_ERR_HIP if the launch fails. */
+csa2_status csa2_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                           int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s);
+
 /* Static description of a status code. */
 const char* csa2_status_string(csa2_status st);
 
@@ -279,7 +301,7 @@ const char* csa2_status_string(csa2_status st);
  * installation.  Classes: 0 append, 1 indexer scan (for the dense indexer:
  * threshold, candidates, full rescore and compaction), 2 Top-K select,
  * 3 attention, 4 the dense indexer's matrix-product (candidate) kernel
- * alone.  Pass ring = NULL to uninstall.  Process-wide, not
+ * alone, 5 the branch merge.  Pass ring = NULL to uninstall.  Process-wide, not
  * thread-safe: meant for benchmarks. */
 typedef struct {
   hipEvent_t* start;     /* [capacity] */
@@ -293,7 +315,8 @@ typedef struct {
 #define CSA2_KCLASS_SELECT 2
 #define CSA2_KCLASS_ATTN   3
 #define CSA2_KCLASS_DENSE  4
-#define CSA2_NUM_KCLASSES  5
+#define CSA2_KCLASS_MERGE  5
+#define CSA2_NUM_KCLASSES  6
 csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
 
 #ifdef __cplusplus

@@ -169,3 +169,18 @@ def test_group_step_validation():
     assert lib.csa2_group_step(1, modes, args, None, ctypes.byref(ex)) == L.CSA2_ERR_INVALID_ARG
     # a layer that fails validation (no cache) is reported before anything is enqueued
     assert lib.csa2_group_step(1, modes, args, None, None) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_lse_merge_validation():
+    lib = L.load()
+    p, q, r = 4096, 8192, 12288           # fake, 16-byte aligned addresses: nothing is launched
+    assert lib.csa2_lse_merge(None, None, None, None, 0, 512, None, None, None) == L.CSA2_OK
+    assert lib.csa2_lse_merge(p, q, p, q, -1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG
+    for dim in (0, 2, 6, -4):
+        assert lib.csa2_lse_merge(p, q, p, q, 1, dim, p, r, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_lse_merge(None, q, p, q, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_lse_merge(p, q, p, q, 1, 512, None, r, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_lse_merge(p + 4, q, p, q, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG   # o_a misaligned
+    assert lib.csa2_lse_merge(p, q + 2, p, q, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG   # lse_a misaligned
+    assert lib.csa2_lse_merge(p, q, p, r, 1, 512, p, q, None) == L.CSA2_ERR_INVALID_ARG       # lse is lse_a
+    assert lib.csa2_lse_merge(p, q, p, r, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG       # lse is lse_b
