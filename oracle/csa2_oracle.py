@@ -32,6 +32,12 @@ What is computed, and where it comes from:
     index ascending), returned in ascending index order, padded with -1;
   - attention: softmax(sm_scale * q_h . X_t) over the selected rows, output
     sum_j p_j X_tj per head, plus the natural-log LSE.
+* FP4 for the global KV during training, by quantization-aware training:
+  "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression".  The
+  fake-quantization forward (fake_quant_e2m1) applies the cache's own E2M1 +
+  E8M0 rules to every 32-element block; the pages name no gradient rule, and
+  since the scale rule never clips (every |x| / 2^e <= 6) the plain
+  straight-through gradient (identity) is taken.
 * The global (CSA2) branch sits beside a local sliding-window branch: "DeepSeek-
   V4.1-Flash: Pushing the Limits of KV Cache Compression" (global attention
   over the full context together with local sliding-window attention) and the
@@ -172,6 +178,19 @@ def quantize_kv_rows(x) -> np.ndarray:
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     scales = (e + 127).astype(np.uint8)
     return np.concatenate([packed, scales], axis=1)
+
+
+def fake_quant_e2m1(x) -> np.ndarray:
+    """Quantise-dequantise of values [..., d] (d a multiple of 32) with the
+    main-KV rules: per 32-element block the scale 2^e of block_exponent, the
+    E2M1 code of x / 2^e, decoded back to E2M1(code) * 2^e (sign kept, so a
+    negative value that rounds to zero gives -0)."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % BLOCK == 0
+    b = x.reshape(-1, BLOCK)
+    e = block_exponent(np.abs(b).max(axis=1)).astype(np.float64)
+    codes = e2m1_encode(b / np.exp2(e)[:, None])
+    return (e2m1_decode(codes) * np.exp2(e)[:, None]).reshape(x.shape)
 
 
 def dequantize_kv_rows(b) -> np.ndarray:
