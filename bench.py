@@ -85,6 +85,28 @@ def time_lse_merge(o_a, lse_a, reps: int = 20):
             "hbm_frac": round(b / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def time_fake_quant(x, reps: int = 10):
+    """Times csa2_fake_quant_fp4 on x (device timestamps of its dispatches);
+    algorithmic bytes = x read once and its quantised copy written once."""
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    from fp4_kv_cache_layer_amd import _lib as L
+    out = torch.empty_like(x)
+    for _ in range(2):
+        ops.csa2_fake_quant_fp4(x, out)
+    ring = ops.TimingRing(L.KCLASS_QUANT, reps)
+    ring.install()
+    for _ in range(reps):
+        ops.csa2_fake_quant_fp4(x, out)
+    ring.uninstall()
+    avg_s = statistics.mean(ring.durations_ms()) / 1e3
+    b = 2 * x.numel() * x.element_size()
+    return {"kernel": "fake_quant_" + ("bf16" if x.element_size() == 2 else "f32") + "_kernel",
+            "values": x.numel(), "bytes": b, "avg_us": round(avg_s * 1e6, 2), "GBps": round(b / avg_s / 1e9, 1),
+            "hbm_frac": round(b / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def scan_source_hash() -> str:
     """Hash of the indexer-scan kernel source: a stored counter reading
     applies only to the kernel it was taken on."""
@@ -283,6 +305,9 @@ def bench_prefill(args, spec, dc) -> int:
                            "attn": avg(dur[L.KCLASS_ATTN])},
         "ms_per_step_no_events": round(ms_plain, 5),
         "lse_merge": time_lse_merge(dc.outputs[0]["out"], dc.outputs[0]["lse"]),
+        # the QAT forward on the chunk's attention output (fp32) and on its bf16 copy
+        "fake_quant_f32": time_fake_quant(dc.outputs[0]["out"]),
+        "fake_quant_bf16": time_fake_quant(dc.outputs[0]["out"].to(torch.bfloat16)),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

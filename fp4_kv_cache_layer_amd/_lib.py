@@ -13,7 +13,8 @@ c_int32, c_void_p, c_float, c_size_t = ctypes.c_int32, ctypes.c_void_p, ctypes.c
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
-KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE, KCLASS_MERGE = 0, 1, 2, 3, 4, 5
+KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE, KCLASS_MERGE, KCLASS_QUANT = 0, 1, 2, 3, 4, 5, 6
+DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
 STEP_DENSE_INDEX = 1
 
@@ -70,6 +71,7 @@ def load() -> ctypes.CDLL:
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
     lib.csa2_lse_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                    c_void_p]
+    lib.csa2_fake_quant_fp4.argtypes = [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_void_p]
     lib.csa2_group_events.argtypes = [c_int32, c_int32]
     lib.csa2_group_events.restype = c_int32
     lib.csa2_group_step.argtypes = [c_int32, P(c_int32), P(StepArgs), c_void_p, P(GroupExec)]
@@ -79,7 +81,7 @@ def load() -> ctypes.CDLL:
     lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_set_timing",
+               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4", "csa2_set_timing",
                "csa2_set_prefill_candidate_factor"):
         getattr(lib, fn).restype = c_int32
     _lib = lib

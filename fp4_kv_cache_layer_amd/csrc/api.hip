@@ -356,6 +356,14 @@ csa2_status csa2_lse_merge(const float* o_a, const float* lse_a, const float* o_
   return hip_status(launch_lse_merge(o_a, lse_a, o_b, lse_b, rows, dim, o, lse, s, t.ev));
 }
 
+csa2_status csa2_fake_quant_fp4(const void* x, void* y, int64_t n, int32_t dtype, hipStream_t s) {
+  if (n < 0 || n % 32 != 0 || (dtype != CSA2_DTYPE_F32 && dtype != CSA2_DTYPE_BF16)) return CSA2_ERR_INVALID_ARG;
+  if (n == 0) return CSA2_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return CSA2_ERR_INVALID_ARG;
+  TimedLaunch t(CSA2_KCLASS_QUANT);
+  return hip_status(launch_fake_quant(x, y, n, dtype == CSA2_DTYPE_BF16, s, t.ev));
+}
+
 int32_t csa2_group_events(int32_t n_layers, int32_t n_aux) {
   if (n_layers < 0 || n_layers > CSA2_GROUP_MAX_LAYERS || n_aux < 0 || n_aux > CSA2_GROUP_MAX_AUX) return -1;
   return 1 + 3 * n_layers + n_aux;

@@ -109,4 +109,7 @@ hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32
 hipError_t launch_lse_merge(const float* oa, const float* la, const float* ob, const float* lb, int rows, int dim,
                             float* o, float* lse, hipStream_t s, const KEvents& ev = {});
 
+// FP4 fake quantisation of n values (n a multiple of 32), fp32 or bf16.
+hipError_t launch_fake_quant(const void* x, void* y, int64_t n, bool bf16, hipStream_t s, const KEvents& ev = {});
+
 }  // namespace csa2

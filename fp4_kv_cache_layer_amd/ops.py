@@ -207,6 +207,39 @@ def csa2_lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, ls
     return out, lse
 
 
+def csa2_fake_quant_fp4(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """FP4 quantise-dequantise of x (fp32 or bf16, contiguous, numel a multiple
+    of 32, blocks of 32 consecutive values) with the main-KV rules (see
+    csa2_fake_quant_fp4 in include/csa2.h)."""
+    if x.dtype == torch.float32:
+        dt = L.DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        dt = L.DTYPE_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.numel() != x.numel():
+        raise ValueError("out must match x")
+    L.check("csa2_fake_quant_fp4", L.load().csa2_fake_quant_fp4(_ptr(x), _ptr(out), x.numel(), dt, _stream(stream)))
+    return out
+
+
+class FakeQuantFP4(torch.autograd.Function):
+    """Quantization-aware training op: forward csa2_fake_quant_fp4, backward
+    the straight-through gradient (identity; the scale rule never clips)."""
+
+    @staticmethod
+    def forward(ctx, x):
+        return csa2_fake_quant_fp4(x.contiguous())
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad
+
+
 class GroupCall:
     """Prepared csa2_group_step over LayerCalls: appends and indexer scans on
     the calling stream, selects and attentions on n_aux auxiliary streams

@@ -288,6 +288,24 @@ csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_a
 csa2_status csa2_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                            int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s);
 
+/* FP4 fake quantisation for quantization-aware training: the global KV is
+ * trained with FP4 ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ * Compression").  Every 32-element block of x (consecutive in memory) is
+ * encoded with exactly the main-KV rules of csa2_append_quant_fp4 (E8M0 scale
+ * 2^e, the smallest with amax <= 6 * 2^e; E2M1 codes, round to nearest, ties
+ * to the even code, sign kept) and decoded back: y = E2M1(code) * 2^e, in the
+ * dtype of x (the values are exact in fp32 and bf16).  Backward: the
+ * straight-through gradient is the identity, exact here because the scale
+ * rule never clips, so no backward entry point is needed.
+ * x, y: n values of dtype (CSA2_DTYPE_F32 or CSA2_DTYPE_BF16), device memory
+ * owned by the caller, 16-byte aligned; y may be x (in place).  n must be a
+ * non-negative multiple of 32; n = 0 enqueues nothing.  Errors:
+ * CSA2_ERR_INVALID_ARG for a bad n or dtype, null or misaligned pointers;
+ * CSA2_ERR_HIP if the launch fails. */
+#define CSA2_DTYPE_F32  0
+#define CSA2_DTYPE_BF16 1
+csa2_status csa2_fake_quant_fp4(const void* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
+
 /* Static description of a status code. */
 const char* csa2_status_string(csa2_status st);
 
@@ -301,7 +319,8 @@ const char* csa2_status_string(csa2_status st);
  * installation.  Classes: 0 append, 1 indexer scan (for the dense indexer:
  * threshold, candidates, full rescore and compaction), 2 Top-K select,
  * 3 attention, 4 the dense indexer's matrix-product (candidate) kernel
- * alone, 5 the branch merge.  Pass ring = NULL to uninstall.  Process-wide, not
+ * alone, 5 the branch merge, 6 the FP4 fake quantisation.  Pass ring = NULL
+ * to uninstall.  Process-wide, not
  * thread-safe: meant for benchmarks. */
 typedef struct {
   hipEvent_t* start;     /* [capacity] */
@@ -316,7 +335,8 @@ typedef struct {
 #define CSA2_KCLASS_ATTN   3
 #define CSA2_KCLASS_DENSE  4
 #define CSA2_KCLASS_MERGE  5
-#define CSA2_NUM_KCLASSES  6
+#define CSA2_KCLASS_QUANT  6
+#define CSA2_NUM_KCLASSES  7
 csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
 
 #ifdef __cplusplus

@@ -184,3 +184,14 @@ def test_lse_merge_validation():
     assert lib.csa2_lse_merge(p, q + 2, p, q, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG   # lse_a misaligned
     assert lib.csa2_lse_merge(p, q, p, r, 1, 512, p, q, None) == L.CSA2_ERR_INVALID_ARG       # lse is lse_a
     assert lib.csa2_lse_merge(p, q, p, r, 1, 512, p, r, None) == L.CSA2_ERR_INVALID_ARG       # lse is lse_b
+
+
+def test_fake_quant_validation():
+    lib = L.load()
+    p = 4096
+    assert lib.csa2_fake_quant_fp4(None, None, 0, L.DTYPE_F32, None) == L.CSA2_OK
+    for n in (-32, 16, 33):
+        assert lib.csa2_fake_quant_fp4(p, p, n, L.DTYPE_F32, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_fake_quant_fp4(p, p, 32, 2, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_fake_quant_fp4(None, p, 32, L.DTYPE_BF16, None) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_fake_quant_fp4(p + 8, p, 32, L.DTYPE_BF16, None) == L.CSA2_ERR_INVALID_ARG
