@@ -87,3 +87,49 @@ def test_config4_ragged_paged():
     lens = np.array(spec.cached)
     sample = sorted({int(lens.argmin()), int(lens.argmax()), int(np.argsort(lens)[len(lens) // 2])})
     _check_sampled(spec, sample=sample)
+
+
+def test_config1_group_step_equals_layer_calls():
+    """The benchmark's group step (Reuse attentions on an auxiliary stream)
+    against the per-layer calls on the full decode workload: identical bits."""
+    from fp4_kv_cache_layer_amd import runner
+    spec = W.config(1)
+    say(f"[fullsize] {spec.name}: group step vs layer calls")
+    dc = runner.DeviceCase(spec, gen_device="cuda", group=1)
+    dc.run_layers()
+    want = dc.results_host()
+    for rep in range(2):
+        dc.run_group()
+        got = dc.results_host()
+        for li, (x, y) in enumerate(zip(got, want)):
+            for key in ("idx", "cnt", "out", "lse"):
+                assert np.array_equal(x[key], y[key]), (rep, li, key)
+    del dc
+    torch.cuda.empty_cache()
+
+
+def test_prefill_sized_merge_and_fake_quant_sampled():
+    """Branch merge and FP4 fake quantisation at the benchmark's prefill size
+    (262,144 rows of 512), checked against the oracle on sampled rows."""
+    from fp4_kv_cache_layer_amd import ops
+    rows, dim = 4096 * 64, 512
+    g = torch.Generator(device="cuda").manual_seed(12)
+    oa = torch.randn(rows, dim, generator=g, device="cuda")
+    ob = torch.randn(rows, dim, generator=g, device="cuda") * 2
+    la = torch.randn(rows, generator=g, device="cuda") * 20
+    lb = torch.randn(rows, generator=g, device="cuda") * 20
+    say(f"[fullsize] merge and fake quant, {rows} rows of {dim}")
+    o, lse = ops.csa2_lse_merge(oa, la, ob, lb)
+    fq = ops.csa2_fake_quant_fp4(oa)
+    fqb = ops.csa2_fake_quant_fp4(ob.to(torch.bfloat16))
+    sample = torch.tensor([0, 1, 77, rows // 2, rows - 2, rows - 1], device="cuda")
+    sa, sb = oa[sample].cpu().numpy(), ob[sample].cpu().numpy()
+    ro, rl = O.lse_merge(sa, la[sample].cpu().numpy(), sb, lb[sample].cpu().numpy())
+    got_o = o[sample].cpu().numpy()
+    assert (np.abs(got_o - ro) <= 2e-6 * np.maximum(np.abs(sa), np.abs(sb)) + 1e-7).all()
+    assert np.allclose(lse[sample].cpu().numpy(), rl, rtol=2e-7, atol=2e-7)
+    want_fq = O.fake_quant_e2m1(sa.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(fq[sample].cpu().numpy().view(np.uint32), want_fq.view(np.uint32))
+    sbb = ob.to(torch.bfloat16)[sample].float().cpu().numpy()
+    want_fqb = O.fake_quant_e2m1(sbb.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(fqb[sample].float().cpu().numpy().view(np.uint32), want_fqb.view(np.uint32))
