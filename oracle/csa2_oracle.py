@@ -32,6 +32,12 @@ What is computed, and where it comes from:
     index ascending), returned in ascending index order, padded with -1;
   - attention: softmax(sm_scale * q_h . X_t) over the selected rows, output
     sum_j p_j X_tj per head, plus the natural-log LSE.
+* Hierarchical Sparse Indexer: later indexers are restricted to a shared
+  candidate pool chosen by an earlier indexer ("DeepSeek-V4.1-Flash: Pushing
+  the Limits of KV Cache Compression", Method).  The pool's size and the way it
+  is chosen are not given; the reading used: the earlier (Full) layer's own
+  Top-P under the same order (P >= k), and a later (Reindex) layer scores only
+  the pool's entries and keeps its Top-k among them (pool_index_topk).
 * FP4 for the global KV during training, by quantization-aware training:
   "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression".  The
   fake-quantization forward (fake_quant_e2m1) applies the cache's own E2M1 +
@@ -304,6 +310,29 @@ def index_topk(cache: Cache, q_idx, w, q_seq, q_vis, k: int):
     for i in range(nq):
         s = index_scores(cache, int(q_seq[i]), int(q_vis[i]), q_idx[i], w[i])
         idx[i], cnt[i] = select_topk(s, k)
+    return idx, cnt
+
+
+def pool_index_topk(cache: Cache, q_idx, w, q_seq, pool, pool_cnt, k: int):
+    """Hierarchical indexer: per query, the scores of the entries of its pool
+    only (pool [nq][P] entry indices, ascending, the first pool_cnt valid),
+    then the first min(k, pool_cnt) of them under (score descending, entry
+    index ascending), returned ascending by index and padded with -1."""
+    q_idx = np.asarray(q_idx, np.uint8)
+    w = np.asarray(w, np.float64)
+    pool = np.asarray(pool, np.int64)
+    nq = len(q_seq)
+    idx = np.full((nq, k), -1, dtype=np.int32)
+    cnt = np.zeros(nq, dtype=np.int32)
+    for i in range(nq):
+        t = pool[i, :int(pool_cnt[i])]
+        qi = e4m3fn_decode(q_idx[i]).reshape(-1, D_INDEX)
+        kt = e4m3fn_decode(cache.idxk_rows(int(q_seq[i]), t))                  # [n][128]
+        s = np.maximum(kt @ qi.T, 0.0) @ w[i] + 0.0                            # -0 -> +0
+        kp = min(k, t.size)
+        order = np.lexsort((t, -s))
+        idx[i, :kp] = np.sort(t[order[:kp]])
+        cnt[i] = kp
     return idx, cnt
 
 
