@@ -14,9 +14,10 @@ c_int32, c_void_p, c_float, c_size_t = ctypes.c_int32, ctypes.c_void_p, ctypes.c
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
 KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE, KCLASS_MERGE, KCLASS_QUANT = 0, 1, 2, 3, 4, 5, 6
+KCLASS_POOL_SCAN, KCLASS_POOL_SELECT = 7, 8
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
-STEP_DENSE_INDEX = 1
+STEP_DENSE_INDEX, STEP_POOL = 1, 2
 
 
 class CacheView(ctypes.Structure):
@@ -31,7 +32,8 @@ class StepArgs(ctypes.Structure):
                 ("q", c_void_p), ("h", c_int32), ("sm_scale", c_float),
                 ("q_seq", c_void_p), ("q_vis", c_void_p), ("nq", c_int32), ("k", c_int32), ("max_vis", c_int32),
                 ("idx", c_void_p), ("cnt", c_void_p), ("out", c_void_p), ("lse", c_void_p),
-                ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32)]
+                ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32),
+                ("pool", c_void_p), ("pool_cnt", c_void_p), ("pool_k", c_int32)]
 
 
 GROUP_MAX_LAYERS, GROUP_MAX_AUX = 64, 4
@@ -66,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.csa2_index_topk.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                     c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_prefill_index_topk.argtypes = lib.csa2_index_topk.argtypes
+    lib.csa2_pool_index_topk.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                         c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.csa2_pool_workspace_bytes.argtypes = [c_int32, c_int32]
+    lib.csa2_pool_workspace_bytes.restype = c_size_t
     lib.csa2_sparse_attn.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
@@ -80,7 +86,7 @@ def load() -> ctypes.CDLL:
     lib.csa2_set_timing.argtypes = [c_int32, P(TimingRing)]
     lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
-               "csa2_sparse_attn",
+               "csa2_pool_index_topk", "csa2_sparse_attn",
                "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4", "csa2_set_timing",
                "csa2_set_prefill_candidate_factor"):
         getattr(lib, fn).restype = c_int32

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
 SOURCES = ["api.hip", "append_quant.hip", "index_scan.hip", "prefill_scan.hip", "topk_select.hip", "sparse_attn.hip",
-           "lse_merge.hip", "fake_quant.hip"]
+           "lse_merge.hip", "fake_quant.hip", "pool_index.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

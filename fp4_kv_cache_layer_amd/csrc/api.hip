@@ -4,6 +4,7 @@
 #include "csa2.h"
 #include "csa2_internal.h"
 
+#include <algorithm>
 #include <cmath>
 
 using namespace csa2;
@@ -150,14 +151,35 @@ struct Step {
   const csa2_step_args* a;
   CacheArgs ca;
   bool dense;
+  bool pool;                 // hierarchical indexer (Full: writes the pool; Reindex: reads it)
   IndexWs iw;
+  float* pool_sc;            // pool scores, in the workspace's score region
   void* part;
 };
+
+csa2_status validate_pool(const int32_t* pool, const int32_t* pool_cnt, int32_t nq, int32_t p, int32_t k,
+                          const int32_t* out_idx, const int32_t* out_cnt) {
+  if (nq < 0 || p < 1 || p > CSA2_MAX_K || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_INVALID_ARG;
+  if (nq == 0) return CSA2_OK;
+  if (!pool || !pool_cnt || !out_idx || !out_cnt) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(pool, 16) || !aligned(pool_cnt, 4) || !aligned(out_idx, 4) || !aligned(out_cnt, 4))
+    return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
 
 // Every check of csa2_layer_step, before anything is launched.
 csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
   if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
-  if (a->flags & ~CSA2_STEP_DENSE_INDEX) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL)) return CSA2_ERR_INVALID_ARG;
+  const bool pool = (a->flags & CSA2_STEP_POOL) != 0;
+  if (pool) {
+    if (mode == CSA2_REUSE || a->pool_k < a->k) return CSA2_ERR_INVALID_ARG;
+    csa2_status st = validate_pool(a->pool, a->pool_cnt, a->nq, a->pool_k, a->k, a->idx, a->cnt);
+    if (st != CSA2_OK) return st;
+    if (a->nq > 0 && (a->pool == a->idx || a->pool_cnt == a->cnt)) return CSA2_ERR_INVALID_ARG;
+  } else if (a->pool || a->pool_cnt || a->pool_k != 0) {
+    return CSA2_ERR_INVALID_ARG;
+  }
   csa2_status st;
   if (mode == CSA2_FULL) {
     st = validate_append(a->cache, a->new_slots, a->new_kv, a->new_idxk, a->n_new, &p->ca);
@@ -166,8 +188,11 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
     return CSA2_ERR_INVALID_ARG;
   }
   if (mode != CSA2_REUSE) {
-    st = validate_index(a->cache, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis, a->idx,
-                        a->cnt, a->ws, a->ws_bytes, &p->ca);
+    // a Full pool layer's indexer writes its Top-pool_k into the pool
+    const bool to_pool = pool && mode == CSA2_FULL;
+    st = validate_index(a->cache, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, to_pool ? a->pool_k : a->k,
+                        a->max_vis, to_pool ? a->pool : a->idx, to_pool ? a->pool_cnt : a->cnt, a->ws, a->ws_bytes,
+                        &p->ca);
     if (st != CSA2_OK) return st;
   } else if (a->q_idx || a->w || a->h_idx != 0) {
     return CSA2_ERR_INVALID_ARG;
@@ -177,13 +202,18 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
   p->mode = mode;
   p->a = a;
   p->dense = (a->flags & CSA2_STEP_DENSE_INDEX) != 0;
+  p->pool = pool;
   p->iw = IndexWs{};
+  p->pool_sc = nullptr;
   p->part = nullptr;
   if (a->nq == 0) return CSA2_OK;
   const size_t z = zero_state_bytes(a->nq), part = attn_part_bytes(a->nq, a->h, a->k);
   if (mode != CSA2_REUSE) {
-    if (a->ws_bytes < z + part + index_score_bytes(a->nq, a->max_vis)) return CSA2_ERR_WORKSPACE;
+    // the pool scores reuse the exhaustive scores' region (dead once the pool is selected)
+    const size_t need = std::max(index_score_bytes(a->nq, a->max_vis), pool ? pool_score_bytes(a->nq, a->pool_k) : 0);
+    if (a->ws_bytes < z + part + need) return CSA2_ERR_WORKSPACE;
     p->iw = index_ws(a->ws, a->nq, a->max_vis, z + part);
+    if (pool) p->pool_sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a->ws) + z + part);
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;
   }
@@ -201,22 +231,43 @@ csa2_status stage_append(const Step& p, hipStream_t s) {
 csa2_status stage_scan(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (p.mode == CSA2_REUSE || a->nq == 0 || a->max_vis == 0) return CSA2_OK;
+  if (p.pool && p.mode == CSA2_REINDEX) return CSA2_OK;     // the pool is scored in stage_select
   if (p.dense) {
     TimedLaunch t(CSA2_KCLASS_SCAN), tp(CSA2_KCLASS_DENSE);
-    return hip_status(launch_prefill_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k,
-                                          a->max_vis, p.iw, s, t.ev, tp.ev));
+    return hip_status(launch_prefill_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx,
+                                          p.pool ? a->pool_k : a->k, a->max_vis, p.iw, s, t.ev, tp.ev));
   }
   TimedLaunch t(CSA2_KCLASS_SCAN);
   return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->max_vis, p.iw, s,
                                       t.ev));
 }
 
+csa2_status run_pool(const Step& p, hipStream_t s) {
+  const csa2_step_args* a = p.a;
+  TimedLaunch ts(CSA2_KCLASS_POOL_SCAN), tl(CSA2_KCLASS_POOL_SELECT);
+  return hip_status(launch_pool_index(p.ca, a->q_idx, a->w, a->q_seq, a->pool, a->pool_cnt, a->nq, a->h_idx,
+                                      a->pool_k, a->k, a->idx, a->cnt, p.pool_sc, s, ts.ev, tl.ev));
+}
+
+// Full and Reindex: Top-k of the scores.  With a pool, a Full layer selects
+// its Top-pool_k into the pool and then its Top-k among the pool (the same
+// set: the order is total), a Reindex layer scores and selects in the pool.
 csa2_status stage_select(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (p.mode == CSA2_REUSE || a->nq == 0) return CSA2_OK;
-  TimedLaunch t(CSA2_KCLASS_SELECT);
-  if (p.dense) return hip_status(launch_topk_final(p.iw, a->q_vis, a->nq, a->k, a->idx, a->cnt, s, t.ev));
-  return hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, a->k, a->max_vis, a->idx, a->cnt, s, t.ev));
+  if (p.pool && p.mode == CSA2_REINDEX) return run_pool(p, s);
+  const bool to_pool = p.pool;
+  int32_t* idx = to_pool ? a->pool : a->idx;
+  int32_t* cnt = to_pool ? a->pool_cnt : a->cnt;
+  const int32_t k = to_pool ? a->pool_k : a->k;
+  csa2_status st;
+  {
+    TimedLaunch t(CSA2_KCLASS_SELECT);
+    st = p.dense ? hip_status(launch_topk_final(p.iw, a->q_vis, a->nq, k, idx, cnt, s, t.ev))
+                 : hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, k, a->max_vis, idx, cnt, s, t.ev));
+  }
+  if (st != CSA2_OK || !to_pool) return st;
+  return run_pool(p, s);
 }
 
 csa2_status stage_attn(const Step& p, hipStream_t s) {
@@ -249,6 +300,16 @@ bool layers_conflict(const Step& i, const Step& j) {
     if (!(iw && !jw)) return true;
   }
   if (j.mode == CSA2_FULL && b->n_new > 0 && same(i.ca.kv, j.ca.kv)) return true;
+  // pool buffers: any overlap with the other layer's buffers, unless both only read them
+  auto touches = [&](const csa2_step_args* x, const void* ptr) {
+    return same(x->ws, ptr) || same(x->out, ptr) || same(x->lse, ptr) || same(x->idx, ptr) || same(x->cnt, ptr);
+  };
+  const bool iwp = i.pool && i.mode == CSA2_FULL, jwp = j.pool && j.mode == CSA2_FULL;
+  for (const void* ptr : {a->pool, a->pool_cnt})
+    if (i.pool && (touches(b, ptr) || (j.pool && (iwp || jwp) && (same(b->pool, ptr) || same(b->pool_cnt, ptr)))))
+      return true;
+  for (const void* ptr : {b->pool, b->pool_cnt})
+    if (j.pool && touches(a, ptr)) return true;
   return false;
 }
 
@@ -285,8 +346,13 @@ size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t
   (void)h_idx; (void)k;
   if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;
   size_t b = zero_state_bytes(nq) + attn_part_bytes(nq, h, k);
-  if (mode != CSA2_REUSE) b += index_score_bytes(nq, max_vis);
+  if (mode != CSA2_REUSE) b += std::max(index_score_bytes(nq, max_vis), pool_score_bytes(nq, CSA2_MAX_K));
   return b;
+}
+
+size_t csa2_pool_workspace_bytes(int32_t nq, int32_t p) {
+  if (nq <= 0 || p < 1 || p > CSA2_MAX_K) return 0;
+  return pool_score_bytes(nq, p);
 }
 
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, hipStream_t s) {
@@ -322,6 +388,24 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
                    index_ws(ws, nq, max_vis, zero_state_bytes(nq)), true, s);
+}
+
+csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,
+                                 const int32_t* q_seq, const int32_t* pool, const int32_t* pool_cnt, int32_t nq,
+                                 int32_t h_idx, int32_t p, int32_t k, int32_t* out_idx, int32_t* out_cnt, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
+  if (nq < 0 || h_idx < 1 || h_idx > CSA2_MAX_H_IDX) return CSA2_ERR_INVALID_ARG;
+  csa2_status st = validate_pool(pool, pool_cnt, nq, p, k, out_idx, out_cnt);
+  if (st != CSA2_OK) return st;
+  CacheArgs ca;
+  st = check_cache(c, &ca);
+  if (st != CSA2_OK || nq == 0) return st;
+  if (!q_idx || !w || !q_seq || !ws) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(q_seq, 4) || !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
+  if (ws_bytes < pool_score_bytes(nq, p)) return CSA2_ERR_WORKSPACE;
+  TimedLaunch ts(CSA2_KCLASS_POOL_SCAN), tl(CSA2_KCLASS_POOL_SELECT);
+  return hip_status(launch_pool_index(ca, q_idx, w, q_seq, pool, pool_cnt, nq, h_idx, p, k, out_idx, out_cnt,
+                                     reinterpret_cast<float*>(ws), s, ts.ev, tl.ev));
 }
 
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,

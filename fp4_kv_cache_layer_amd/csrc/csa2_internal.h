@@ -104,6 +104,15 @@ hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
                               void* part, hipStream_t s, const KEvents& ev = {});
 
+// Hierarchical indexer: scores of each query's pool entries only (pool
+// [nq][p] ascending entry indices, pool_cnt valid; scores [nq][round_up(p, 64)]
+// fp32 in sc), then its Top-k among them.
+size_t pool_score_bytes(int nq, int p);
+hipError_t launch_pool_index(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
+                             const int32_t* pool, const int32_t* pool_cnt, int nq, int h_idx, int p, int k,
+                             int32_t* out_idx, int32_t* out_cnt, float* sc, hipStream_t s,
+                             const KEvents& ev_scan = {}, const KEvents& ev_select = {});
+
 // Branch merge: O and LSE of one softmax over the union of two key sets
 // ([rows][dim] fp32 outputs, [rows] LSEs; dim a multiple of 4).
 hipError_t launch_lse_merge(const float* oa, const float* la, const float* ob, const float* lb, int rows, int dim,

@@ -120,6 +120,34 @@ def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: t
     return out_idx, out_cnt
 
 
+def csa2_pool_workspace(nq: int, p: int, device="cuda") -> torch.Tensor:
+    """Workspace for csa2_pool_index_topk (no initial state)."""
+    return torch.empty(int(L.load().csa2_pool_workspace_bytes(nq, p)), dtype=torch.uint8, device=device)
+
+
+def csa2_pool_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: torch.Tensor,
+                         pool: torch.Tensor, pool_cnt: torch.Tensor, k: int, ws: Optional[torch.Tensor] = None,
+                         out_idx: Optional[torch.Tensor] = None, out_cnt: Optional[torch.Tensor] = None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Hierarchical indexer: Top-k of each query among its pool [nq][P]."""
+    nq, h_idx = q_idx.shape[0], q_idx.shape[1]
+    _need(q_idx, (torch.uint8,), "q_idx")
+    _need(w, (torch.float32,), "w")
+    _need(pool, (torch.int32,), "pool")
+    _need(pool_cnt, (torch.int32,), "pool_cnt")
+    p = pool.shape[1]
+    if ws is None:
+        ws = csa2_pool_workspace(nq, p, device=q_idx.device)
+    if out_idx is None:
+        out_idx = torch.empty((nq, k), dtype=torch.int32, device=q_idx.device)
+    if out_cnt is None:
+        out_cnt = torch.empty(nq, dtype=torch.int32, device=q_idx.device)
+    L.check("csa2_pool_index_topk", L.load().csa2_pool_index_topk(
+        ctypes.byref(cache.view), _ptr(q_idx), _ptr(w), _ptr(q_seq), _ptr(pool), _ptr(pool_cnt), nq, h_idx, p, k,
+        _ptr(out_idx), _ptr(out_cnt), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_cnt
+
+
 def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: torch.Tensor, cnt: torch.Tensor,
                      sm_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      with_lse: bool = True, ws: Optional[torch.Tensor] = None,
@@ -151,10 +179,12 @@ class LayerCall:
                  q_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
                  new_slots: Optional[torch.Tensor] = None, new_kv: Optional[torch.Tensor] = None,
                  new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                 dense: bool = False):
+                 dense: bool = False, pool: Optional[torch.Tensor] = None, pool_cnt: Optional[torch.Tensor] = None):
+        """pool / pool_cnt ([nq][P], [nq] int32): hierarchical indexer; a Full
+        layer writes its Top-P there, a Reindex layer scores only those."""
         self.mode = mode
         self.cache = cache
-        self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws)
+        self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws, pool, pool_cnt)
         a = L.StepArgs()
         a.cache = ctypes.pointer(cache.view)
         if mode == FULL and new_slots is not None and new_slots.numel() > 0:
@@ -167,6 +197,9 @@ class LayerCall:
         a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = _ptr(q_seq), _ptr(q_vis), q.shape[0], k, max_vis
         a.idx, a.cnt, a.out, a.lse = _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse)
         a.flags = L.STEP_DENSE_INDEX if dense else 0
+        if pool is not None:
+            a.flags |= L.STEP_POOL
+            a.pool, a.pool_cnt, a.pool_k = _ptr(pool), _ptr(pool_cnt), pool.shape[1]
         self.args = a
         self._ref = ctypes.byref(a)
         self._fn = L.load().csa2_layer_step
@@ -180,9 +213,9 @@ class LayerCall:
 def csa2_layer_step(mode: int, cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, q_vis: torch.Tensor, k: int,
                     max_vis: int, sm_scale: float, idx: torch.Tensor, cnt: torch.Tensor, out: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, q_idx=None, w=None, new_slots=None, new_kv=None,
-                    new_idxk=None, ws=None, stream=None, dense: bool = False) -> None:
+                    new_idxk=None, ws=None, stream=None, dense: bool = False, pool=None, pool_cnt=None) -> None:
     LayerCall(mode, cache, q, q_seq, q_vis, k, max_vis, sm_scale, idx, cnt, out, lse, q_idx, w,
-              new_slots, new_kv, new_idxk, ws, dense)(stream)
+              new_slots, new_kv, new_idxk, ws, dense, pool, pool_cnt)(stream)
 
 
 def csa2_lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,

@@ -82,6 +82,11 @@ class DeviceCase:
         self.calls: List[ops.LayerCall] = []
         group_calls: List[ops.LayerCall] = []
         full_idx = full_cnt = None
+        # hierarchical indexer: the Full layer's Top-pool_k, scored again by the Reindex layers
+        self.pool = self.pool_cnt = None
+        if spec.pool_k:
+            self.pool = torch.empty((nq, spec.pool_k), dtype=torch.int32, device=dev)
+            self.pool_cnt = torch.empty(nq, dtype=torch.int32, device=dev)
         for li, mode in enumerate(spec.modes):
             qi, w, q = W.layer_queries(spec, li, self.gen_device)
             qi, w, q = qi.to(dev).contiguous(), w.to(dev).contiguous(), q.to(dev).contiguous()
@@ -103,9 +108,11 @@ class DeviceCase:
                 if mode == ops.FULL:
                     return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
                                          idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
-                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=ws, dense=self.dense)
+                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=ws, dense=self.dense,
+                                         pool=self.pool, pool_cnt=self.pool_cnt)
                 return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                     idx, cnt, out, lse, q_idx=qi, w=w, ws=ws, dense=self.dense)
+                                     idx, cnt, out, lse, q_idx=qi, w=w, ws=ws, dense=self.dense,
+                                     pool=self.pool, pool_cnt=self.pool_cnt)
             call = make(self.ws)
             if self.group_ws is not None:
                 group_calls.append(make(self.group_ws[li]))

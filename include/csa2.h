@@ -119,7 +119,9 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
  * first; then, for batches small enough that the attention splits each
  * query's rows across workgroups, the attention shares; then (Full and
  * Reindex) per-query scores [nq][round_up(max_vis, 64)] fp32 and candidate
- * indices of the same shape.  csa2_index_topk and csa2_sparse_attn accept a
+ * indices of the same shape, that region being at least nq * 8 KB so a
+ * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk and
+ * csa2_sparse_attn accept a
  * workspace sized by this call for the same shape.  The histogram part carries state:
  * every call leaves it zeroed for the next one, so zero the whole workspace
  * once after allocating it (csa2_workspace_init does this).  Calls that
@@ -208,11 +210,46 @@ typedef struct {
   void*           ws;
   size_t          ws_bytes;
   uint32_t        flags;         /* CSA2_STEP_* bits, 0 by default            */
+  int32_t*        pool;          /* CSA2_STEP_POOL: [nq][pool_k] candidate pool
+                                    (Full: written; Reindex: read)           */
+  int32_t*        pool_cnt;      /* [nq]                                      */
+  int32_t         pool_k;        /* pool width P, k <= P <= CSA2_MAX_K        */
 } csa2_step_args;
 
 /* Full/Reindex: score as csa2_prefill_index_topk (all queries of the call
  * belong to the sequence q_seq[0], e.g. one prefill chunk). */
 #define CSA2_STEP_DENSE_INDEX 1u
+/* Hierarchical indexer (see csa2_pool_index_topk).  Full: the indexer keeps
+ * its Top-pool_k as the pool (written to pool/pool_cnt, ascending) and the
+ * layer's Top-k is then taken among the pool, which equals its plain Top-k.
+ * Reindex: only the entries of pool (an earlier Full layer's) are scored.
+ * Reuse: not allowed. */
+#define CSA2_STEP_POOL 2u
+
+/* Hierarchical indexer: the indexer of a later (Reindex) layer scores only
+ * the shared candidate pool an earlier indexer chose, and keeps its Top-k
+ * among it ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ * Compression", Method: the Hierarchical Sparse Indexer restricts the
+ * indexers to a shared candidate pool selected by an earlier indexer).  The
+ * pages do not say how large the pool is or how it is chosen; the reading
+ * here: the earlier layer's own Top-P (csa2_index_topk with k = P), so pool
+ * rows are ascending entry indices.  Per query: s_t as in csa2_index_topk for
+ * the pool's first pool_cnt entries t only (bit-identical to the exhaustive
+ * scan's s_t), then the first min(k, pool_cnt) of them under (score
+ * descending, index ascending), written ascending to out_idx [nq][k], -1
+ * padded; out_cnt [nq].
+ *   pool [nq][p] int32 (first pool_cnt[q] valid, ascending, each < the
+ *   sequence's visible length), 1 <= p <= CSA2_MAX_K, 1 <= k <= CSA2_MAX_K;
+ *   other arguments as csa2_index_topk.  ws: at least
+ *   csa2_pool_workspace_bytes(nq, p) bytes, 16-byte aligned, no initial state.
+ * Errors: CSA2_ERR_INVALID_ARG for bad sizes or null/misaligned pointers,
+ * CSA2_ERR_WORKSPACE for a short workspace, CSA2_ERR_HIP on launch failure;
+ * nq = 0 enqueues nothing.  Pool values are trusted device data. */
+csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,
+                                 const int32_t* q_seq, const int32_t* pool, const int32_t* pool_cnt,
+                                 int32_t nq, int32_t h_idx, int32_t p, int32_t k,
+                                 int32_t* out_idx, int32_t* out_cnt, void* ws, size_t ws_bytes, hipStream_t s);
+size_t csa2_pool_workspace_bytes(int32_t nq, int32_t p);
 
 /* One CSA2 layer in the given mode:
  *   Full    = append (if n_new > 0) -> index_topk -> sparse_attn
@@ -336,7 +373,9 @@ typedef struct {
 #define CSA2_KCLASS_DENSE  4
 #define CSA2_KCLASS_MERGE  5
 #define CSA2_KCLASS_QUANT  6
-#define CSA2_NUM_KCLASSES  7
+#define CSA2_KCLASS_POOL_SCAN   7   /* hierarchical indexer: pool scoring */
+#define CSA2_KCLASS_POOL_SELECT 8   /* hierarchical indexer: Top-k of the pool */
+#define CSA2_NUM_KCLASSES  9
 csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
 
 #ifdef __cplusplus

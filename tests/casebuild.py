@@ -73,12 +73,15 @@ def build(spec: W.CaseSpec, device="cpu") -> OracleCase:
 
 def run_group(case: OracleCase) -> List[Dict[str, np.ndarray]]:
     """The workload's layer group through the oracle.  Reindex and Reuse layers
-    read the preceding Full layer's cache; Reuse reads that layer's indices."""
+    read the preceding Full layer's cache; Reuse reads that layer's indices.
+    With spec.pool_k, the Full layer's Top-pool_k is the pool (returned with
+    its results) and Reindex layers select among it."""
     spec = case.spec
     q_seq, q_vis = spec.q_seq(), spec.q_vis()
     results = []
     cache = None
     full_idx = full_cnt = None
+    pool = pool_cnt = None
     for L in case.layers:
         if L.mode == O.FULL:
             cache = case.fresh_cache()
@@ -86,6 +89,13 @@ def run_group(case: OracleCase) -> List[Dict[str, np.ndarray]]:
                                             q_idx=L.q_idx, w=L.w, new_slots=case.new_slots,
                                             new_kv=case.new_kv, new_idxk=case.new_ik)
             full_idx, full_cnt = idx, cnt
+            if spec.pool_k:
+                pool, pool_cnt = O.index_topk(cache, L.q_idx, L.w, q_seq, q_vis, spec.pool_k)
+                results.append(dict(idx=idx, cnt=cnt, out=o, lse=lse, pool=pool, pool_cnt=pool_cnt))
+                continue
+        elif L.mode == O.REINDEX and spec.pool_k:
+            idx, cnt = O.pool_index_topk(cache, L.q_idx, L.w, q_seq, pool, pool_cnt, spec.k)
+            o, lse = O.sparse_attn(cache, L.q, q_seq, idx, cnt, spec.sm_scale)
         elif L.mode == O.REINDEX:
             idx, cnt, o, lse = O.layer_step(O.REINDEX, cache, L.q, q_seq, q_vis, spec.k, spec.sm_scale,
                                             q_idx=L.q_idx, w=L.w)

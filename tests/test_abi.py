@@ -118,7 +118,7 @@ def test_layer_step_mode_field_rules():
     assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG   # Full needs q_idx/w/ws
     a.nq = 0
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK              # nothing to do
-    a.flags = 2                                          # unknown flag bit
+    a.flags = 4                                          # unknown flag bit
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
     a.flags = L.STEP_DENSE_INDEX
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
@@ -195,3 +195,63 @@ def test_fake_quant_validation():
     assert lib.csa2_fake_quant_fp4(p, p, 32, 2, None) == L.CSA2_ERR_INVALID_ARG
     assert lib.csa2_fake_quant_fp4(None, p, 32, L.DTYPE_BF16, None) == L.CSA2_ERR_INVALID_ARG
     assert lib.csa2_fake_quant_fp4(p + 8, p, 32, L.DTYPE_BF16, None) == L.CSA2_ERR_INVALID_ARG
+
+
+def _pool(lib, view, **kw):
+    a = dict(q_idx=FAKE, w=FAKE, q_seq=FAKE, pool=FAKE, pool_cnt=FAKE, nq=1, h_idx=8, p=2048, k=512,
+             out_idx=FAKE, out_cnt=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.csa2_pool_index_topk(ctypes.byref(view), a["q_idx"], a["w"], a["q_seq"], a["pool"], a["pool_cnt"],
+                                    a["nq"], a["h_idx"], a["p"], a["k"], a["out_idx"], a["out_cnt"], a["ws"],
+                                    a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(h_idx=0), dict(h_idx=17), dict(p=0), dict(p=2049), dict(k=0), dict(k=2049),
+                                dict(nq=-1), dict(pool=None), dict(pool_cnt=None), dict(pool=FAKE + 4),
+                                dict(q_idx=None), dict(w=None), dict(ws=None), dict(out_idx=None),
+                                dict(q_idx=FAKE + 8), dict(ws=FAKE + 4)])
+def test_pool_index_rejects(kw):
+    assert _pool(L.load(), _view(), **kw) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_pool_index_workspace_and_empty():
+    lib = L.load()
+    assert lib.csa2_pool_workspace_bytes(32, 2048) == 32 * 2048 * 4
+    assert lib.csa2_pool_workspace_bytes(3, 100) == 3 * 128 * 4          # rows padded to 64 scores
+    assert lib.csa2_pool_workspace_bytes(0, 100) == 0
+    assert lib.csa2_pool_workspace_bytes(4, 2049) == 0
+    assert _pool(lib, _view(), ws_bytes=2048 * 4 - 4) == L.CSA2_ERR_WORKSPACE
+    assert _pool(lib, _view(), nq=0, q_idx=None, ws=None) == L.CSA2_OK
+    # Full / Reindex workspaces leave room to score a pool of any width
+    assert lib.csa2_workspace_bytes(L.CSA2_FULL, 8, 10, 8, 64, 64) >= lib.csa2_pool_workspace_bytes(8, 2048)
+
+
+def test_layer_step_pool_field_rules():
+    lib = L.load()
+    v = _view()
+    a = L.StepArgs()
+    a.cache = ctypes.pointer(v)
+    a.q, a.h, a.sm_scale, a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = FAKE, 64, 0.04, FAKE, FAKE, 0, 512, 100
+    a.idx, a.cnt, a.out = FAKE, FAKE, FAKE
+    a.q_idx, a.w, a.h_idx, a.ws, a.ws_bytes = FAKE, FAKE, 8, FAKE, 1 << 30
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_OK       # nq = 0: nothing to do
+    a.pool = FAKE                                        # pool fields without the flag
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.pool, a.pool_k = None, 1024
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.flags, a.pool, a.pool_cnt = L.STEP_POOL, FAKE + 4096, FAKE + 8192
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_OK
+    assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_OK
+    a.pool_k = 256                                       # pool narrower than k
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.pool_k = 2049
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.pool_k, a.nq = 1024, 1
+    a.pool = FAKE + 4                                    # misaligned pool
+    assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.pool = FAKE                                        # the pool is the layer's own output
+    assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.pool, a.pool_cnt = FAKE + 4096, None
+    assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.q_idx, a.w, a.h_idx, a.pool_cnt = None, None, 0, FAKE + 8192          # Reuse: no pool
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG

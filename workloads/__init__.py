@@ -75,6 +75,7 @@ class CaseSpec:
     shuffle_pages: bool = False
     prefill: bool = False           # queries are the n_new appended rows (causal), else one query per sequence
     extra_pages: int = 0            # unused pages in the pool (exercise page ids beyond the used range)
+    pool_k: int = 0                 # > 0: hierarchical indexer, the Full layer's Top-pool_k is the Reindex pool
 
     @property
     def num_seqs(self) -> int:
@@ -227,8 +228,8 @@ def config(i: int, integer_indexer: Optional[bool] = None) -> CaseSpec:
 def small_case(name: str, seed: int, cached: List[int], n_new: int = 1, h_idx: int = 8, h: int = 16,
                k: int = 512, modes=(FULL, REINDEX, REUSE, REUSE), integer_indexer: bool = False,
                page_size: int = 64, shuffle_pages: bool = True, prefill: bool = False,
-               extra_pages: int = 3) -> CaseSpec:
+               extra_pages: int = 3, pool_k: int = 0) -> CaseSpec:
     """A reduced workload for oracle-checked parity: same structure, small sizes."""
     return CaseSpec(name, seed, list(cached), n_new, h_idx, h, k=k, modes=tuple(modes),
                     integer_indexer=integer_indexer, page_size=page_size,
-                    shuffle_pages=shuffle_pages, prefill=prefill, extra_pages=extra_pages)
+                    shuffle_pages=shuffle_pages, prefill=prefill, extra_pages=extra_pages, pool_k=pool_k)
