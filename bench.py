@@ -107,6 +107,71 @@ def time_fake_quant(x, reps: int = 10):
             "hbm_frac": round(b / avg_s / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def pool_scan_bytes(nq: int, pool_k: int, h_idx: int) -> int:
+    """Algorithmic bytes of one pool-scoring launch: each query's pool indices
+    (4 B) and gathered indexer-K rows (128 B), its indexer query and weights,
+    and the pool scores written (4 B each)."""
+    return nq * (pool_k * (4 + 128 + 4) + h_idx * (128 + 4))
+
+
+def time_hierarchical(dc, pool_k: int, steps: int):
+    """The decode group with the hierarchical indexer: the Full layer keeps its
+    Top-pool_k as the pool and the Reindex layer scores only the pool
+    (per-layer calls, device timestamps on the pool kernels).  Also reports
+    how much of each Reindex layer's exhaustive Top-k the pooled one keeps."""
+    import numpy as np
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    from fp4_kv_cache_layer_amd import _lib as L
+    spec = dc.spec
+    reindex = [li for li, m in enumerate(spec.modes) if m == ops.REINDEX]
+    dc.run_layers()
+    torch.cuda.synchronize()
+    exhaustive = {li: (dc.outputs[li]["idx"].cpu().numpy(), dc.outputs[li]["cnt"].cpu().numpy()) for li in reindex}
+    pool, pool_cnt = dc.new_pool(pool_k)
+    calls = [dc.make_call(li, dc.ws, pool, pool_cnt) for li in range(len(spec.modes))]
+
+    def step():
+        for c in calls:
+            c()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    n_pool = len(reindex) + 1
+    rings = {c: ops.TimingRing(c, steps * n_pool) for c in (L.KCLASS_POOL_SCAN, L.KCLASS_POOL_SELECT)}
+    rings[L.KCLASS_SCAN] = ops.TimingRing(L.KCLASS_SCAN, steps)
+    for r in rings.values():
+        r.install()
+    for _ in range(steps):
+        step()
+    for r in rings.values():
+        r.uninstall()
+    dur = {c: r.durations_ms() for c, r in rings.items()}
+    kept = []
+    for li in reindex:
+        ei, ec = exhaustive[li]
+        gi, gc = dc.outputs[li]["idx"].cpu().numpy(), dc.outputs[li]["cnt"].cpu().numpy()
+        inter = sum(len(set(a[:x].tolist()) & set(b[:y].tolist())) for a, x, b, y in zip(ei, ec, gi, gc))
+        kept.append(round(inter / max(1, int(ec.sum())), 4))
+    scan_us = statistics.mean(dur[L.KCLASS_POOL_SCAN]) * 1e3
+    pb = pool_scan_bytes(spec.nq, pool_k, spec.h_idx)
+    return {"pool_k": pool_k, "execution": "one csa2_layer_step call per layer",
+            "ms_per_step_no_events": round(ms, 5),
+            "tokens_per_s": round(spec.num_seqs * spec.n_new / (ms / 1e3), 1),
+            "kernels_avg_us": {"scan_full": round(statistics.mean(dur[L.KCLASS_SCAN]) * 1e3, 2),
+                               "pool_scan": round(scan_us, 2),
+                               "pool_select": round(statistics.mean(dur[L.KCLASS_POOL_SELECT]) * 1e3, 2)},
+            "pool_scan_bytes_per_launch": pb, "pool_scan_GBps": round(pb / (scan_us / 1e6) / 1e9, 1),
+            "reindex_topk_kept_vs_exhaustive": kept,
+            "entries_scored_per_query": {"exhaustive": int(spec.q_vis().max()), "pool": pool_k}}
+
+
 def scan_source_hash() -> str:
     """Hash of the indexer-scan kernel source: a stored counter reading
     applies only to the kernel it was taken on."""
@@ -331,6 +396,8 @@ def main() -> int:
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "scan_traffic.json"),
                     help="HBM traffic per scan launch measured with rocprofv3 counters (optional)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pool-k", type=int, default=2048,
+                    help="pool width of the hierarchical-indexer variant timed beside the headline (0: skip)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
@@ -480,6 +547,8 @@ def main() -> int:
                             "tokens_per_s": round(spec.num_seqs * spec.n_new / (ms_other / 1e3), 1)},
         "group_hbm_frac": None,
         "lse_merge": time_lse_merge(dc.outputs[0]["out"], dc.outputs[0]["lse"]),
+        "hierarchical_indexer": (time_hierarchical(dc, args.pool_k, args.steps)
+                                 if args.pool_k and ops.REINDEX in spec.modes else None),
     }
     # whole-group algorithmic bytes: scans + gathered rows + Q + O + LSE + append
     attn_b = attn_bytes(spec)

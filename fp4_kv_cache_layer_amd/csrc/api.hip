@@ -251,7 +251,8 @@ csa2_status run_pool(const Step& p, hipStream_t s) {
 
 // Full and Reindex: Top-k of the scores.  With a pool, a Full layer selects
 // its Top-pool_k into the pool and then its Top-k among the pool (the same
-// set: the order is total), a Reindex layer scores and selects in the pool.
+// set: the order is total) from the scores it already has, a Reindex layer
+// scores and selects in the pool.
 csa2_status stage_select(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (p.mode == CSA2_REUSE || a->nq == 0) return CSA2_OK;
@@ -267,7 +268,10 @@ csa2_status stage_select(const Step& p, hipStream_t s) {
                  : hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, k, a->max_vis, idx, cnt, s, t.ev));
   }
   if (st != CSA2_OK || !to_pool) return st;
-  return run_pool(p, s);
+  if (p.dense) return run_pool(p, s);         // the dense indexer keeps candidate scores only: rescore the pool
+  TimedLaunch t(CSA2_KCLASS_POOL_SELECT);     // every visible entry's score is in the workspace
+  return hip_status(launch_pool_select_by_entry(a->pool, a->pool_cnt, a->nq, a->pool_k, p.iw.scores, p.iw.vstride,
+                                                a->k, a->idx, a->cnt, s, t.ev));
 }
 
 csa2_status stage_attn(const Step& p, hipStream_t s) {

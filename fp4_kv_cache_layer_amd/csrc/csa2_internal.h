@@ -112,6 +112,11 @@ hipError_t launch_pool_index(const CacheArgs& c, const uint8_t* q_idx, const flo
                              const int32_t* pool, const int32_t* pool_cnt, int nq, int h_idx, int p, int k,
                              int32_t* out_idx, int32_t* out_cnt, float* sc, hipStream_t s,
                              const KEvents& ev_scan = {}, const KEvents& ev_select = {});
+// Top-k of each query's pool from an exhaustive scan's score rows (score of
+// entry t at scores[q * vstride + t]): no rescoring.
+hipError_t launch_pool_select_by_entry(const int32_t* pool, const int32_t* pool_cnt, int nq, int p,
+                                       const float* scores, int64_t vstride, int k, int32_t* out_idx,
+                                       int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 
 // Branch merge: O and LSE of one softmax over the union of two key sets
 // ([rows][dim] fp32 outputs, [rows] LSEs; dim a multiple of 4).

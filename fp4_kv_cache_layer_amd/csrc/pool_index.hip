@@ -11,10 +11,12 @@
 // operand (same layout, same product, same ReLU * w reduction as the scan), so
 // a pool entry's score has the bits the exhaustive scan gives it.
 //
-// pool_select_kernel: one workgroup per query; the pool's (score, position)
-// keys are sorted in LDS (bitonic, at most 2,048 keys), the first k positions
-// are flagged, and the flagged pool entries are written in pool order, which
-// is ascending entry order.
+// pool_select_kernel: one workgroup per query, eight pool positions per
+// thread.  A most-significant-digit-first radix search over the 32-bit score
+// keys (four 8-bit digits, histograms in LDS) finds the k-th largest key T
+// and how many entries tied at T still fit; the entries above T and the
+// first of those tied at T in pool order are selected, and a block-wide
+// prefix count writes them in pool order, which is ascending entry order.
 #include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_internal.h"
@@ -22,8 +24,9 @@
 namespace csa2 {
 
 constexpr int kPoolWaves = 4;
-constexpr int kPoolChunk = 256;               // pool entries per scan workgroup
-constexpr int kPoolSelectThreads = 1024;
+constexpr int kPoolChunk = 16 * kPoolWaves;   // pool entries per scan workgroup: one tile per wave
+constexpr int kPoolSelThreads = 256;
+constexpr int kPoolPer = CSA2_MAX_K / kPoolSelThreads;   // pool positions per select thread
 
 __global__ void __launch_bounds__(kPoolWaves * 64)
 pool_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -34,100 +37,141 @@ pool_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __
   const int q = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - q * nchunks;
   const int n = min(pool_cnt[q], p);
-  const int e0 = chunk * kPoolChunk;
-  if (e0 >= n) return;                                   // uniform
-  const int e1 = min(n, e0 + kPoolChunk);
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = chunk * kPoolChunk + 16 * wave;          // this wave's tile
+  if (e0 >= n) return;                                     // uniform per wave; no workgroup barrier follows
+  const int e1 = min(n, e0 + 16);
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
+  // the tile's rows first (pool index -> page -> row: three dependent loads)
+  const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
+  const int t_max = (c.max_pages << c.lg_page) - 1;       // keeps a bad pool entry inside the page table
+  const int t = pool[(int64_t)q * p + min(e0 + (lane >> 2), e1 - 1)];
+  const int64_t row = entry_row(pt_row, min(max(t, 0), t_max), c.lg_page);
+  const uint8_t* src = c.idx_k + row * kIndexDim + 32 * (lane & 3);
+  const intx4 lo = *reinterpret_cast<const intx4*>(src);
+  const intx4 hi = *reinterpret_cast<const intx4*>(src + 16);
   intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
   if (r < h_idx) a = load_fp8_operand(q_idx + ((int64_t)q * h_idx + r) * kIndexDim, g);
   float wv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < h_idx) ? w[(int64_t)q * h_idx + 4 * g + i] : 0.0f;
-  const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
-  const int32_t* prow = pool + (int64_t)q * p;
-  const int t_max = (c.max_pages << c.lg_page) - 1;     // keeps a bad pool entry inside the page table
-  float* srow = sc + (int64_t)q * pstride;
-  uint8_t* const slot = stage[wave];
-  const int ntiles = (e1 - e0 + 15) >> 4;
-  // tiles j = wave, wave + 4, ...: gather lane l's 32 bytes of entry l / 4
-  auto load = [&](int j, intx8& lin) {
-    const int pos = min(e0 + 16 * j + (lane >> 2), e1 - 1);
-    const int64_t row = entry_row(pt_row, min(max(prow[pos], 0), t_max), c.lg_page);
-    const uint8_t* src = c.idx_k + row * kIndexDim + 32 * (lane & 3);
-    const intx4 lo = *reinterpret_cast<const intx4*>(src);
-    const intx4 hi = *reinterpret_cast<const intx4*>(src + 16);
-    lin = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  intx8 cur, nxt;
-  load(wave, cur);
-  for (int j = wave; j < ntiles; j += kPoolWaves) {
-    load(min(j + kPoolWaves, ntiles - 1), nxt);
-    const intx8 b = fp8_tile_operand(slot, cur, lane);
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
-    const float part = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));   // every lane: entry r's score
-    uint32_t u32 = __float_as_uint(part);
-    if ((u32 << 1) == 0) u32 = 0;                         // -0 -> +0
-    const int pos = min(e0 + 16 * j + r, pstride - 1);    // positions past the count are never read
-    srow[pos] = __uint_as_float(u32);
-    cur = nxt;
-  }
+  // gathered rows take the scan's operand path, so every score has its bits
+  const intx8 b = fp8_tile_operand(stage[wave], intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, lane);
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+  const float part = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));   // every lane: entry r's score
+  uint32_t u32 = __float_as_uint(part);
+  if ((u32 << 1) == 0) u32 = 0;                           // -0 -> +0
+  if (g == 0 && e0 + r < e1) sc[(int64_t)q * pstride + e0 + r] = __uint_as_float(u32);
 }
 
-// Top-k of one query's pool.  Keys (score key << 32) | ~position order as
-// (score descending, position ascending) = (score descending, entry index
-// ascending), the pool being ascending; padding keys are 0 (below every key).
-__global__ void __launch_bounds__(kPoolSelectThreads)
-pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_cnt, int p, const float* sc,
-                   int pstride, int k, int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
-  __shared__ uint64_t key[CSA2_MAX_K];
-  __shared__ uint8_t flag[CSA2_MAX_K];
-  __shared__ uint32_t wsum[kPoolSelectThreads / 64];
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = max(0, min(pool_cnt[q], p));
-  const int kp = min(k, n);
-  const int32_t* prow = pool + (int64_t)q * p;
-  int32_t* orow = out_idx + (int64_t)q * k;
-  int n2 = 1;
-  while (n2 < n) n2 <<= 1;
-  for (int i = tid; i < n2; i += kPoolSelectThreads) {
-    key[i] = i < n ? ((uint64_t)score_key(sc[(int64_t)q * pstride + i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i)
-                   : 0ull;
-    flag[i] = 0;
-  }
-  lds_barrier();
-  for (int size = 2; size <= n2; size <<= 1) {           // bitonic sort, descending
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n2 / 2; i += kPoolSelectThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t x = key[lo], y = key[hi];
-        if ((x < y) == desc) { key[lo] = y; key[hi] = x; }
-      }
-      lds_barrier();
-    }
-  }
-  for (int i = tid; i < kp; i += kPoolSelectThreads) flag[0xFFFFFFFFu - (uint32_t)key[i]] = 1;
-  lds_barrier();
-  // flagged positions in pool order: thread t owns positions [2t, 2t + 2)
-  const int p0 = 2 * tid;
-  const uint32_t mine = (p0 < n ? flag[p0] : 0) + (p0 + 1 < n ? flag[p0 + 1] : 0);
-  uint32_t x = mine;
+// Exclusive prefix sum of v over the workgroup (kPoolSelThreads threads);
+// part must hold one slot per wave and not be in use by another scan.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) wsum[wave] = x;
+  if (lane == 63) part[wave] = x;
   lds_barrier();
-  uint32_t pos = x - mine;
-  for (int i = 0; i < wave; ++i) pos += wsum[i];
-  if (p0 < n && flag[p0]) orow[pos++] = prow[p0];
-  if (p0 + 1 < n && flag[p0 + 1]) orow[pos] = prow[p0 + 1];
-  for (int i = kp + tid; i < k; i += kPoolSelectThreads) orow[i] = -1;
+  uint32_t base = 0;
+  for (int i = 0; i < wave; ++i) base += part[i];
+  return base + x - v;
+}
+
+// Scores: by_entry == 0: sc[q * sstride + position] (the pool scan's output);
+// by_entry != 0: sc[q * sstride + entry] (an exhaustive scan's score row).
+__global__ void __launch_bounds__(kPoolSelThreads)
+pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_cnt, int p,
+                   const float* __restrict__ sc, int64_t sstride, int by_entry, int k, int32_t* __restrict__ out_idx,
+                   int32_t* __restrict__ out_cnt) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t part[2][kPoolSelThreads / 64];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int n = max(0, min(pool_cnt[q], p));
+  const int kp = min(k, n);
+  const int32_t* prow = pool + (int64_t)q * p;
+  const float* srow = sc + q * sstride;
+  int32_t* orow = out_idx + (int64_t)q * k;
+  uint32_t key[kPoolPer];
+  int32_t ent[kPoolPer];
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) ent[i] = kPoolPer * tid + i < n ? prow[kPoolPer * tid + i] : 0;
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    const int pos = kPoolPer * tid + i;
+    key[i] = pos < n ? score_key(srow[by_entry ? ent[i] : pos]) : 0u;
+  }
+  auto valid = [&](int i) { return kPoolPer * tid + i < n; };
+  // threshold T: the kp-th largest key; need: how many keys equal to T are taken
+  uint32_t T = 0, need = 0;
+  if (kp < n) {
+    uint32_t prefix = 0;
+    need = (uint32_t)kp;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int sh = 24 - 8 * pass;
+      hist[tid] = 0;
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < kPoolPer; ++i)
+        if (valid(i) && (pass == 0 || (key[i] >> (sh + 8)) == prefix)) atomicAdd(&hist[(key[i] >> sh) & 255u], 1u);
+      lds_barrier();
+      if (tid < 64) {
+        // lane l: digits 255 - 4l - i, i = 0..3 (descending); the lane whose
+        // range holds the need-th largest key resolves the digit
+        uint32_t c[4], mine = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * tid - i]; mine += c[i]; }
+        uint32_t x = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(x, o);
+          if (tid >= o) x += y;
+        }
+        uint32_t run = x - mine;
+        if (run < need && need <= x) {
+          bool done = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!done && need <= run + c[i]) {
+              res[0] = 255u - 4u * tid - i;
+              res[1] = run;
+              done = true;
+            }
+            run += c[i];
+          }
+        }
+      }
+      lds_barrier();
+      prefix = (prefix << 8) | res[0];
+      need -= res[1];
+    }
+    T = prefix;
+  }
+  uint32_t eq = 0;
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) eq += (valid(i) && key[i] == T) ? 1u : 0u;
+  uint32_t rank = block_excl_sum(eq, part[0]);             // tied keys before this thread's, in pool order
+  uint32_t take = 0;
+  bool sel[kPoolPer];
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    const bool tie = valid(i) && key[i] == T;
+    sel[i] = valid(i) && (kp == n || key[i] > T || (tie && rank < need));
+    rank += tie ? 1u : 0u;
+    take += sel[i] ? 1u : 0u;
+  }
+  uint32_t pos = block_excl_sum(take, part[1]);
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i)
+    if (sel[i] && pos < (uint32_t)k) orow[pos++] = ent[i];
+  for (int i = kp + tid; i < k; i += kPoolSelThreads) orow[i] = -1;
   if (tid == 0) out_cnt[q] = kp;
 }
 
@@ -146,8 +190,20 @@ hipError_t launch_pool_index(const CacheArgs& c, const uint8_t* q_idx, const flo
   const int nchunks = (p + kPoolChunk - 1) / kPoolChunk;
   launch(pool_scan_kernel, dim3((unsigned)((int64_t)nq * nchunks)), dim3(kPoolWaves * 64), s, ev_scan, c, q_idx, w,
          q_seq, pool, pool_cnt, nq, h_idx, p, nchunks, sc, pstride);
-  launch(pool_select_kernel, dim3((unsigned)nq), dim3(kPoolSelectThreads), s, ev_select, pool, pool_cnt, p,
-         (const float*)sc, pstride, k, out_idx, out_cnt);
+  launch(pool_select_kernel, dim3((unsigned)nq), dim3(kPoolSelThreads), s, ev_select, pool, pool_cnt, p,
+         (const float*)sc, (int64_t)pstride, 0, k, out_idx, out_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_select_by_entry(const int32_t* pool, const int32_t* pool_cnt, int nq, int p,
+                                       const float* scores, int64_t vstride, int k, int32_t* out_idx,
+                                       int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
+  if (nq <= 0) {
+    record_empty(ev, s);
+    return hipSuccess;
+  }
+  launch(pool_select_kernel, dim3((unsigned)nq), dim3(kPoolSelThreads), s, ev, pool, pool_cnt, p, scores, vstride, 1,
+         k, out_idx, out_cnt);
   return hipGetLastError();
 }
 

@@ -79,14 +79,11 @@ class DeviceCase:
                          for li, mode in enumerate(spec.modes)] if self.group_aux > 0 else None
         self.inputs = []
         self.outputs = []
-        self.calls: List[ops.LayerCall] = []
-        group_calls: List[ops.LayerCall] = []
-        full_idx = full_cnt = None
         # hierarchical indexer: the Full layer's Top-pool_k, scored again by the Reindex layers
         self.pool = self.pool_cnt = None
         if spec.pool_k:
-            self.pool = torch.empty((nq, spec.pool_k), dtype=torch.int32, device=dev)
-            self.pool_cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+            self.pool, self.pool_cnt = self.new_pool(spec.pool_k)
+        full_idx = full_cnt = None
         for li, mode in enumerate(spec.modes):
             qi, w, q = W.layer_queries(spec, li, self.gen_device)
             qi, w, q = qi.to(dev).contiguous(), w.to(dev).contiguous(), q.to(dev).contiguous()
@@ -100,26 +97,37 @@ class DeviceCase:
                 cnt = torch.empty(nq, dtype=torch.int32, device=dev)
                 if mode == ops.FULL:
                     full_idx, full_cnt = idx, cnt
-
-            def make(ws, mode=mode, qi=qi, w=w, q=q, idx=idx, cnt=cnt, out=out, lse=lse):
-                if mode == ops.REUSE:
-                    return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                         idx, cnt, out, lse, ws=ws)
-                if mode == ops.FULL:
-                    return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                         idx, cnt, out, lse, q_idx=qi, w=w, new_slots=self.new_slots,
-                                         new_kv=self.new_kv, new_idxk=self.new_ik, ws=ws, dense=self.dense,
-                                         pool=self.pool, pool_cnt=self.pool_cnt)
-                return ops.LayerCall(mode, self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale,
-                                     idx, cnt, out, lse, q_idx=qi, w=w, ws=ws, dense=self.dense,
-                                     pool=self.pool, pool_cnt=self.pool_cnt)
-            call = make(self.ws)
-            if self.group_ws is not None:
-                group_calls.append(make(self.group_ws[li]))
             self.outputs.append(dict(idx=idx, cnt=cnt, out=out, lse=lse))
-            self.calls.append(call)
+        self.calls: List[ops.LayerCall] = [self.make_call(li, self.ws) for li in range(len(spec.modes))]
+        group_calls = ([self.make_call(li, self.group_ws[li]) for li in range(len(spec.modes))]
+                       if self.group_ws is not None else [])
 
         self.group = ops.GroupCall(group_calls, n_aux=self.group_aux) if self.group_aux > 0 else None
+
+    def new_pool(self, pool_k: int):
+        """Pool buffers [nq][pool_k], [nq] for a hierarchical-indexer variant."""
+        nq = self.spec.nq
+        return (torch.empty((nq, pool_k), dtype=torch.int32, device=self.device),
+                torch.empty(nq, dtype=torch.int32, device=self.device))
+
+    def make_call(self, li: int, ws, pool=None, pool_cnt=None) -> ops.LayerCall:
+        """csa2_layer_step arguments of layer li on workspace ws; pool (default:
+        the case's own) switches on the hierarchical indexer for Full and
+        Reindex layers."""
+        spec, k = self.spec, self.spec.k
+        mode = spec.modes[li]
+        qi, w, q = self.inputs[li]
+        o = self.outputs[li]
+        if pool is None:
+            pool, pool_cnt = self.pool, self.pool_cnt
+        common = (self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale, o["idx"], o["cnt"],
+                  o["out"], o["lse"])
+        if mode == ops.REUSE:
+            return ops.LayerCall(mode, *common, ws=ws)
+        if mode == ops.FULL:
+            return ops.LayerCall(mode, *common, q_idx=qi, w=w, new_slots=self.new_slots, new_kv=self.new_kv,
+                                 new_idxk=self.new_ik, ws=ws, dense=self.dense, pool=pool, pool_cnt=pool_cnt)
+        return ops.LayerCall(mode, *common, q_idx=qi, w=w, ws=ws, dense=self.dense, pool=pool, pool_cnt=pool_cnt)
 
     def run_group(self, stream=None) -> None:
         if self.group is not None:

@@ -27,6 +27,8 @@ def _check_sampled(spec, sample, exact=False):
     got = dc.results_host()
     q_seq, q_vis = spec.q_seq(), spec.q_vis()
     full_idx = got[0]["idx"]
+    if spec.pool_k:
+        pool, pool_cnt = dc.pool.cpu().numpy(), dc.pool_cnt.cpu().numpy()
     inter = total = 0
     for i in sample:
         s, vis = int(q_seq[i]), int(q_vis[i])
@@ -36,7 +38,27 @@ def _check_sampled(spec, sample, exact=False):
         for li, mode in enumerate(spec.modes):
             g = got[li]
             qi, w, q = (x.cpu().numpy() for x in dc.inputs[li])
-            if mode != O.REUSE:
+            if mode == O.FULL and spec.pool_k:
+                # the pool: this layer's Top-pool_k
+                sc = O.index_scores(cache, 0, vis, qi[i], w[i])
+                pi, pc = O.select_topk(sc, spec.pool_k)
+                if exact:
+                    assert pool_cnt[i] == pc and np.array_equal(pool[i, :pc], pi[:pc])
+                else:
+                    check_selection_valid(pool[i], pool_cnt[i], pi, pc, sc, spec.pool_k)
+            if mode == O.REINDEX and spec.pool_k:
+                # Top-k of the GPU's pool: exact on integer inputs, else valid up to near-ties
+                oi, oc = O.pool_index_topk(cache, qi[i:i + 1], w[i:i + 1], np.zeros(1, np.int32), pool[i:i + 1],
+                                           pool_cnt[i:i + 1], spec.k)
+                oi, oc = oi[0], int(oc[0])
+                full = O.index_scores(cache, 0, vis, qi[i], w[i])
+                sc = np.full(full.shape, -np.inf)
+                sc[pool[i, :pool_cnt[i]]] = full[pool[i, :pool_cnt[i]]]
+                if exact:
+                    assert g["cnt"][i] == oc and np.array_equal(g["idx"][i], oi)
+                else:
+                    check_selection_valid(g["idx"][i], g["cnt"][i], oi, oc, sc, spec.k)
+            elif mode != O.REUSE:
                 sc = O.index_scores(cache, 0, vis, qi[i], w[i])
                 oi, oc = O.select_topk(sc, spec.k)
                 if exact:
@@ -72,6 +94,18 @@ def test_config1_decode_b32_64k_group():
 
 def test_config1_integer_exact():
     _check_sampled(W.config(1, integer_indexer=True), sample=[5, 30], exact=True)
+
+
+def test_config1_hierarchical_indexer_integer_exact():
+    """The decode workload with a 2,048-entry pool: the Full layer's pool and
+    selection and the Reindex layer's selection in the pool, bit-exact."""
+    import dataclasses
+    _check_sampled(dataclasses.replace(W.config(1, integer_indexer=True), pool_k=2048), sample=[3, 28], exact=True)
+
+
+def test_config1_hierarchical_indexer_gaussian():
+    import dataclasses
+    _check_sampled(dataclasses.replace(W.config(1), pool_k=2048), sample=[0, 31])
 
 
 def test_config2_prefill_sampled_rows():
