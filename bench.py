@@ -146,6 +146,7 @@ def time_hierarchical(dc, pool_k: int, steps: int):
     n_pool = len(reindex) + 1
     rings = {c: ops.TimingRing(c, steps * n_pool) for c in (L.KCLASS_POOL_SCAN, L.KCLASS_POOL_SELECT)}
     rings[L.KCLASS_SCAN] = ops.TimingRing(L.KCLASS_SCAN, steps)
+    rings[L.KCLASS_SELECT] = ops.TimingRing(L.KCLASS_SELECT, steps)
     for r in rings.values():
         r.install()
     for _ in range(steps):
@@ -153,6 +154,19 @@ def time_hierarchical(dc, pool_k: int, steps: int):
     for r in rings.values():
         r.uninstall()
     dur = {c: r.durations_ms() for c, r in rings.items()}
+    group_ms = None
+    if dc.group_ws is not None:
+        # the same group as one csa2_group_step, Reuse attentions on an auxiliary stream
+        gcall = ops.GroupCall([dc.make_call(li, dc.group_ws[li], pool, pool_cnt) for li in range(len(spec.modes))],
+                              n_aux=1)
+        for _ in range(3):
+            gcall()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gcall()
+        torch.cuda.synchronize()
+        group_ms = (time.perf_counter() - t0) * 1e3 / steps
     kept = []
     for li in reindex:
         ei, ec = exhaustive[li]
@@ -164,7 +178,12 @@ def time_hierarchical(dc, pool_k: int, steps: int):
     return {"pool_k": pool_k, "execution": "one csa2_layer_step call per layer",
             "ms_per_step_no_events": round(ms, 5),
             "tokens_per_s": round(spec.num_seqs * spec.n_new / (ms / 1e3), 1),
+            "group_step": (None if group_ms is None else
+                           {"execution": "csa2_group_step, Reuse attentions on 1 auxiliary stream",
+                            "ms_per_step_no_events": round(group_ms, 5),
+                            "tokens_per_s": round(spec.num_seqs * spec.n_new / (group_ms / 1e3), 1)}),
             "kernels_avg_us": {"scan_full": round(statistics.mean(dur[L.KCLASS_SCAN]) * 1e3, 2),
+                               "select_full_top_pool_k": round(statistics.mean(dur[L.KCLASS_SELECT]) * 1e3, 2),
                                "pool_scan": round(scan_us, 2),
                                "pool_select": round(statistics.mean(dur[L.KCLASS_POOL_SELECT]) * 1e3, 2)},
             "pool_scan_bytes_per_launch": pb, "pool_scan_GBps": round(pb / (scan_us / 1e6) / 1e9, 1),

@@ -11,12 +11,14 @@
 // operand (same layout, same product, same ReLU * w reduction as the scan), so
 // a pool entry's score has the bits the exhaustive scan gives it.
 //
-// pool_select_kernel: one workgroup per query, eight pool positions per
+// pool_select_kernel: one workgroup per query, four pool positions per
 // thread.  A most-significant-digit-first radix search over the 32-bit score
-// keys (four 8-bit digits, histograms in LDS) finds the k-th largest key T
-// and how many entries tied at T still fit; the entries above T and the
-// first of those tied at T in pool order are selected, and a block-wide
-// prefix count writes them in pool order, which is ascending entry order.
+// keys (four 8-bit digits, histograms in LDS, digit search by a DPP wave
+// prefix sum) finds the k-th largest key T and how many entries tied at T
+// still fit; the entries above T and the first of those tied at T in pool
+// order are selected, and a block-wide prefix count writes them in pool
+// order, which is ascending entry order.  Every load is issued unconditionally
+// (positions clamped) so they are all in flight at once.
 #include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_internal.h"
@@ -25,7 +27,7 @@ namespace csa2 {
 
 constexpr int kPoolWaves = 4;
 constexpr int kPoolChunk = 16 * kPoolWaves;   // pool entries per scan workgroup: one tile per wave
-constexpr int kPoolSelThreads = 256;
+constexpr int kPoolSelThreads = 512;
 constexpr int kPoolPer = CSA2_MAX_K / kPoolSelThreads;   // pool positions per select thread
 
 __global__ void __launch_bounds__(kPoolWaves * 64)
@@ -66,16 +68,24 @@ pool_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __
   if (g == 0 && e0 + r < e1) sc[(int64_t)q * pstride + e0 + r] = __uint_as_float(u32);
 }
 
+// Inclusive prefix sum over the wave: DPP row shifts within each 16-lane row,
+// then the totals of the rows below (read from lanes 15, 31, 47).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+                 r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Exclusive prefix sum of v over the workgroup (kPoolSelThreads threads);
 // part must hold one slot per wave and not be in use by another scan.
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) part[wave] = x;
   lds_barrier();
   uint32_t base = 0;
@@ -100,12 +110,19 @@ pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__
   int32_t* orow = out_idx + (int64_t)q * k;
   uint32_t key[kPoolPer];
   int32_t ent[kPoolPer];
+  if (n == 0) {
+    for (int i = tid; i < k; i += kPoolSelThreads) orow[i] = -1;
+    if (tid == 0) out_cnt[q] = 0;
+    return;
+  }
 #pragma unroll
-  for (int i = 0; i < kPoolPer; ++i) ent[i] = kPoolPer * tid + i < n ? prow[kPoolPer * tid + i] : 0;
+  for (int i = 0; i < kPoolPer; ++i) ent[i] = prow[min(kPoolPer * tid + i, n - 1)];
+  if (by_entry) {
 #pragma unroll
-  for (int i = 0; i < kPoolPer; ++i) {
-    const int pos = kPoolPer * tid + i;
-    key[i] = pos < n ? score_key(srow[by_entry ? ent[i] : pos]) : 0u;
+    for (int i = 0; i < kPoolPer; ++i) key[i] = score_key(srow[ent[i]]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPoolPer; ++i) key[i] = score_key(srow[min(kPoolPer * tid + i, n - 1)]);
   }
   auto valid = [&](int i) { return kPoolPer * tid + i < n; };
   // threshold T: the kp-th largest key; need: how many keys equal to T are taken
@@ -116,7 +133,7 @@ pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
       const int sh = 24 - 8 * pass;
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < kPoolPer; ++i)
@@ -128,12 +145,7 @@ pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__
         uint32_t c[4], mine = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * tid - i]; mine += c[i]; }
-        uint32_t x = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(x, o);
-          if (tid >= o) x += y;
-        }
+        const uint32_t x = wave_incl_sum(mine);
         uint32_t run = x - mine;
         if (run < need && need <= x) {
           bool done = false;
