@@ -371,7 +371,10 @@ int attn_nsplit(int nq, int h, int k) {
   const int units = nq * ((h + 15) / 16);
   const int ntiles = (k + kTileRows - 1) / kTileRows;
   const int rg = attn_rgroups(nq, h);
-  const int target = rg > 1 ? 256 : 512;                 // workgroups that fill the chip
+  // Splitting pays only while few units run: a split halves the tile loop but
+  // adds the share write-out and a combine launch, which at 128 units (32
+  // decode queries x 64 heads) already cost more than they save.
+  const int target = rg > 1 ? 128 : 512;
   int ns = 1;
   // split across workgroups only while every row group keeps two tiles per share
   while (ns < 16 && units * ns < target && ntiles >= 2 * rg * 2 * ns) ns *= 2;
