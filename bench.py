@@ -3,9 +3,12 @@
 One step = one CSA2 layer group (Full, Reindex, Reuse, Reuse) over a batch of
 32 decode sequences with 65,536 cached entries each plus one entry appended
 by quantize-on-append (indexer 8 x 128 FP8, 64 heads over the 512-wide FP4
-latent, Top-512), run as one csa2_group_step (the Reuse layers' attention on
-an auxiliary stream).  Inputs are synthetic, seeded, and already resident in
-HBM when timing starts.  Prints one JSON line.
+latent, Top-512), as one csa2_layer_step call per layer in layer order: in a
+model each layer's queries depend on the previous layer's output, so this is
+the schedule a real decode step can run (the group step, which overlaps the
+Reuse layers' attention with the next layers, is timed beside it).  Inputs
+are synthetic, seeded, and already resident in HBM when timing starts.
+Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --config 2             # causal prefill of 4,096 rows against
@@ -410,7 +413,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--aux-streams", type=int, default=1,
+    ap.add_argument("--aux-streams", type=int, default=0,
                     help="run the timed multi-layer group as one csa2_group_step with this many auxiliary "
                          "streams (0: one csa2_layer_step call per layer); the other mode is timed too")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "scan_traffic.json"),
