@@ -67,7 +67,7 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float scale) {
 template <int RG>
 struct AttnShared {
   uint8_t xs[4 * RG][kSliceBytes];   // [wave] bf16 slice rows of its current tile (8,704 B each)
-  floatx4 sp[RG][4][2][4][16];       // partial S^T per row group and wave: [m-tile][row quad][head] of 4 rows
+  floatx4 sp[RG == 2 ? 2 : 1][RG][4][2][4][16];   // [buffer][row group][wave]: partial S^T, [m-tile][row quad][head]
   uint32_t row[kMaxShareRows];       // physical row of every selected entry of the share (8,192 B)
 };
 
@@ -181,16 +181,17 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       for (int s = 0; s < 4; ++s)
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(rowp + 16 * s), qop[s], st,
                                                      0, 0, 0);
-      S.sp[rg][ds][mt][g][r] = st;                      // lanes write consecutive 16 B: no bank conflicts
+      S.sp[RG == 2 ? (tt & 1) : 0][rg][ds][mt][g][r] = st;   // lanes write consecutive 16 B: no bank conflicts
     }
     lds_barrier();
     // ---- full scores of head r, rows mt*16 + 4g + i (fixed summation order) ----
     float v[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      floatx4 acc = S.sp[rg][0][mt][g][r];
+      const int sb = RG == 2 ? (tt & 1) : 0;
+      floatx4 acc = S.sp[sb][rg][0][mt][g][r];
 #pragma unroll
-      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[rg][d2][mt][g][r];
+      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[sb][rg][d2][mt][g][r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[mt][i] = acc[i] * sm_scale;
     }
@@ -254,7 +255,10 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb, oacc[nt], 0, 0, 0);
       oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb, oacc[nt], 0, 0, 0);
     }
-    lds_barrier();
+    // With two partial-S buffers, a wave may write tile t+1's partial while
+    // others still read tile t's: every read of the buffer it overwrites
+    // (tile t-1) came before this tile's barrier.  Slice rows are per wave.
+    if (RG != 2) lds_barrier();
   }
   }
 
