@@ -17,16 +17,16 @@
 //     pass.  Queries with V <= k need no threshold; short contexts keep all.
 //  2. candidates (prefill_scan_kernel, first pass): the product itself; an
 //     entry whose score reaches the threshold has its score stored at its
-//     position and its bit set in a per-(query, 16-entry tile) mask; each
-//     query counts its candidates.
-//  3. exactness (same kernel, second launch): a query with fewer than k
-//     candidates (the sample was unlucky) is rescored in full with every
-//     visible entry a candidate; blocks without such a query exit at once.
-//  4. compaction (prefill_compact_kernel): masks -> ordered candidate list,
-//     plus the 2,048-bin histogram of the candidates' score keys, which is all
-//     the final select needs: every entry at or above the k-th key is a
-//     candidate, so the k-th key and the entries above it are the same as
-//     over all entries.
+//     position and its bit set in a per-(query, 16-entry tile) mask.
+//  3. compaction (prefill_compact_kernel): masks -> ordered candidate list
+//     and its count, plus the 2,048-bin histogram of the candidates' score
+//     keys, which is all the final select needs: every entry at or above the
+//     k-th key is a candidate, so the k-th key and the entries above it are
+//     the same as over all entries.
+//  4. exactness (the scan kernel again, then the compaction again): a query
+//     with fewer than k candidates (the sample was unlucky) is rescored in
+//     full with every visible entry a candidate and compacted anew; blocks
+//     without such a query exit at once.
 //
 // Matrix product: A = the queries' indexer heads ([nq * h_idx] x 128 E4M3),
 // B = the sequence's indexer-K rows (128 x V E4M3).  A workgroup of 4 waves
@@ -185,7 +185,7 @@ prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* 
 // 2./3. candidate pass (RESCORE = false) and full rescore of short queries
 // ---------------------------------------------------------------------------
 template <int QPT, bool RESCORE>
-__global__ void __launch_bounds__(kPfWaves * 64, 4)
+__global__ void __launch_bounds__(kPfWaves * 64, 3)
 prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
                     int nq, int h_idx, int k, int chunk, int per_xcd, IndexWs ws) {
@@ -214,7 +214,8 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: tile indices stay scalar
   const int g = lane >> 4, r = lane & 15;
   // A tiles in registers; their head weights, the same for all 16 lanes of a
-  // row group, in LDS (read back as one broadcast per use)
+  // row group, staged through LDS once and then held in registers (three
+  // waves per SIMD leave room for them, so no epilogue waits on LDS)
   intx8 a[kPfTiles];
 #pragma unroll
   for (int t = 0; t < kPfTiles; ++t) {
@@ -300,22 +301,20 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
       acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[kPerSet * p + i], bop, acc[i], 0, 0, 0, 0, 0, 0);
     }
   };
+  float4 wreg[kPfTiles];
+#pragma unroll
+  for (int t = 0; t < kPfTiles; ++t) wreg[t] = S.w[t][g];
   auto finish = [&](int p, const floatx4 (&acc)[kPerSet]) {
     if (QPT == 2) {
-      return pair_rows2(relu_weighted4(acc[0], S.w[2 * p][g]), relu_weighted4(acc[1], S.w[2 * p + 1][g]));
+      return pair_rows2(relu_weighted4(acc[0], wreg[2 * p]), relu_weighted4(acc[1], wreg[2 * p + 1]));
     } else {
       float sq[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sq[i] = halves_sum(rows_pair_sum(relu_weighted4(acc[i], S.w[4 * p + i][g])));
+      for (int i = 0; i < 4; ++i) sq[i] = halves_sum(rows_pair_sum(relu_weighted4(acc[i], wreg[4 * p + i])));
       return g == 0 ? sq[0] : g == 1 ? sq[1] : g == 2 ? sq[2] : sq[3];
     }
   };
 
-  uint32_t cnt[kSets][4];                            // candidates per (set, row): wave-uniform
-#pragma unroll
-  for (int p = 0; p < kSets; ++p)
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) cnt[p][gg] = 0;
   // sink: last score slot of the block's first row, never read
   const uint32_t sink_off = (uint32_t)(ws.vstride - 1) * 4u;
 
@@ -335,12 +334,10 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     for (int p = 0; p < kSets; ++p) {
       if (p + 1 < kSets) products(bop, p + 1, nxt);
       const float sc = finish(p, cur);
-      const bool keep = e < vis_of[p] && sc >= tau_of[p];   // causal mask, threshold
-      const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+      const bool c1 = e < vis_of[p], c2 = sc >= tau_of[p];   // causal mask, threshold
+      const uint64_t m = __builtin_amdgcn_ballot_w64(c1) & __builtin_amdgcn_ballot_w64(c2);
       masks[p] = m;
-      *reinterpret_cast<float*>(st + (keep ? soff[p] : sink)) = sc;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) cnt[p][gg] += (uint32_t)__builtin_popcountll(m & (0xFFFFull << (16 * gg)));
+      *reinterpret_cast<float*>(st + (c1 && c2 ? soff[p] : sink)) = sc;
 #pragma unroll
       for (int i = 0; i < kPerSet; ++i) cur[i] = nxt[i];
     }
@@ -383,28 +380,23 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     load(j + 4 * kPfWaves, l1);
     process(j + 2 * kPfWaves, l2);
   }
-  if (!RESCORE && lane == 0) {
-#pragma unroll
-    for (int p = 0; p < kSets; ++p)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int ql = (QPT == 2) ? 4 * p + 2 * (gg & 1) + (gg >> 1) : 4 * p + gg;
-        if (cnt[p][gg]) atomicAdd(&ws.cand_cnt[q0 + ql], cnt[p][gg]);
-      }
-  }
 }
 
 // ---------------------------------------------------------------------------
 // 4. compaction: masks -> candidate list + key histogram (list order is free:
 //    the final select orders its output itself)
 // ---------------------------------------------------------------------------
+// short_only: the pass after the full rescore, for the queries the first
+// compaction left with fewer than k candidates (their masks now hold every
+// visible entry); every other query keeps its list.
 __global__ void __launch_bounds__(kCompactThreads)
-prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, IndexWs ws) {
+prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int short_only, IndexWs ws) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t total;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int V = q_vis[q];
   if (V <= k) return;                                // the final select needs no candidates
+  if (short_only && (int)ws.cand_cnt[q] >= k) return;   // uniform
   for (int i = tid; i < kHistBins; i += kCompactThreads) h[i] = 0;
   if (tid == 0) total = 0;
   const int kq = kPfTiles * qpt, nsets = kPfTiles * qpt / 4;
@@ -479,20 +471,25 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
   const dim3 grid((unsigned)(8 * per_xcd * nqb)), block(kPfWaves * 64);
   const dim3 tgrid((unsigned)((nq + kTauWaves * qpt - 1) / (kTauWaves * qpt))), tblock(kTauWaves * 64);
   const int factor = g_prefill_cand_factor;
+  // threshold, candidates, compaction (which counts each query's
+  // candidates), full rescore of the queries left short, their compaction
   if (qpt == 2) {
     launch(prefill_tau_kernel<2>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
     launch(prefill_scan_kernel<2, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
-           per_xcd, ws);
-    launch(prefill_scan_kernel<2, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
   } else {
     launch(prefill_tau_kernel<1>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
     launch(prefill_scan_kernel<1, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
+  }
+  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, KEvents{}, q_vis, k, qpt, 0, ws);
+  if (qpt == 2)
+    launch(prefill_scan_kernel<2, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+           per_xcd, ws);
+  else
     launch(prefill_scan_kernel<1, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
-  }
-  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, ev.last(), q_vis, k, qpt, ws);
+  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, ev.last(), q_vis, k, qpt, 1, ws);
   return hipGetLastError();
 }
 
