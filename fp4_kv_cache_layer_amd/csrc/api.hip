@@ -109,7 +109,8 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   r.vstride = index_vstride(max_vis);
   r.scores = reinterpret_cast<float*>(p + score_off);
   r.cand = reinterpret_cast<int32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
-  r.mask = reinterpret_cast<uint64_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
+  r.ckey = reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
+  r.mask = reinterpret_cast<uint64_t*>(p + score_off + 3 * (size_t)nq * (size_t)r.vstride * 4);
   return r;
 }
 

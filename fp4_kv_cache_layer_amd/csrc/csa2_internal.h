@@ -29,6 +29,7 @@ struct IndexWs {
   uint32_t* cand_cnt;
   float* scores;
   int32_t* cand;
+  uint32_t* ckey;        // score key of cand[i], stored beside it (the final select reads no scores)
   uint64_t* mask;
   int64_t vstride;
 };

@@ -34,7 +34,7 @@ size_t zero_state_bytes(int32_t nq) {
 size_t index_score_bytes(int32_t nq, int32_t max_vis) {
   const size_t v = (size_t)index_vstride(max_vis);
   const size_t nq16 = ((size_t)nq + 15) / 16 * 16;      // candidate masks cover whole 16-query blocks
-  return (size_t)nq * 8 * v + nq16 * v / 8;
+  return (size_t)nq * 12 * v + nq16 * v / 8;           // scores, candidates, candidate keys, masks
 }
 
 __global__ void __launch_bounds__(kScanWaves * 64)

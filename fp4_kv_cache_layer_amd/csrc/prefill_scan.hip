@@ -439,6 +439,7 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
   }
   __syncthreads();                                   // the list is complete (global writes included)
   const uint32_t n = total;
+  uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride;
   for (uint32_t i0 = 0; i0 < n; i0 += kCompactThreads * kBatch) {
     float sv[kBatch];
 #pragma unroll
@@ -447,8 +448,14 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
       sv[u] = i < n ? sc[cand[i]] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (i0 + u * kCompactThreads + tid < n) atomicAdd(&h[score_key(sv[u]) >> (32 - kHistBits)], 1u);
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = i0 + u * kCompactThreads + tid;
+      if (i < n) {
+        const uint32_t key = score_key(sv[u]);
+        ckey[i] = key;
+        atomicAdd(&h[key >> (32 - kHistBits)], 1u);
+      }
+    }
   }
   lds_barrier();
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;

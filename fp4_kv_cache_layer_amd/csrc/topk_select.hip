@@ -34,10 +34,6 @@ namespace {
 constexpr int kSelCap = 2048;
 constexpr int kCollectThreads = 256;
 
-__device__ __forceinline__ uint64_t composite(float s, int t) {
-  return ((uint64_t)score_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
-}
-
 // Lowest float whose orderable key is >= key (scores are canonical: no -0, no NaN).
 __device__ __forceinline__ float key_floor_float(uint32_t key) {
   if (key == 0) return -INFINITY;
@@ -137,6 +133,7 @@ __global__ void __launch_bounds__(kCollectThreads)
 topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int nslices) {
   __shared__ __attribute__((aligned(16))) uint32_t h[kHistBins];
   __shared__ int32_t list[kCollectSlice];             // this slice's candidates
+  __shared__ uint32_t klist[kCollectSlice];           // and their score keys
   __shared__ uint32_t res[2];
   __shared__ int count, base;
   const int q = blockIdx.x / nslices;
@@ -187,7 +184,10 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int t = t0 + 4 * vi + c;
-        if (t < t1 && e[c] >= floor_s) list[pos++] = t;   // at most kCollectSlice entries in all
+        if (t < t1 && e[c] >= floor_s) {                  // at most kCollectSlice entries in all
+          list[pos] = t;
+          klist[pos++] = score_key(e[c]);
+        }
       }
     }
   }
@@ -198,7 +198,11 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
   if (tid == 0) base = atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
   lds_barrier();
   int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
-  for (int i = tid; i < n; i += kCollectThreads) cand[i] = list[i];
+  uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride + base;
+  for (int i = tid; i < n; i += kCollectThreads) {
+    cand[i] = list[i];
+    ckey[i] = klist[i];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -225,8 +229,8 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = q_vis[q];
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
-  const float* sc = ws.scores + (int64_t)q * ws.vstride;
   const int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
+  const uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride;
   int32_t* oi = out_idx + (int64_t)q * k;
 
   if (V <= k) {                                       // everything visible is selected
@@ -256,7 +260,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
     lds_barrier();
     for (int i = tid; i < ncand; i += kSelectThreads) {
       const int t = cand[i];
-      const uint64_t C = composite(sc[t], t);
+      const uint64_t C = ((uint64_t)ckey[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
       if ((C >> (64 - nbits)) == P) atomicAdd(&S.h[(uint32_t)(C >> (64 - nbits - d)) & ((1u << d) - 1)], 1u);
     }
     lds_barrier();
@@ -270,20 +274,22 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
   }
 
   // candidates: prefix above P -> selected; prefix equal to P -> parked.
-  // Batches of kCandBatch per thread: all their indices, then all their
-  // scores, are in flight together.
+  // Batches of kCandBatch per thread: all their indices and keys are in
+  // flight together.
   constexpr int kCandBatch = 4;
   for (int i0 = 0; i0 < ncand; i0 += kCandBatch * kSelectThreads) {
     int t[kCandBatch];
-    float sv[kCandBatch];
+    uint32_t kv[kCandBatch];
 #pragma unroll
-    for (int b = 0; b < kCandBatch; ++b) t[b] = cand[min(i0 + b * kSelectThreads + tid, ncand - 1)];
-#pragma unroll
-    for (int b = 0; b < kCandBatch; ++b) sv[b] = sc[t[b]];
+    for (int b = 0; b < kCandBatch; ++b) {
+      const int i = min(i0 + b * kSelectThreads + tid, ncand - 1);
+      t[b] = cand[i];
+      kv[b] = ckey[i];
+    }
 #pragma unroll
     for (int b = 0; b < kCandBatch; ++b) {
       const bool valid = i0 + b * kSelectThreads + tid < ncand;
-      const uint64_t C = composite(sv[b], t[b]);
+      const uint64_t C = ((uint64_t)kv[b] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t[b]);
       const uint64_t pre = C >> (64 - nbits);
       wave_append<int32_t>(valid && pre > P, t[b], &S.selcnt, S.sel, kSelCap);
       wave_append<uint64_t>(valid && pre == P, C, &S.tiecnt, S.tie, kTieCap);

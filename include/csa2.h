@@ -118,8 +118,9 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
  * per-query histograms [nq][2048] u32 and candidate counters [nq] u32
  * first; then, for batches small enough that the attention splits each
  * query's rows across workgroups, the attention shares; then (Full and
- * Reindex) per-query scores [nq][round_up(max_vis, 64)] fp32 and candidate
- * indices of the same shape, that region being at least nq * 8 KB so a
+ * Reindex) per-query scores [nq][round_up(max_vis, 64)] fp32, candidate
+ * indices and their score keys of the same shape, that region being at
+ * least nq * 8 KB so a
  * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk and
  * csa2_sparse_attn accept a
  * workspace sized by this call for the same shape.  The histogram part carries state:
