@@ -68,19 +68,6 @@ pool_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __
   if (g == 0 && e0 + r < e1) sc[(int64_t)q * pstride + e0 + r] = __uint_as_float(u32);
 }
 
-// Inclusive prefix sum over the wave: DPP row shifts within each 16-lane row,
-// then the totals of the rows below (read from lanes 15, 31, 47).
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
-                 r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
-
 // Exclusive prefix sum of v over the workgroup (kPoolSelThreads threads);
 // part must hold one slot per wave and not be in use by another scan.
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* part) {

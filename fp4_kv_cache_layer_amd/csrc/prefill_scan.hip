@@ -419,12 +419,7 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const uint32_t n = __builtin_popcount(bits[u]);
-      uint32_t x = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
+      const uint32_t x = wave_incl_sum(n);
       uint32_t wbase = 0;
       if (lane == 63 && x) wbase = atomicAdd(&total, x);
       wbase = __shfl(wbase, 63);

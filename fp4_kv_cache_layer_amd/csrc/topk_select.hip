@@ -44,45 +44,38 @@ __device__ __forceinline__ float key_floor_float(uint32_t key) {
 // Search over a descending-ordered histogram h[0..nb) (nb <= 2048): the
 // largest digit d* whose suffix count reaches need (1 <= need <= total), and
 // the count strictly above it, written to result[0..1].  One wave does the
-// search (lane l sums the digits at descending positions [l*per, l*per + per),
-// then a wave scan finds the lane holding d*); the workgroup barrier at the
-// end publishes the result.  Callers have h complete (a barrier) first.
+// search; the workgroup barrier at the end publishes the result.  Callers
+// have h complete (a barrier) first.
 __device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* result) {
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
     if (nb == kHistBins) {
-      // lane l holds digits [base, base + 32), base = nb - 32 (l + 1), read as
-      // eight 16-byte vectors; descending position i is digit base + 31 - i
+      // Lane l sums the digits [base, base + 32), base = nb - 32 (l + 1)
+      // (descending positions 32l .. 32l+31), reading its eight 16-byte
+      // pieces in a lane-rotated order so the wave's reads spread over the
+      // banks; a wave scan finds the lane L whose range holds d*.  Then lanes
+      // 0..31 take one digit each of L's range, descending, and a second scan
+      // finds d* itself.
       const int base = nb - 32 * (lane + 1);
-      uint32_t v[32];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 w = *reinterpret_cast<const uint4*>(h + base + 4 * j);
-        v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
-      }
       uint32_t mine = 0;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) mine += v[i];
-      uint32_t x = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
+      for (int j = 0; j < 8; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(h + base + 4 * ((j + lane) & 7));
+        mine += (w.x + w.y) + (w.z + w.w);
       }
-      const uint32_t excl = x - mine;
-      if (excl < need && need <= x) {
-        uint32_t run = excl, dig = 0, above = 0;
-        bool done = false;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint32_t c = v[31 - i];
-          const bool hit = !done && need <= run + c;
-          dig = hit ? (uint32_t)(base + 31 - i) : dig;
-          above = hit ? run : above;
-          done = done || hit;
-          run += c;
-        }
-        result[0] = dig;
+      const uint32_t x = wave_incl_sum(mine);
+      const uint64_t hm = __builtin_amdgcn_ballot_w64(x - mine < need && need <= x);
+      const int L = __builtin_ctzll(hm);
+      const uint32_t run0 = __builtin_amdgcn_readlane(x - mine, L);
+      const int dig = nb - 1 - 32 * L - lane;                 // lanes 0..31: L's digits, descending
+      const uint32_t hv = h[lane < 32 ? dig : 0];
+      const uint32_t c = lane < 32 ? hv : 0u;
+      const uint32_t y = wave_incl_sum(c) + run0;
+      const uint64_t dm = __builtin_amdgcn_ballot_w64(lane < 32 && need <= y && y - c < need);
+      const int L2 = __builtin_ctzll(dm);
+      const uint32_t above = __builtin_amdgcn_readlane(y - c, L2);
+      if (lane == 0) {
+        result[0] = (uint32_t)(nb - 1 - 32 * L - L2);
         result[1] = above;
       }
     } else {
@@ -90,12 +83,7 @@ __device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* r
       const int p0 = min(nb, lane * per), p1 = min(nb, p0 + per);
       uint32_t mine = 0;
       for (int p = p0; p < p1; ++p) mine += h[nb - 1 - p];
-      uint32_t x = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-      }
+      const uint32_t x = wave_incl_sum(mine);
       const uint32_t excl = x - mine;
       if (excl < need && need <= x) {
         uint32_t run = excl;
@@ -167,12 +155,7 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
     for (int c = 0; c < 4; ++c) mine += (t0 + 4 * vi + c < t1 && e[c] >= floor_s) ? 1u : 0u;
   }
   const int lane = tid & 63;
-  uint32_t x = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_sum(mine);
   int wbase = 0;
   if (lane == 63 && x) wbase = atomicAdd(&count, (int)x);
   int pos = __shfl(wbase, 63) + (int)(x - mine);
@@ -360,12 +343,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
     const int w0 = min(tid * W, nwords), w1 = min(w0 + W, nwords);
     uint32_t mine = 0;
     for (int i = w0; i < w1; ++i) mine += __builtin_popcount(bm[i]);
-    uint32_t x = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_sum(mine);
     if (lane == 63) S.scratch[wave] = x;
     lds_barrier();
     uint32_t pos = x - mine;
