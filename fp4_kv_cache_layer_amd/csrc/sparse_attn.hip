@@ -23,7 +23,7 @@
 //   - gathers whole 64-byte row segments of its slice (four lanes per row)
 //     with their scale bytes, dequantises them with
 //     V_CVT_SCALEF32_PK_BF16_FP4 into its bf16 slice rows in LDS (row stride
-//     272 B: the 16-byte accesses and the transposing 8-byte reads both spread
+//     288 B: the 16-byte accesses and the transposing 8-byte reads both spread
 //     evenly over the banks), and reads back the A operand of S^T = X Q^T
 //     (bf16 MFMA 16x16x32, K = its 128 dims, permuted alike in the Q operand),
 //   - publishes its partial S^T (32 rows x 16 heads) in LDS,
@@ -39,8 +39,8 @@
 namespace csa2 {
 
 constexpr int kTileRows = 32;
-constexpr int kSliceStride = 272;                       // bytes per bf16 slice row (128 * 2 + 16 pad)
-constexpr int kSliceBytes = kTileRows * kSliceStride;   // 8,704
+constexpr int kSliceStride = 288;                       // bytes per bf16 slice row (128 * 2 + 32 pad)
+constexpr int kSliceBytes = kTileRows * kSliceStride;   // 9,216
 constexpr int kPrefetch = 4;                            // tiles of row gathers in flight per wave
 constexpr float kRescaleSlack = 8.0f;                   // nats the running max may lag the true max
 constexpr int kMaxShareRows = 2048;
@@ -66,7 +66,7 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float scale) {
 
 template <int RG>
 struct AttnShared {
-  uint8_t xs[4 * RG][kSliceBytes];   // [wave] bf16 slice rows of its current tile (8,704 B each)
+  uint8_t xs[4 * RG][kSliceBytes];   // [wave] bf16 slice rows of its current tile (9,216 B each)
   floatx4 sp[RG == 2 ? 2 : 1][RG][4][2][4][16];   // [buffer][row group][wave]: partial S^T, [m-tile][row quad][head]
   uint32_t row[kMaxShareRows];       // physical row of every selected entry of the share (8,192 B)
 };
