@@ -189,3 +189,31 @@ def test_pool_layers_gaussian(seed, cached, pool_k):
         assert set(got[1]["idx"][i, :got[1]["cnt"][i]].tolist()) <= set(pool[i, :pool_cnt[i]].tolist())
     for li in range(3):
         _check_attn(spec, ocache, case.layers[li], got[li])
+
+
+@pytest.mark.parametrize("seed,cached,n_new,k,pool_k", [(71, [700], 37, 64, 256), (72, [3000], 130, 128, 512)])
+def test_pool_prefill_dense_integer_exact(seed, cached, n_new, k, pool_k):
+    """Prefill chunk through the dense indexer with the hierarchical indexer:
+    the Full layer's dense Top-pool_k is the pool, the Reindex layer rescores
+    only the pool (its dense flag has no effect); bit-exact against the
+    oracle on integer inputs."""
+    _, runner = _ops()
+    spec = W.small_case("pool_prefill", seed, cached, n_new=n_new, h_idx=8, h=16, k=k, integer_indexer=True,
+                        modes=(W.FULL, W.REINDEX, W.REUSE), prefill=True, pool_k=pool_k)
+    say(f"[pool prefill] seed={seed} cached={cached} n_new={n_new} k={k} pool_k={pool_k}")
+    dc = runner.DeviceCase(spec, gen_device="cpu")
+    assert dc.dense
+    dc.run_layers()
+    got = dc.results_host()
+    pool, pool_cnt = dc.pool.cpu().numpy(), dc.pool_cnt.cpu().numpy()
+    case = CB.build(spec)
+    ref = CB.run_group(case)
+    assert np.array_equal(pool_cnt, ref[0]["pool_cnt"])
+    for i in range(spec.nq):
+        assert np.array_equal(pool[i, :pool_cnt[i]], ref[0]["pool"][i, :pool_cnt[i]]), f"pool row {i}"
+    ocache = _oracle_cache_after_step(case)
+    for li, (g, r, L) in enumerate(zip(got, ref, case.layers)):
+        assert np.array_equal(g["cnt"], r["cnt"]), f"layer {li} cnt"
+        bad = np.nonzero((g["idx"] != r["idx"]).any(1))[0]
+        assert bad.size == 0, f"layer {li}: {bad.size} queries differ, first {bad[:3]}"
+        _check_attn(spec, ocache, L, g)
