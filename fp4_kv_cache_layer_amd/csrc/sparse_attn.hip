@@ -33,6 +33,8 @@
 //     O[16 heads][its 128 dims] += P X with P split into bf16 hi + lo terms;
 //     the B operand (rows as K) comes from LDS through the transposing read
 //     DS_READ_B64_TR_B16.
+#include <cfloat>
+
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -124,7 +126,12 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   floatx4 oacc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // Running max of the unscaled logits q.X (finite: the first tile with a
+  // visible row replaces it) and running sum of 2^((v - m_run) * c2) =
+  // e^(sm_scale (v - m_run)).
+  float m_run = -FLT_MAX, l_run = 0.0f;
+  const float c2 = sm_scale * 1.44269504088896341f;       // sm_scale * log2(e)
+  const float slack = kRescaleSlack / sm_scale;            // the rescale slack in unscaled units
   const int ntiles = (n + kTileRows - 1) / kTileRows;
   const int ntiles_rg = (ntiles + RG - 1) / RG;          // tiles rg, rg + RG, ... of this row group
   uint8_t* xs = &S.xs[wv][0];
@@ -193,7 +200,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
 #pragma unroll
       for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[sb][rg][d2][mt][g][r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[mt][i] = acc[i] * sm_scale;
+      for (int i = 0; i < 4; ++i) v[mt][i] = acc[i];
     }
     if (lim < kTileRows) {                              // uniform: only a tile holding the end of the share
 #pragma unroll
@@ -206,9 +213,9 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
                        fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
     tmax = halves_max(rows_pair_max(tmax));
     // rescale only when the max moved by more than the slack
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) {
-      const float m_new = tmax > m_run + kRescaleSlack ? tmax : m_run;
-      const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);   // m_run = -inf -> 0
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + slack)) {
+      const float m_new = tmax > m_run + slack ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);   // first visible tile: 0
       l_run *= alpha;
       m_run = m_new;
       float al[4];
@@ -219,13 +226,14 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
     }
+    const float mc = -m_run * c2;
     float p[2][4];
     float psum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[mt][i] = m_run == -INFINITY ? 0.0f : __expf(v[mt][i] - m_run);   // -inf -> 0
+        p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[mt][i], c2, mc));   // masked (-inf) -> 0
         psum += p[mt][i];
       }
     psum = halves_sum(rows_pair_sum(psum));
@@ -284,8 +292,8 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
       const float* other = mbuf + ((o - 1) * 4 + ds) * kMergeFloats + lane * 34;
       const float m_o = other[32], l_o = other[33];
       const float m_new = fmaxf(m_run, m_o);
-      const float a_me = m_run == -INFINITY ? 0.0f : __expf(m_run - m_new);
-      const float a_o = m_o == -INFINITY ? 0.0f : __expf(m_o - m_new);
+      const float a_me = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      const float a_o = __builtin_amdgcn_exp2f((m_o - m_new) * c2);
       l_run = a_me * l_run + a_o * l_o;
       m_run = m_new;
       float am[4], ao[4];                                 // O rows are heads 4g+i
@@ -316,7 +324,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
         if (hd < h) out[((int64_t)qi * h + hd) * kLatent + 128 * ds + 16 * nt + r] = oacc[nt][i] * linv[i];
       }
     if (lse != nullptr && ds == 0 && g == 0 && head < h)
-      lse[(int64_t)qi * h + head] = (m_run == -INFINITY) ? -INFINITY : m_run + __logf(l_run);
+      lse[(int64_t)qi * h + head] = l_run > 0.0f ? m_run * sm_scale + __logf(l_run) : -INFINITY;
     return;
   }
   // share of a split unit: unnormalised output, running max and sum
@@ -327,7 +335,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
     for (int i = 0; i < 4; ++i)
       part_o[(pbase * 16 + 4 * g + i) * kLatent + 128 * ds + 16 * nt + r] = oacc[nt][i];
   if (ds == 0 && g == 0) {
-    part_ml[pbase * 32 + r] = m_run;
+    part_ml[pbase * 32 + r] = l_run > 0.0f ? m_run * sm_scale : -INFINITY;   // the combine works in scaled units
     part_ml[pbase * 32 + 16 + r] = l_run;
   }
 }
