@@ -62,7 +62,7 @@ constexpr int kHistBits = 11;                // first radix digit of the score k
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kScanChunk = 2048;             // entries per scan workgroup
 constexpr int kSelectThreads = 1024;
-constexpr int kTieCap = 12288;               // composite keys held in LDS by the select kernel
+constexpr int kTieCap = 4096;                // composite keys held in LDS by the select kernel (32 KB of LDS)
 constexpr int kCollectSlice = 8192;          // entries per candidate-collect workgroup
 
 int64_t index_vstride(int32_t max_vis);
