@@ -195,6 +195,34 @@ def time_hierarchical(dc, pool_k: int, steps: int):
             "entries_scored_per_query": {"exhaustive": int(spec.q_vis().max()), "pool": pool_k}}
 
 
+def measured_hbm_read(nbytes: int):
+    """Measured HBM read rates (GB/s) of a plain streaming-read kernel over
+    nbytes: warm (the same buffer every launch, as the timed region reads the
+    same indexer-K every step) and cold (successive slices of a buffer far
+    larger than the 256 MB last-level cache)."""
+    import torch
+
+    from fp4_kv_cache_layer_amd import probe
+
+    nb = (nbytes + 15) // 16 * 16
+    rot = 8
+    buf = torch.ones(rot * nb, dtype=torch.uint8, device="cuda")
+    warm = probe.stream_read_gbps(buf, nb, rotate=1)
+    cold = probe.stream_read_gbps(buf, nb, rotate=rot)
+    del buf
+    torch.cuda.empty_cache()
+    return warm, cold
+
+
+def measured_mfma_fp8():
+    """Measured dense FP8 MFMA rates (TFLOP/s): the bare instruction stream,
+    and the same stream with the indexer's minimal per-score epilogue (ReLU
+    and head-weight multiply-add per output, one add) sharing the SIMD."""
+    from fp4_kv_cache_layer_amd import probe
+
+    return probe.mfma_fp8_tflops(epilogue=False), probe.mfma_fp8_tflops(epilogue=True)
+
+
 def scan_source_hash() -> str:
     """Hash of the indexer-scan kernel source: a stored counter reading
     applies only to the kernel it was taken on."""
@@ -359,6 +387,7 @@ def bench_prefill(args, spec, dc) -> int:
     def avg(xs):
         return round(statistics.mean(xs) * 1e3, 2) if xs else None
 
+    mf_peak, mf_epi = measured_mfma_fp8()
     flops = dense_flops(spec)
     prod_avg_s = statistics.mean(prod_ms) / 1e3
     achieved = flops / prod_avg_s / 1e12
@@ -383,7 +412,12 @@ def bench_prefill(args, spec, dc) -> int:
                    "indexer_heads": spec.h_idx, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "prefill_scan_kernel", "achieved": round(achieved, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "flop_per_launch": flops, "avg_launch_us": round(prod_avg_s * 1e6, 2)},
+                     "traffic": None, "flop_per_launch": flops, "avg_launch_us": round(prod_avg_s * 1e6, 2),
+                     "peak_measured": round(mf_peak, 1), "frac_of_measured": round(achieved / mf_peak, 4),
+                     "measured_by": "csa2_probe_mfma_fp8: back-to-back 16x16x128 FP8 MFMAs, 4 waves per SIMD",
+                     "epilogue_ceiling": {"achieved": round(mf_epi, 1), "frac": round(mf_epi / FP8_PEAK_TFLOPS, 4),
+                                          "measured_by": "csa2_probe_mfma_fp8 with the per-score ReLU, "
+                                                         "head-weight fma and add beside each MFMA"}},
         "indexer_all_kernels": {"avg_us": round(index_s * 1e6, 2),
                                 "mfma_frac": round(flops / index_s / 1e12 / FP8_PEAK_TFLOPS, 4)},
         "attention": {"avg_us": round(attn_s * 1e6, 2), "bytes": ab,
@@ -534,6 +568,7 @@ def main() -> int:
     def avg(xs):
         return round(statistics.mean(xs) * 1e3, 2) if xs else None
 
+    hbm_warm, hbm_cold = measured_hbm_read(sbytes)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -554,7 +589,9 @@ def main() -> int:
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "index_scan_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": sbytes, "avg_launch_us": round(scan_avg * 1e3, 2)},
+                     "traffic": traffic, "bytes_per_launch": sbytes, "avg_launch_us": round(scan_avg * 1e3, 2),
+                     "peak_measured": round(hbm_warm, 1), "frac_of_measured": round(achieved / hbm_warm, 4),
+                     "measured_by": "csa2_probe_stream_read over the same byte count, same buffer every launch"},
         "kernels_avg_us": {"append": avg(dur[L.KCLASS_APPEND]), "scan_full": avg(dur[L.KCLASS_SCAN][0::n_scan]),
                            "scan_reindex": avg(dur[L.KCLASS_SCAN][1::n_scan]) if n_scan > 1 else None,
                            "select": avg(dur[L.KCLASS_SELECT]), "attn": avg(dur[L.KCLASS_ATTN])},
@@ -562,7 +599,10 @@ def main() -> int:
                            "scan_avg_us": avg(scrubbed_scan),
                            "scan_full_us": avg(scrubbed_scan[0::n_scan]),
                            "scan_reindex_us": avg(scrubbed_scan[1::n_scan]) if n_scan > 1 else None,
-                           "scan_frac": round(sbytes / (statistics.mean(scrubbed_scan) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+                           "scan_frac": round(sbytes / (statistics.mean(scrubbed_scan) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "stream_read_cold_GBps": round(hbm_cold, 1),
+                           "scan_frac_of_measured_cold": round(
+                               sbytes / (statistics.mean(scrubbed_scan) / 1e3) / 1e9 / hbm_cold, 4)},
         "ms_per_step_no_events": round(ms_plain, 5),
         "other_execution": {"execution": ("one csa2_layer_step call per layer" if aux else
                                           "csa2_group_step, Reuse attentions on 1 auxiliary stream"),

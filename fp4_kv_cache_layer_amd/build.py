@@ -1,4 +1,5 @@
-"""Builds libcsa2.so (gfx950) in-tree with hipcc.
+"""Builds libcsa2.so and the peak-probe library libcsa2_probe.so (gfx950)
+in-tree with hipcc.
 
     python -m fp4_kv_cache_layer_amd.build
 """
@@ -12,6 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
+PROBE_LIB = os.path.join(PKG, "libcsa2_probe.so")
+PROBE_SOURCE = "probe.hip"
 SOURCES = ["api.hip", "append_quant.hip", "index_scan.hip", "prefill_scan.hip", "topk_select.hip", "sparse_attn.hip",
            "lse_merge.hip", "fake_quant.hip", "pool_index.hip"]
 ARCH = "gfx950"
@@ -55,9 +58,12 @@ def _finish(proc, verbose: bool, what: str) -> None:
 
 def build(verbose: bool = False) -> str:
     """Compiles every HIP source (in parallel, each with its own flags) and
-    links them into one shared library; returns its path."""
+    links them into one shared library, plus the probe library; returns the
+    main library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    probe_tmp = PROBE_LIB + ".tmp"
+    probe = _run([hipcc(), *FLAGS, *inc, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp], verbose)
     objs, procs = [], []
     for s in SOURCES:
         obj = os.path.join(BUILD_DIR, s.replace(".hip", ".o"))
@@ -69,6 +75,8 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose), verbose, "link")
     os.replace(tmp, LIB)
+    _finish(probe, verbose, PROBE_SOURCE)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 

@@ -255,3 +255,23 @@ def test_layer_step_pool_field_rules():
     assert lib.csa2_layer_step(L.CSA2_REINDEX, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
     a.q_idx, a.w, a.h_idx, a.pool_cnt = None, None, 0, FAKE + 8192          # Reuse: no pool
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_probe_library_exports_and_rejects():
+    """The peak-probe library exports what its header declares and rejects
+    out-of-range arguments before launching anything."""
+    import re
+
+    from fp4_kv_cache_layer_amd import probe
+    lib = probe.load()
+    txt = re.sub(r"/\*.*?\*/", "", open(probe.HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(csa2_probe_[a-z0-9_]+)\s*\(", txt)))
+    assert names == ["csa2_probe_mfma_fp8", "csa2_probe_stream_read"]
+    for n in names:
+        assert hasattr(lib, n), n
+    invalid = 1                                   # hipErrorInvalidValue
+    for blocks, iters, epi in ((0, 4, 0), (1 << 21, 4, 0), (1, 0, 0), (1, 6, 0), (1, 4, 2)):
+        assert lib.csa2_probe_mfma_fp8(blocks, iters, epi, FAKE, None) == invalid
+    assert lib.csa2_probe_mfma_fp8(1, 4, 0, None, None) == invalid
+    for src, nbytes, blocks in ((FAKE, 0, 1), (FAKE, 24, 1), (FAKE + 8, 32, 1), (FAKE, 32, 0), (None, 32, 1)):
+        assert lib.csa2_probe_stream_read(src, nbytes, blocks, FAKE, None) == invalid
