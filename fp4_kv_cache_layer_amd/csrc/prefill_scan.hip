@@ -30,14 +30,15 @@
 //
 // Matrix product: A = the queries' indexer heads ([nq * h_idx] x 128 E4M3),
 // B = the sequence's indexer-K rows (128 x V E4M3).  A workgroup of 4 waves
-// owns 8 A tiles of 16 rows (QPT queries x 16/QPT heads each, held in
-// registers by every wave) and one chunk of entries, which its waves stream as
-// 16-entry B tiles straight into MFMA operands (V_MFMA_F32_16X16X128_F8F6F4:
-// lane l supplies row / entry l % 16 and 32 bytes of it, load_fp8_operand);
-// each B tile feeds 8 MFMAs.  Workgroups sharing a chunk run on the same XCD, so the
-// chunk's indexer-K stays in that XCD's L2.  Every score is the same fma
-// chain and cross-row add as in the per-query scan, so both produce
-// identical bits.
+// owns 8 A tiles of 16 query-head rows (16 queries in all; load_set_tile
+// gives the row order), held in registers by every wave, and one chunk of
+// entries, which its waves stream as 16-entry B tiles (loaded coalesced, put
+// into the V_MFMA_F32_16X16X128_F8F6F4 operand layout of load_fp8_operand
+// through a per-wave LDS slot); each B tile feeds 8 MFMAs.  Workgroups
+// sharing a chunk run on the same XCD, so the chunk's indexer-K stays in
+// that XCD's L2.  Every score is the same two four-head fma chains and the
+// same add of the two as in the per-query scan, so both produce identical
+// bits.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -88,11 +89,27 @@ __device__ __forceinline__ void load_a_tile(const uint8_t* q_idx, const float* w
   }
 }
 
-// Rows 0/1 and 2/3 exchange halves: row 0 gets x_row0 + x_row1, row 1 gets
-// y_row0 + y_row1, row 2 gets x_row2 + x_row3, row 3 gets y_row2 + y_row3.
-__device__ __forceinline__ float pair_rows2(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// A tile t of the candidate pass and the weights of its output rows 4g .. 4g+3.
+// QPT = 2 (at most 8 heads): output set p = t / 2 covers the four queries
+// qs .. qs+3 (qs = q0 + 4p); tile 2p carries heads 0..3 and tile 2p+1 heads
+// 4..7 of each (A row m: query qs + m / 4, head 4 * (t & 1) + m % 4), so
+// output rows 4g .. 4g+3 of the two tiles are all heads of query qs + g and
+// a lane's score is the sum of its two four-head partials, with no lane
+// exchange.  QPT = 1: tile t is query q0 + t, rows = heads.
+template <int QPT>
+__device__ __forceinline__ void load_set_tile(const uint8_t* q_idx, const float* w, int nq, int h_idx, int q0, int t,
+                                              int r, int g, intx8& a, float (&wv)[4]) {
+  if constexpr (QPT == 2) {
+    const int qs = q0 + 4 * (t >> 1), hb = 4 * (t & 1);
+    const int qa = qs + (r >> 2), ha = hb + (r & 3);
+    a = intx8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (qa < nq && ha < h_idx) a = load_fp8_operand(q_idx + ((int64_t)qa * h_idx + ha) * kIndexDim, g);
+    const int qw = qs + g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = (qw < nq && hb + i < h_idx) ? w[(int64_t)qw * h_idx + hb + i] : 0.0f;
+  } else {
+    load_a_tile<1>(q_idx, w, nq, h_idx, q0 + t, r, g, a, wv);
+  }
 }
 
 __device__ __forceinline__ float row16_max(float x) {
@@ -220,15 +237,14 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
 #pragma unroll
   for (int t = 0; t < kPfTiles; ++t) {
     float wv[4];
-    load_a_tile<QPT>(q_idx, w, nq, h_idx, q0 + QPT * t, r, g, a[t], wv);
+    load_set_tile<QPT>(q_idx, w, nq, h_idx, q0, t, r, g, a[t], wv);
     if (wave == 0 && r == 0) S.w[t][g] = make_float4(wv[0], wv[1], wv[2], wv[3]);
   }
   lds_barrier();
 
 
-  // After the head sums, output set p puts query ql(p, g) in lane row g:
-  //   QPT = 2: tiles 2p and 2p+1 -> ql = 4p + 2*(g & 1) + (g >> 1)
-  //   QPT = 1: tiles 4p .. 4p+3   -> ql = 4p + g
+  // After the head sums, output set p puts query ql = 4p + g in lane row g
+  // (QPT = 2: tiles 2p and 2p+1; QPT = 1: tiles 4p .. 4p+3).
   // Candidate masks: per (query block, set, 16-entry tile) one 64-bit word
   // whose bit 16g + r marks entry 16*tile + r of query ql(p, g).
   constexpr int kSets = kPfTiles * QPT / 4;
@@ -238,7 +254,7 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   uint64_t own_rows[kSets];                          // rows whose query this pass writes
 #pragma unroll
   for (int p = 0; p < kSets; ++p) {
-    const int ql = (QPT == 2) ? 4 * p + 2 * (g & 1) + (g >> 1) : 4 * p + g;
+    const int ql = 4 * p + g;
     const int qg = q0 + ql;
     const bool valid = qg < nq;
     const int v = valid ? q_vis[qg] : 0;
@@ -306,7 +322,9 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   for (int t = 0; t < kPfTiles; ++t) wreg[t] = S.w[t][g];
   auto finish = [&](int p, const floatx4 (&acc)[kPerSet]) {
     if (QPT == 2) {
-      return pair_rows2(relu_weighted4(acc[0], wreg[2 * p]), relu_weighted4(acc[1], wreg[2 * p + 1]));
+      // heads 0..3 + heads 4..7: the per-query scan adds the same two
+      // partials (across a lane pair), so the bits agree
+      return relu_weighted4(acc[0], wreg[2 * p]) + relu_weighted4(acc[1], wreg[2 * p + 1]);
     } else {
       float sq[4];
 #pragma unroll
@@ -401,7 +419,7 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
   if (tid == 0) total = 0;
   const int kq = kPfTiles * qpt, nsets = kPfTiles * qpt / 4;
   const int ql = q % kq, p = ql >> 2;
-  const int g = qpt == 2 ? (((ql & 1) << 1) | ((ql >> 1) & 1)) : (ql & 3);
+  const int g = ql & 3;
   const int64_t mtiles = ws.vstride >> 4;
   const uint64_t* mq = ws.mask + ((int64_t)(q / kq) * nsets + p) * mtiles;
   const float* sc = ws.scores + (int64_t)q * ws.vstride;
