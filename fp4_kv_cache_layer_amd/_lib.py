@@ -85,10 +85,11 @@ def load() -> ctypes.CDLL:
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_set_timing.argtypes = [c_int32, P(TimingRing)]
     lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
+    lib.csa2_set_attn_head_sharing.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_pool_index_topk", "csa2_sparse_attn",
                "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4", "csa2_set_timing",
-               "csa2_set_prefill_candidate_factor"):
+               "csa2_set_prefill_candidate_factor", "csa2_set_attn_head_sharing"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

@@ -347,6 +347,12 @@ csa2_status csa2_set_prefill_candidate_factor(int32_t factor) {
   return CSA2_OK;
 }
 
+csa2_status csa2_set_attn_head_sharing(int32_t enable) {
+  if (enable != 0 && enable != 1) return CSA2_ERR_INVALID_ARG;
+  g_attn_share_heads = enable;
+  return CSA2_OK;
+}
+
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
   (void)h_idx; (void)k;
   if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;

@@ -88,6 +88,9 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
 // Expected candidates per query of the dense indexer, in units of k (0 sends
 // every query through the full rescore).
 extern int g_prefill_cand_factor;
+// 1: large batches of 64-head queries take the attention form that shares
+// each gathered row among the 64 heads.
+extern int g_attn_share_heads;
 // Launches of the final select alone (the dense indexer compacts its own candidates).
 hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
                              int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});

@@ -97,7 +97,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   const int ds = wv & 3, rg = wv >> 2;                  // latent slice, row group
   const int g = lane >> 4, r = lane & 15;
   const int head = hg * 16 + r;
-  const int n_all = cnt[qi];
+  const int n_all = max(0, min(cnt[qi], k));            // counts outside [0, k] are clamped
   const int ntiles_all = (n_all + kTileRows - 1) / kTileRows;
   const int per_split = (ntiles_all + nsplit - 1) / nsplit;
   const int j0 = split * per_split * kTileRows;         // first selected row of this share
@@ -340,6 +340,202 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
   }
 }
 
+// Large batches (prefill): one workgroup of 16 waves serves the 64 heads of
+// a query (4 head groups of 16).  Wave (head group hg, slice ds) gathers and
+// dequantises 8 of the tile's 32 rows of slice ds into slice rows that the
+// four head groups share, so each selected row is fetched and converted once
+// per query instead of once per head group.  Per head group the arithmetic is
+// that of sparse_attn_kernel<1> (the same partial sums in the same order, the
+// same softmax and P split), so both forms give identical bits.  Slice rows
+// and partial-S tiles are double buffered: two barriers per tile.
+constexpr int kHg = 4;                                  // head groups per workgroup
+
+struct AttnHgShared {
+  uint8_t xs[2][4][kSliceBytes];     // [buffer][slice] bf16 slice rows of the tile (73,728 B)
+  floatx4 sp[2][kHg][4][2][4][16];   // [buffer][head group][slice]: partial S^T (65,536 B)
+  uint32_t row[kMaxShareRows];       // physical row of every selected entry (8,192 B)
+};
+
+__global__ void __launch_bounds__(256 * kHg, 1)
+sparse_attn_hg_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
+                      const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int h, int k,
+                      float sm_scale, float* __restrict__ out, float* __restrict__ lse, int nunits, int per_xcd) {
+  __shared__ AttnHgShared S;
+  // Block order: XCD x (blocks go to XCDs round-robin) serves the units
+  // x * per_xcd .. x * per_xcd + per_xcd - 1, so neighbouring queries, which
+  // select many of the same rows, share that XCD's L2.
+  const int b = blockIdx.x;
+  const int unit = (b & 7) * per_xcd + (b >> 3);         // (query, quad of head groups)
+  if (unit >= nunits) return;                            // uniform
+  const int nquads = h / (16 * kHg);
+  const int qi = unit / nquads, hq = unit - qi * nquads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ds = wv & 3, hgl = wv >> 2;                 // latent slice, head group within the quad
+  const int g = lane >> 4, r = lane & 15;
+  const int hg = hq * kHg + hgl;
+  const int head = hg * 16 + r;                          // < h: h is a multiple of 64
+  const int n = max(0, min(cnt[qi], k));                // counts outside [0, k] are clamped
+
+  // Q^T operand: head r, K-step s holds dims 128*ds + 32*g + 8*s .. +7.
+  bf16x8 qop[4];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)qi * h + head) * kLatent + 128 * ds + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8, src[s]);
+  }
+  const int ntiles = (n + kTileRows - 1) / kTileRows;
+  {
+    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
+    const int32_t* irow = idx + (int64_t)qi * k;
+    for (int j = tid; j < ntiles * kTileRows; j += 256 * kHg) {
+      const int t = irow[min(j, k - 1)];
+      if (j < n) S.row[j] = (uint32_t)entry_row(pt_row, t, c.lg_page);
+    }
+  }
+  lds_barrier();
+
+  floatx4 oacc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -FLT_MAX, l_run = 0.0f;
+  const float c2 = sm_scale * 1.44269504088896341f;
+  const float slack = kRescaleSlack / sm_scale;
+
+  // Ring of row gathers: lanes 8i .. 8i+7 read 8 code bytes each of row
+  // 8 * hgl + i's 64-byte segment of this slice, and the scale byte of their
+  // 32-value block.  Loads are unconditional (rows past the selection read
+  // physical row 0, which always exists).
+  const int grow = 8 * hgl + (lane >> 3), gpart = lane & 7;
+  uint2 cd[kPrefetch];
+  uint32_t sb[kPrefetch];
+  auto gather = [&](int tt, uint2& cw, uint32_t& sw) {
+    const int j = tt * kTileRows + grow;
+    const uint8_t* src = c.kv + (size_t)(j < n ? S.row[j] : 0u) * kKvRowBytes;
+    cw = *reinterpret_cast<const uint2*>(src + 64 * ds + 8 * gpart);
+    sw = src[kCodeBytes + 4 * ds + (gpart >> 1)];
+  };
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) gather(u, cd[u], sb[u]);
+
+  const int ntiles_pad = (ntiles + kPrefetch - 1) / kPrefetch * kPrefetch;
+  for (int t0 = 0; t0 < ntiles_pad; t0 += kPrefetch) {
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) {
+    const int tt = t0 + u;
+    const int buf = tt & 1;
+    const int lim = n - tt * kTileRows;                 // rows of this tile inside the selection
+    uint8_t* xs = &S.xs[buf][ds][0];
+    {
+      // a row past the selection keeps its (finite) codes but gets scale 1:
+      // its logit is masked below, so it only ever meets a zero probability
+      const float scale = e8m0_to_float(grow < lim ? sb[u] : 127u);
+      uint8_t* rowp = xs + grow * kSliceStride + 32 * gpart;
+      *reinterpret_cast<bf16x8*>(rowp) = dequant8(cd[u].x, scale);
+      *reinterpret_cast<bf16x8*>(rowp + 16) = dequant8(cd[u].y, scale);
+    }
+    gather(tt + kPrefetch, cd[u], sb[u]);
+    // the tile's slice rows are complete; the buffers of tile tt-2 were
+    // last read before every wave reached the previous tile's first barrier
+    lds_barrier();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint8_t* rowp = xs + (mt * 16 + r) * kSliceStride + 64 * g;
+      floatx4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(rowp + 16 * s), qop[s], st,
+                                                     0, 0, 0);
+      S.sp[buf][hgl][ds][mt][g][r] = st;
+    }
+    lds_barrier();
+    float v[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      floatx4 acc = S.sp[buf][hgl][0][mt][g][r];
+#pragma unroll
+      for (int d2 = 1; d2 < 4; ++d2) acc += S.sp[buf][hgl][d2][mt][g][r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[mt][i] = acc[i];
+    }
+    if (lim < kTileRows) {                              // uniform: only a tile holding the end of the selection
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (mt * 16 + 4 * g + i >= lim) v[mt][i] = -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
+                       fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
+    tmax = halves_max(rows_pair_max(tmax));
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + slack)) {
+      const float m_new = tmax > m_run + slack ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+      m_run = m_new;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
+    }
+    const float mc = -m_run * c2;
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[mt][i], c2, mc));
+        psum += p[mt][i];
+      }
+    psum = halves_sum(rows_pair_sum(psum));
+    l_run += psum;
+    uint32_t whi[4], wlo[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const float a = p[pr >> 1][2 * (pr & 1)], b2 = p[pr >> 1][2 * (pr & 1) + 1];
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{a, b2}), bf16x2));
+      const float ra = a - __uint_as_float(hi << 16), rb = b2 - __uint_as_float(hi & 0xFFFF0000u);
+      whi[pr] = hi;
+      wlo[pr] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{ra, rb}), bf16x2));
+    }
+    const bf16x8 pa_hi = __builtin_bit_cast(bf16x8, make_uint4(whi[0], whi[1], whi[2], whi[3]));
+    const bf16x8 pa_lo = __builtin_bit_cast(bf16x8, make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]));
+    const int off_a = (4 * g + (r >> 2)) * kSliceStride + 8 * (r & 3);
+    const int off_b = off_a + 16 * kSliceStride;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const shortx4 lo = lds_read_tr16(xs, off_a + 32 * nt);
+      const shortx4 hi = lds_read_tr16(xs, off_b + 32 * nt);
+      typedef short shortx8 __attribute__((ext_vector_type(8)));
+      const shortx8 b8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, b8);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb, oacc[nt], 0, 0, 0);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb, oacc[nt], 0, 0, 0);
+    }
+  }
+  }
+
+  float linv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float Li = __shfl(l_run, 4 * g + i);
+    linv[i] = Li > 0.0f ? 1.0f / Li : 0.0f;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hd = hg * 16 + 4 * g + i;
+      out[((int64_t)qi * h + hd) * kLatent + 128 * ds + 16 * nt + r] = oacc[nt][i] * linv[i];
+    }
+  if (lse != nullptr && ds == 0 && g == 0)
+    lse[(int64_t)qi * h + head] = l_run > 0.0f ? m_run * sm_scale + __logf(l_run) : -INFINITY;
+}
+
 // Merges the nsplit shares of one (query, head): O = sum_s e^(m_s - M) O_s / L,
 // L = sum_s e^(m_s - M) l_s, LSE = M + ln L.  One workgroup per head, one
 // float4 of the output per thread, so every share is read in one round trip.
@@ -370,6 +566,11 @@ attn_combine_kernel(int h, int nsplit, const float* __restrict__ part_o, const f
   reinterpret_cast<float4*>(out + ((int64_t)qi * h + hd) * kLatent)[tid] = acc;
   if (lse != nullptr && tid == 0) lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
 }
+
+int g_attn_share_heads = 1;
+// Shared-row workgroups (sparse_attn_hg_kernel) need a batch that gives every
+// CU a few of them; below that the 16-head form spreads the work wider.
+constexpr int64_t kHgMinUnits = 512;
 
 // Row groups per workgroup: small batches (decode) split each query's rows
 // among 2 row groups of 4 waves inside one workgroup, merged through LDS;
@@ -415,7 +616,12 @@ hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32
   float* part_ml = part_o ? part_o + units * ns * 16 * kLatent : nullptr;
   const int64_t npairs = (int64_t)nq * ns;
   const int64_t blocks = (npairs + 7) / 8 * 8 * ngroups;
-  if (attn_rgroups(nq, h) == 2)
+  const int64_t hg_units = (h % (16 * kHg) == 0) ? (int64_t)nq * (h / (16 * kHg)) : 0;
+  if (g_attn_share_heads && ns == 1 && hg_units >= kHgMinUnits) {
+    const int per_xcd = (int)((hg_units + 7) / 8);
+    launch(sparse_attn_hg_kernel, dim3((unsigned)(per_xcd * 8)), dim3(256 * kHg), s, ev, c, q, q_seq, idx, cnt, h, k,
+           sm_scale, out, lse, (int)hg_units, per_xcd);
+  } else if (attn_rgroups(nq, h) == 2)
     launch(sparse_attn_kernel<2>, dim3((unsigned)blocks), dim3(256 * 2), s, ns > 1 ? ev.first() : ev, c, q, q_seq,
            idx, cnt, h, k, sm_scale, out, lse, ns, (int)npairs, part_o, part_ml);
   else

@@ -169,6 +169,10 @@ def csa2_set_prefill_candidate_factor(factor: int) -> None:
     L.check("csa2_set_prefill_candidate_factor", L.load().csa2_set_prefill_candidate_factor(int(factor)))
 
 
+def csa2_set_attn_head_sharing(enable: bool) -> None:
+    L.check("csa2_set_attn_head_sharing", L.load().csa2_set_attn_head_sharing(int(enable)))
+
+
 class LayerCall:
     """Prepared arguments of one csa2_layer_step call (pointers fixed at
     construction, so repeated launches cost one ctypes call each)."""

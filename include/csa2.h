@@ -172,9 +172,19 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
  * meant for tuning and tests.  Returns CSA2_ERR_INVALID_ARG outside [0, 64]. */
 csa2_status csa2_set_prefill_candidate_factor(int32_t factor);
 
+/* Form of sparse attention for large batches (h a multiple of 64, at least
+ * 512 (query, 64-head) units, unsplit): enable = 1 (default) serves the 64
+ * heads of a query in one workgroup that gathers and dequantises each
+ * selected row once for all of them; 0 keeps one workgroup per 16-head
+ * group, which gathers the row once per group.  Both forms give identical
+ * bits.  Process-wide, not thread-safe: meant for tests and measurement.
+ * Returns CSA2_ERR_INVALID_ARG unless enable is 0 or 1. */
+csa2_status csa2_set_attn_head_sharing(int32_t enable);
+
 /* Sparse attention over the selected rows (all three modes end here).
  *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
- *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq],
+ *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq]
+ *   (a count outside [0, k] is taken as the nearest bound),
  *   out [nq][h][512] fp32, lse [nq][h] fp32 (nullable).
  * 1 <= h <= 128; sm_scale > 0 and finite.  ws may be NULL; with a
  * workspace of csa2_workspace_bytes(CSA2_REUSE, nq, 0, 1, h, k) bytes, small

@@ -133,6 +133,14 @@ def test_prefill_candidate_factor_range():
     assert lib.csa2_set_prefill_candidate_factor(4) == L.CSA2_OK
 
 
+def test_attn_head_sharing_switch():
+    lib = L.load()
+    for bad in (-1, 2, 7):
+        assert lib.csa2_set_attn_head_sharing(bad) == L.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_set_attn_head_sharing(0) == L.CSA2_OK
+    assert lib.csa2_set_attn_head_sharing(1) == L.CSA2_OK
+
+
 def test_set_timing_validation():
     lib = L.load()
     assert lib.csa2_set_timing(9, None) == L.CSA2_ERR_INVALID_ARG

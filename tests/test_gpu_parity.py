@@ -284,6 +284,59 @@ def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
 # attention alone, on chosen selections
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("nq,h,k", [(523, 64, 512), (300, 128, 512), (520, 64, 2048)])
+def test_sparse_attn_large_batch_shared_rows(nq, h, k):
+    """Large batches take the form that gathers each selected row once for
+    all 64 heads of a query: identical bits to the one-workgroup-per-16-heads
+    form on every query, and the oracle's result on sampled queries (counts
+    0, 1, 31..33, k and one above k, which counts as k)."""
+    ops, _ = _ops()
+    say(f"[attn-shared] nq={nq} h={h} k={k}")
+    rng = np.random.default_rng(nq + h + k)
+    n, ps = 5000, 64
+    npg = (n + ps - 1) // ps
+    perm = rng.permutation(npg).astype(np.int32)
+    cache = ops.Cache(npg, ps, torch.from_numpy(perm[None]))
+    ocache = O.Cache.empty(npg, ps, perm[None], [n])
+    kv = (rng.standard_normal((n, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kv[5] = 0
+    ik = np.zeros((n, 128), dtype=np.uint16)
+    t = np.arange(n)
+    slots = (perm[t // ps].astype(np.int64) * ps + t % ps).astype(np.int32)
+    ops.csa2_append_quant_fp4(cache, torch.from_numpy(slots).cuda(), torch.from_numpy(kv.view(np.int16)).cuda(),
+                              torch.from_numpy(ik.view(np.int16)).cuda())
+    O.append_quant_fp4(ocache, slots, kv, ik)
+    cnts = rng.integers(0, k + 1, nq).astype(np.int32)
+    cnts[:7] = [0, 1, 31, 32, 33, k, k + 5]
+    idx = np.full((nq, k), -1, dtype=np.int32)
+    for i, c in enumerate(cnts):
+        c = min(int(c), k)
+        idx[i, :c] = np.sort(rng.choice(n, c, replace=False))
+    q = (rng.standard_normal((nq, h, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q_seq = np.zeros(nq, dtype=np.int32)
+    args = (cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda(),
+            torch.from_numpy(idx).cuda(), torch.from_numpy(cnts).cuda(), 1 / np.sqrt(512))
+    try:
+        ops.csa2_set_attn_head_sharing(False)
+        out0, lse0 = (x.cpu().numpy() for x in ops.csa2_sparse_attn(*args))
+        ops.csa2_set_attn_head_sharing(True)
+        out1, lse1 = (x.cpu().numpy() for x in ops.csa2_sparse_attn(*args))
+    finally:
+        ops.csa2_set_attn_head_sharing(True)
+    assert np.array_equal(out0.view(np.uint32), out1.view(np.uint32))
+    assert np.array_equal(lse0.view(np.uint32), lse1.view(np.uint32))
+    sample = [0, 1, 2, 3, 4, 5, 6, nq // 2, nq - 1]
+    o_ref, lse_ref = O.sparse_attn(ocache, q[sample], q_seq[sample], idx[sample],
+                                   np.minimum(cnts[sample], k), 1 / np.sqrt(512))
+    err = np.abs(out1[sample] - o_ref).max()
+    say(f"  max|dO| {err:.2e}")
+    assert err <= OUT_ATOL
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse1[sample]), fin)
+    assert (np.abs(lse1[sample][fin] - lse_ref[fin]) <= LSE_RTOL * np.maximum(1, np.abs(lse_ref[fin]))).all()
+    assert (out1[0] == 0).all()
+
+
 @pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("h,cnts", [(16, [0, 1, 2, 3, 17, 512]), (64, [512, 300, 2]), (40, [33, 512]), (128, [511, 5])])
 def test_sparse_attn_given_selection(h, cnts, with_ws):
