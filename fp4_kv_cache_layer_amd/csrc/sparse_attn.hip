@@ -10,8 +10,9 @@
 // Compression", Introduction: near-constant decode FLOPs from 4K to 1M).
 //
 // Work split.  A workgroup serves one (query, group of 16 heads) unit, or a
-// share of its selected rows; large batches of 64-head queries instead give
-// each query one workgroup for all its heads (sparse_attn_hg_kernel below).  Its waves form RG row groups of four: the four
+// share of its selected rows (large batches of 64-head queries instead give
+// each query one workgroup for all its heads: sparse_attn_hg_kernel below).
+// Its waves form RG row groups of four: the four
 // waves of a row group own the four 128-wide slices of the latent, and row
 // group g takes tiles g, g + RG, ...; at the end row groups merge their
 // (output, running max, running sum) through LDS.  Small decode batches use
