@@ -223,11 +223,27 @@ def measured_mfma_fp8():
     return probe.mfma_fp8_tflops(epilogue=False), probe.mfma_fp8_tflops(epilogue=True)
 
 
-def scan_source_hash() -> str:
-    """Hash of the indexer-scan kernel source: a stored counter reading
-    applies only to the kernel it was taken on."""
-    src = os.path.join(ROOT, "fp4_kv_cache_layer_amd", "csrc", "index_scan.hip")
+def source_hash(name: str) -> str:
+    """Hash of a kernel source file: a stored counter reading applies only to
+    the kernel it was taken on."""
+    src = os.path.join(ROOT, "fp4_kv_cache_layer_amd", "csrc", name)
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def scan_source_hash() -> str:
+    return source_hash("index_scan.hip")
+
+
+def stored_traffic(path: str, workload: str, src_name: str):
+    """HBM bytes per launch from a stored rocprofv3 FETCH_SIZE/WRITE_SIZE
+    reading, or None when it is missing or was taken on other source."""
+    try:
+        tr = json.load(open(path))
+        if tr.get("workload") == workload and tr.get("kernel_source_sha256_16") == source_hash(src_name):
+            return tr.get("bytes_per_launch")
+    except Exception:
+        pass
+    return None
 
 
 COPY_BYTES = 1 << 30
@@ -412,7 +428,9 @@ def bench_prefill(args, spec, dc) -> int:
                    "indexer_heads": spec.h_idx, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "prefill_scan_kernel", "achieved": round(achieved, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "flop_per_launch": flops, "avg_launch_us": round(prod_avg_s * 1e6, 2),
+                     "traffic": stored_traffic(os.path.join(ROOT, "profiles", "prefill_scan_traffic.json"), spec.name,
+                                               "prefill_scan.hip"),
+                     "flop_per_launch": flops, "avg_launch_us": round(prod_avg_s * 1e6, 2),
                      "peak_measured": round(mf_peak, 1), "frac_of_measured": round(achieved / mf_peak, 4),
                      "measured_by": "csa2_probe_mfma_fp8: back-to-back 16x16x128 FP8 MFMAs, 4 waves per SIMD",
                      "epilogue_ceiling": {"achieved": round(mf_epi, 1), "frac": round(mf_epi / FP8_PEAK_TFLOPS, 4),
@@ -556,14 +574,7 @@ def main() -> int:
     scan_avg = statistics.mean(scan_ms)
     sbytes = scan_bytes(spec)
     achieved = sbytes / (scan_avg / 1e3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic):
-        try:
-            tr = json.load(open(args.traffic))
-            if tr.get("workload") == spec.name and tr.get("kernel_source_sha256_16") == scan_source_hash():
-                traffic = tr.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = stored_traffic(args.traffic, spec.name, "index_scan.hip")
 
     def avg(xs):
         return round(statistics.mean(xs) * 1e3, 2) if xs else None
