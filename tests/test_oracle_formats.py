@@ -196,3 +196,37 @@ def test_idxk_row_is_elementwise_e4m3():
     b = O.quantize_idxk_rows(x)
     assert b.shape == (5, 128)
     assert np.array_equal(O.e4m3fn_decode(b), x)
+
+
+def test_bf16_decode_matches_torch_every_pattern():
+    """bf16_to_f64 against torch's own bfloat16 -> float64 conversion on all
+    65,536 bit patterns: values equal, NaN at the same positions, sign bits
+    equal (so -0 stays -0)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_to_f64(bits)
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == want[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(want[~nan])).all()
+    assert nan.sum() == 2 * 127                     # exponent 0xFF with a nonzero mantissa, both signs
+
+
+def test_bf16_decode_closed_forms():
+    """bf16 is fp32's top half: sign, 8 exponent bits (bias 127), 7 mantissa
+    bits; exponent 0 is subnormal (m * 2^-133), exponent 0xFF with m = 0 is
+    infinity.  Spot values written from that definition, not from the oracle."""
+    cases = {0x0000: 0.0, 0x8000: -0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC040: -3.0,
+             0x3F00: 0.5, 0x3FC0: 1.5, 0x4120: 10.0, 0x0001: 2.0 ** -133, 0x807F: -127 * 2.0 ** -133,
+             0x0080: 2.0 ** -126, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: np.inf, 0xFF80: -np.inf,
+             0x3E00: 0.125, 0x42F6: 123.0}
+    for b, v in cases.items():
+        got = float(O.bf16_to_f64(np.array([b], dtype=np.uint16))[0])
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(b), got, v)
+    # every normal pattern against the bit-field formula, in exact Python integers
+    for b in range(0, 1 << 16, 97):
+        s, e, m = b >> 15, (b >> 7) & 0xFF, b & 0x7F
+        if e == 0xFF:
+            continue
+        mag = m * 2.0 ** -133 if e == 0 else (128 + m) * 2.0 ** (e - 134)
+        assert float(O.bf16_to_f64(np.array([b], dtype=np.uint16))[0]) == (-mag if s else mag), hex(b)
