@@ -13,16 +13,27 @@ c_int32, c_void_p, c_float, c_size_t = ctypes.c_int32, ctypes.c_void_p, ctypes.c
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, 1, 2, 3, 4
 CSA2_FULL, CSA2_REINDEX, CSA2_REUSE = 0, 1, 2
-KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE, KCLASS_MERGE, KCLASS_QUANT = 0, 1, 2, 3, 4, 5, 6
-KCLASS_POOL_SCAN, KCLASS_POOL_SELECT = 7, 8
+KCLASS_APPEND, KCLASS_SCAN, KCLASS_SELECT, KCLASS_ATTN, KCLASS_DENSE = 0, 1, 2, 3, 4
+KCLASS_POOL_SCAN, KCLASS_POOL_SELECT = 5, 6
+NUM_KCLASSES = 7
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
-STEP_DENSE_INDEX, STEP_POOL = 1, 2
+STEP_DENSE_INDEX, STEP_POOL, STEP_ATTN_PER_HEAD_GROUP = 1, 2, 4
+DENSE_RESCORE_ALL = -1
 
 
 class CacheView(ctypes.Structure):
     _fields_ = [("kv", c_void_p), ("idx_k", c_void_p), ("page_table", c_void_p), ("seq_lens", c_void_p),
                 ("num_pages", c_int32), ("page_size", c_int32), ("num_seqs", c_int32), ("max_pages", c_int32)]
+
+
+class TimingRing(ctypes.Structure):
+    _fields_ = [("start", ctypes.POINTER(c_void_p)), ("stop", ctypes.POINTER(c_void_p)),
+                ("capacity", c_int32), ("count", c_int32)]
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("ring", ctypes.POINTER(TimingRing) * NUM_KCLASSES)]
 
 
 class StepArgs(ctypes.Structure):
@@ -33,7 +44,8 @@ class StepArgs(ctypes.Structure):
                 ("q_seq", c_void_p), ("q_vis", c_void_p), ("nq", c_int32), ("k", c_int32), ("max_vis", c_int32),
                 ("idx", c_void_p), ("cnt", c_void_p), ("out", c_void_p), ("lse", c_void_p),
                 ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32),
-                ("pool", c_void_p), ("pool_cnt", c_void_p), ("pool_k", c_int32)]
+                ("pool", c_void_p), ("pool_cnt", c_void_p), ("pool_k", c_int32),
+                ("dense_cand_factor", c_int32), ("timing", ctypes.POINTER(Timing))]
 
 
 GROUP_MAX_LAYERS, GROUP_MAX_AUX = 64, 4
@@ -42,11 +54,6 @@ GROUP_MAX_LAYERS, GROUP_MAX_AUX = 64, 4
 class GroupExec(ctypes.Structure):
     _fields_ = [("aux", c_void_p * GROUP_MAX_AUX), ("n_aux", c_int32),
                 ("events", ctypes.POINTER(c_void_p)), ("n_events", c_int32)]
-
-
-class TimingRing(ctypes.Structure):
-    _fields_ = [("start", ctypes.POINTER(c_void_p)), ("stop", ctypes.POINTER(c_void_p)),
-                ("capacity", c_int32), ("count", c_int32)]
 
 
 _lib = None
@@ -83,13 +90,9 @@ def load() -> ctypes.CDLL:
     lib.csa2_group_step.argtypes = [c_int32, P(c_int32), P(StepArgs), c_void_p, P(GroupExec)]
     lib.csa2_status_string.argtypes = [c_int32]
     lib.csa2_status_string.restype = ctypes.c_char_p
-    lib.csa2_set_timing.argtypes = [c_int32, P(TimingRing)]
-    lib.csa2_set_prefill_candidate_factor.argtypes = [c_int32]
-    lib.csa2_set_attn_head_sharing.argtypes = [c_int32]
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_pool_index_topk", "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4", "csa2_set_timing",
-               "csa2_set_prefill_candidate_factor", "csa2_set_attn_head_sharing"):
+               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

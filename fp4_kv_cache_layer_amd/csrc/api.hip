@@ -11,16 +11,14 @@ using namespace csa2;
 
 namespace {
 
-csa2_timing_ring* g_rings[CSA2_NUM_KCLASSES] = {};
-
-// Takes the next slot of a kernel class's timing ring, if one is installed;
-// the launch records the slot's events as part of its dispatches.
+// Takes the next slot of a kernel class's timing ring, if the call carries
+// one; the launch records the slot's events as part of its dispatches.
 struct TimedLaunch {
   csa2_timing_ring* ring;
   int slot;
   KEvents ev;
-  explicit TimedLaunch(int cls) : ring(g_rings[cls]), slot(-1) {
-    if (ring && ring->count < ring->capacity) {
+  TimedLaunch(const csa2_timing* tm, int cls) : ring(tm ? tm->ring[cls] : nullptr), slot(-1) {
+    if (ring && ring->start && ring->stop && ring->count >= 0 && ring->count < ring->capacity) {
       slot = ring->count;
       ev.start = ring->start[slot];
       ev.stop = ring->stop[slot];
@@ -52,6 +50,7 @@ csa2_status check_cache(const csa2_cache_view* c, CacheArgs* out) {
   out->page_table = c->page_table;
   out->max_pages = c->max_pages;
   out->lg_page = lg;
+  out->num_pages = c->num_pages;
   return CSA2_OK;
 }
 
@@ -103,6 +102,7 @@ csa2_status validate_append(const csa2_cache_view* c, const int32_t* slots, cons
 
 IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   IndexWs r;
+  r.vis_cap = max_vis;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   r.hist = reinterpret_cast<uint32_t*>(p);
   r.cand_cnt = reinterpret_cast<uint32_t*>(p + (size_t)nq * kHistBins * 4);
@@ -128,21 +128,17 @@ csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w,
   if (dense) {
     // the dense indexer leaves a compacted candidate list: only the final select remains
     if (max_vis > 0) {
-      TimedLaunch t(CSA2_KCLASS_SCAN), tp(CSA2_KCLASS_DENSE);
-      csa2_status st =
-          hip_status(launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, s, t.ev, tp.ev));
+      csa2_status st = hip_status(
+          launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, kDefaultCandFactor, s));
       if (st != CSA2_OK) return st;
     }
-    TimedLaunch t(CSA2_KCLASS_SELECT);
-    return hip_status(launch_topk_final(iw, q_vis, nq, k, out_idx, out_cnt, s, t.ev));
+    return hip_status(launch_topk_final(iw, q_vis, nq, k, out_idx, out_cnt, s));
   }
   if (max_vis > 0) {
-    TimedLaunch t(CSA2_KCLASS_SCAN);
-    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s, t.ev));
+    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s));
     if (st != CSA2_OK) return st;
   }
-  TimedLaunch t(CSA2_KCLASS_SELECT);
-  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s, t.ev));
+  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s));
 }
 
 // One layer of a step, validated, split into the stages that the group
@@ -153,6 +149,9 @@ struct Step {
   CacheArgs ca;
   bool dense;
   bool pool;                 // hierarchical indexer (Full: writes the pool; Reindex: reads it)
+  bool share_heads;          // attention: shared-row form for large 64-head batches
+  int cand_factor;           // dense indexer candidate factor
+  const csa2_timing* tm;     // nullable
   IndexWs iw;
   float* pool_sc;            // pool scores, in the workspace's score region
   void* part;
@@ -171,7 +170,12 @@ csa2_status validate_pool(const int32_t* pool, const int32_t* pool_cnt, int32_t 
 // Every check of csa2_layer_step, before anything is launched.
 csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
   if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
-  if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL)) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL | CSA2_STEP_ATTN_PER_HEAD_GROUP)) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & CSA2_STEP_DENSE_INDEX) {
+    if (a->dense_cand_factor < CSA2_DENSE_RESCORE_ALL || a->dense_cand_factor > 64) return CSA2_ERR_INVALID_ARG;
+  } else if (a->dense_cand_factor != 0) {
+    return CSA2_ERR_INVALID_ARG;
+  }
   const bool pool = (a->flags & CSA2_STEP_POOL) != 0;
   if (pool) {
     if (mode == CSA2_REUSE || a->pool_k < a->k) return CSA2_ERR_INVALID_ARG;
@@ -204,6 +208,10 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
   p->a = a;
   p->dense = (a->flags & CSA2_STEP_DENSE_INDEX) != 0;
   p->pool = pool;
+  p->share_heads = (a->flags & CSA2_STEP_ATTN_PER_HEAD_GROUP) == 0;
+  p->cand_factor = a->dense_cand_factor == 0 ? kDefaultCandFactor
+                   : a->dense_cand_factor == CSA2_DENSE_RESCORE_ALL ? 0 : a->dense_cand_factor;
+  p->tm = a->timing;
   p->iw = IndexWs{};
   p->pool_sc = nullptr;
   p->part = nullptr;
@@ -225,7 +233,7 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
 csa2_status stage_append(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (p.mode != CSA2_FULL || a->n_new == 0) return CSA2_OK;
-  TimedLaunch t(CSA2_KCLASS_APPEND);
+  TimedLaunch t(p.tm, CSA2_KCLASS_APPEND);
   return hip_status(launch_append_quant(p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
 }
 
@@ -234,18 +242,19 @@ csa2_status stage_scan(const Step& p, hipStream_t s) {
   if (p.mode == CSA2_REUSE || a->nq == 0 || a->max_vis == 0) return CSA2_OK;
   if (p.pool && p.mode == CSA2_REINDEX) return CSA2_OK;     // the pool is scored in stage_select
   if (p.dense) {
-    TimedLaunch t(CSA2_KCLASS_SCAN), tp(CSA2_KCLASS_DENSE);
+    TimedLaunch t(p.tm, CSA2_KCLASS_SCAN), tp(p.tm, CSA2_KCLASS_DENSE);
     return hip_status(launch_prefill_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx,
-                                          p.pool ? a->pool_k : a->k, a->max_vis, p.iw, s, t.ev, tp.ev));
+                                          p.pool ? a->pool_k : a->k, a->max_vis, p.iw, p.cand_factor, s, t.ev,
+                                          tp.ev));
   }
-  TimedLaunch t(CSA2_KCLASS_SCAN);
+  TimedLaunch t(p.tm, CSA2_KCLASS_SCAN);
   return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->max_vis, p.iw, s,
                                       t.ev));
 }
 
 csa2_status run_pool(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
-  TimedLaunch ts(CSA2_KCLASS_POOL_SCAN), tl(CSA2_KCLASS_POOL_SELECT);
+  TimedLaunch ts(p.tm, CSA2_KCLASS_POOL_SCAN), tl(p.tm, CSA2_KCLASS_POOL_SELECT);
   return hip_status(launch_pool_index(p.ca, a->q_idx, a->w, a->q_seq, a->pool, a->pool_cnt, a->nq, a->h_idx,
                                       a->pool_k, a->k, a->idx, a->cnt, p.pool_sc, s, ts.ev, tl.ev));
 }
@@ -264,13 +273,13 @@ csa2_status stage_select(const Step& p, hipStream_t s) {
   const int32_t k = to_pool ? a->pool_k : a->k;
   csa2_status st;
   {
-    TimedLaunch t(CSA2_KCLASS_SELECT);
+    TimedLaunch t(p.tm, CSA2_KCLASS_SELECT);
     st = p.dense ? hip_status(launch_topk_final(p.iw, a->q_vis, a->nq, k, idx, cnt, s, t.ev))
                  : hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, k, a->max_vis, idx, cnt, s, t.ev));
   }
   if (st != CSA2_OK || !to_pool) return st;
   if (p.dense) return run_pool(p, s);         // the dense indexer keeps candidate scores only: rescore the pool
-  TimedLaunch t(CSA2_KCLASS_POOL_SELECT);     // every visible entry's score is in the workspace
+  TimedLaunch t(p.tm, CSA2_KCLASS_POOL_SELECT);   // every visible entry's score is in the workspace
   return hip_status(launch_pool_select_by_entry(a->pool, a->pool_cnt, a->nq, a->pool_k, p.iw.scores, p.iw.vstride,
                                                 a->k, a->idx, a->cnt, s, t.ev));
 }
@@ -278,9 +287,9 @@ csa2_status stage_select(const Step& p, hipStream_t s) {
 csa2_status stage_attn(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (a->nq == 0) return CSA2_OK;
-  TimedLaunch t(CSA2_KCLASS_ATTN);
+  TimedLaunch t(p.tm, CSA2_KCLASS_ATTN);
   return hip_status(launch_sparse_attn(p.ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
-                                       a->lse, p.part, s, t.ev));
+                                       a->lse, p.part, p.share_heads, s, t.ev));
 }
 
 csa2_status run_step(const Step& p, hipStream_t s) {
@@ -333,26 +342,6 @@ const char* csa2_status_string(csa2_status st) {
   return "unknown status";
 }
 
-csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring) {
-  if (kernel_class < 0 || kernel_class >= CSA2_NUM_KCLASSES) return CSA2_ERR_INVALID_ARG;
-  if (ring && (ring->capacity < 0 || (ring->capacity > 0 && (!ring->start || !ring->stop))))
-    return CSA2_ERR_INVALID_ARG;
-  g_rings[kernel_class] = ring;
-  return CSA2_OK;
-}
-
-csa2_status csa2_set_prefill_candidate_factor(int32_t factor) {
-  if (factor < 0 || factor > 64) return CSA2_ERR_INVALID_ARG;
-  g_prefill_cand_factor = factor;
-  return CSA2_OK;
-}
-
-csa2_status csa2_set_attn_head_sharing(int32_t enable) {
-  if (enable != 0 && enable != 1) return CSA2_ERR_INVALID_ARG;
-  g_attn_share_heads = enable;
-  return CSA2_OK;
-}
-
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
   (void)h_idx; (void)k;
   if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;
@@ -377,8 +366,7 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
   CacheArgs ca;
   csa2_status st = validate_append(c, slots, kv_rows, idxk_rows, n, &ca);
   if (st != CSA2_OK || n == 0) return st;
-  TimedLaunch t(CSA2_KCLASS_APPEND);
-  return hip_status(launch_append_quant(ca.kv, ca.idx_k, slots, kv_rows, idxk_rows, n, s, t.ev));
+  return hip_status(launch_append_quant(ca.kv, ca.idx_k, slots, kv_rows, idxk_rows, n, s));
 }
 
 csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
@@ -414,9 +402,8 @@ csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx,
   if (!q_idx || !w || !q_seq || !ws) return CSA2_ERR_INVALID_ARG;
   if (!aligned(q_idx, 16) || !aligned(w, 4) || !aligned(q_seq, 4) || !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
   if (ws_bytes < pool_score_bytes(nq, p)) return CSA2_ERR_WORKSPACE;
-  TimedLaunch ts(CSA2_KCLASS_POOL_SCAN), tl(CSA2_KCLASS_POOL_SELECT);
   return hip_status(launch_pool_index(ca, q_idx, w, q_seq, pool, pool_cnt, nq, h_idx, p, k, out_idx, out_cnt,
-                                     reinterpret_cast<float*>(ws), s, ts.ev, tl.ev));
+                                     reinterpret_cast<float*>(ws), s));
 }
 
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
@@ -426,9 +413,8 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
   csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   if (ws && !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
-  TimedLaunch t(CSA2_KCLASS_ATTN);
   return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse,
-                                       attn_part(ws, ws_bytes, nq, h, k), s, t.ev));
+                                       attn_part(ws, ws_bytes, nq, h, k), true, s));
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
@@ -447,16 +433,14 @@ csa2_status csa2_lse_merge(const float* o_a, const float* lse_a, const float* o_
       (lse && !aligned(lse, 4)))
     return CSA2_ERR_INVALID_ARG;
   if (lse && (lse == lse_a || lse == lse_b)) return CSA2_ERR_INVALID_ARG;
-  TimedLaunch t(CSA2_KCLASS_MERGE);
-  return hip_status(launch_lse_merge(o_a, lse_a, o_b, lse_b, rows, dim, o, lse, s, t.ev));
+  return hip_status(launch_lse_merge(o_a, lse_a, o_b, lse_b, rows, dim, o, lse, s));
 }
 
 csa2_status csa2_fake_quant_fp4(const void* x, void* y, int64_t n, int32_t dtype, hipStream_t s) {
   if (n < 0 || n % 32 != 0 || (dtype != CSA2_DTYPE_F32 && dtype != CSA2_DTYPE_BF16)) return CSA2_ERR_INVALID_ARG;
   if (n == 0) return CSA2_OK;
   if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return CSA2_ERR_INVALID_ARG;
-  TimedLaunch t(CSA2_KCLASS_QUANT);
-  return hip_status(launch_fake_quant(x, y, n, dtype == CSA2_DTYPE_BF16, s, t.ev));
+  return hip_status(launch_fake_quant(x, y, n, dtype == CSA2_DTYPE_BF16, s));
 }
 
 int32_t csa2_group_events(int32_t n_layers, int32_t n_aux) {

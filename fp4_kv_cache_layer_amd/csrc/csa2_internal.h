@@ -14,7 +14,22 @@ struct CacheArgs {
   const int32_t* page_table;
   int32_t max_pages;
   int32_t lg_page;       // log2(page_size)
+  int32_t num_pages;
 };
+
+// Page id read from the page table, clamped to the cache's pages.
+__device__ __forceinline__ int clamp_page(int page, const CacheArgs& c) {
+  return min(max(page, 0), c.num_pages - 1);
+}
+
+// Physical row of logical entry t of a sequence (page-table row pt_row), with
+// t clamped to the table's range and the page id to the cache's pages, so a
+// bad index reads some row of the cache rather than stray memory.
+__device__ __forceinline__ int64_t entry_row_clamped(const int32_t* __restrict__ pt_row, int t, const CacheArgs& c) {
+  t = min(max(t, 0), (c.max_pages << c.lg_page) - 1);
+  const int page = clamp_page(pt_row[t >> c.lg_page], c);
+  return ((int64_t)page << c.lg_page) + (t & ((1 << c.lg_page) - 1));
+}
 
 // Workspace of the indexer (byte offsets):
 //   [0, Z)      zero-state: histograms [nq][2048] u32, then candidate
@@ -32,7 +47,11 @@ struct IndexWs {
   uint32_t* ckey;        // score key of cand[i], stored beside it (the final select reads no scores)
   uint64_t* mask;
   int64_t vstride;
+  int32_t vis_cap;       // max_vis of the call: visible counts are clamped to it
 };
+
+// A query's visible count as the indexer kernels use it: clamped to [0, max_vis].
+__device__ __forceinline__ int clamp_vis(int v, const IndexWs& ws) { return min(max(v, 0), ws.vis_cap); }
 
 // Optional device timestamps of one launch class: `start` is taken when its
 // first kernel starts, `stop` when its last kernel ends (recorded by the
@@ -82,15 +101,13 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
 // the candidates), with scores bit-identical to the per-query scan.  ev covers
 // the threshold, candidate, full-rescore and compaction kernels, ev_product
 // the candidate (matrix-product) kernel alone.
+// cand_factor: expected candidates per query in units of k (0 sends every
+// query through the full rescore).
+constexpr int kDefaultCandFactor = 4;
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                               hipStream_t s, const KEvents& ev = {}, const KEvents& ev_product = {});
-// Expected candidates per query of the dense indexer, in units of k (0 sends
-// every query through the full rescore).
-extern int g_prefill_cand_factor;
-// 1: large batches of 64-head queries take the attention form that shares
-// each gathered row among the 64 heads.
-extern int g_attn_share_heads;
+                               int cand_factor, hipStream_t s, const KEvents& ev = {},
+                               const KEvents& ev_product = {});
 // Launches of the final select alone (the dense indexer compacts its own candidates).
 hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
                              int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
@@ -104,9 +121,11 @@ hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, i
 int attn_nsplit(int nq, int h, int k);
 size_t attn_part_bytes(int nq, int h, int k);
 
+// share_heads: large batches of 64-head queries take the form that gathers
+// each selected row once for all 64 heads of a query (identical bits).
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, hipStream_t s, const KEvents& ev = {});
+                              void* part, bool share_heads, hipStream_t s, const KEvents& ev = {});
 
 // Hierarchical indexer: scores of each query's pool entries only (pool
 // [nq][p] ascending entry indices, pool_cnt valid; scores [nq][round_up(p, 64)]

@@ -47,7 +47,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   // a grid larger than one round leaves only short work for the second round
   const int chunk = blockIdx.x / nq;
   const int q = blockIdx.x - chunk * nq;
-  const int vis = q_vis[q];
+  const int vis = clamp_vis(q_vis[q], ws);
   const int t0 = chunk * kScanChunk;
   if (t0 >= vis) return;                              // uniform for the block
   const int t1 = min(vis, t0 + kScanChunk);
@@ -71,7 +71,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
   const int pg0 = t0 >> c.lg_page;
   const int npg = ((t1 - 1) >> c.lg_page) - pg0 + 1;
-  const int page_of_lane = lane < npg ? pt_row[pg0 + lane] : 0;
+  const int page_of_lane = lane < npg ? clamp_page(pt_row[pg0 + lane], c) : 0;
   float* srow = ws.scores + (int64_t)q * ws.vstride;
   const int ntiles = (t1 - t0 + 15) >> 4;
   lds_barrier();

@@ -47,9 +47,8 @@ pool_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __
   const int g = lane >> 4, r = lane & 15;
   // the tile's rows first (pool index -> page -> row: three dependent loads)
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
-  const int t_max = (c.max_pages << c.lg_page) - 1;       // keeps a bad pool entry inside the page table
   const int t = pool[(int64_t)q * p + min(e0 + (lane >> 2), e1 - 1)];
-  const int64_t row = entry_row(pt_row, min(max(t, 0), t_max), c.lg_page);
+  const int64_t row = entry_row_clamped(pt_row, t, c);   // a bad pool entry stays inside the cache
   const uint8_t* src = c.idx_k + row * kIndexDim + 32 * (lane & 3);
   const intx4 lo = *reinterpret_cast<const intx4*>(src);
   const intx4 hi = *reinterpret_cast<const intx4*>(src + 16);

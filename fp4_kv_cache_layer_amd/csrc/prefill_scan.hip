@@ -44,8 +44,6 @@
 
 namespace csa2 {
 
-int g_prefill_cand_factor = 4;
-
 namespace {
 
 constexpr int kPfWaves = 4;
@@ -141,9 +139,9 @@ prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* 
   // the output row of this lane holds query qrow (QPT = 2: rows 0,1 -> qt, rows 2,3 -> qt+1)
   const int qrow = qt + (QPT == 2 ? (g >> 1) : 0);
   const bool valid = qrow < nq;
-  const int V = valid ? q_vis[qrow] : 0;
-  int vmin = q_vis[qt];
-  if (QPT == 2 && qt + 1 < nq) vmin = min(vmin, q_vis[qt + 1]);
+  const int V = valid ? clamp_vis(q_vis[qrow], ws) : 0;
+  int vmin = clamp_vis(q_vis[qt], ws);
+  if (QPT == 2 && qt + 1 < nq) vmin = min(vmin, clamp_vis(q_vis[qt + 1], ws));
   const int ntv = vmin >> 4;                                  // 16-entry tiles visible to the whole tile
 
   // rank r in the sample; 0 = no sampled threshold for this row
@@ -165,7 +163,7 @@ prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* 
 #pragma unroll
     for (int j = 0; j < kSampleTiles; ++j) {
       const int ts = (j * ntv / kSampleTiles) * 16;
-      const int page = pt_row[ts >> c.lg_page];
+      const int page = clamp_page(pt_row[ts >> c.lg_page], c);
       const int64_t row = ((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1)) + r;
       const intx8 b = load_fp8_operand(c.idx_k + row * kIndexDim, g);
       floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -219,7 +217,7 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   bool any_fail = false;
 #pragma unroll
   for (int j = 0; j < kQ; ++j) {
-    const int v = (q0 + j < nq) ? q_vis[q0 + j] : 0;
+    const int v = (q0 + j < nq) ? clamp_vis(q_vis[q0 + j], ws) : 0;
     vmax = max(vmax, v);
     if (RESCORE && v > k && (int)ws.cand_cnt[q0 + j] < k) any_fail = true;
   }
@@ -257,7 +255,7 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     const int ql = 4 * p + g;
     const int qg = q0 + ql;
     const bool valid = qg < nq;
-    const int v = valid ? q_vis[qg] : 0;
+    const int v = valid ? clamp_vis(q_vis[qg], ws) : 0;
     bool own;
     if (RESCORE) {
       own = valid && v > k && (int)ws.cand_cnt[qg] < k;
@@ -284,7 +282,7 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q0] * c.max_pages;
   const int pg0 = e0 >> c.lg_page;
   const int npg = ((e1 - 1) >> c.lg_page) - pg0 + 1;
-  const int page_of_lane = lane < npg ? pt_row[pg0 + lane] : 0;
+  const int page_of_lane = lane < npg ? clamp_page(pt_row[pg0 + lane], c) : 0;
   const int ntiles = (e1 - e0 + 15) >> 4;
 
   // Every query block streams the same chunk; starting each block at its own
@@ -412,7 +410,7 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t total;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int V = q_vis[q];
+  const int V = clamp_vis(q_vis[q], ws);
   if (V <= k) return;                                // the final select needs no candidates
   if (short_only && (int)ws.cand_cnt[q] >= k) return;   // uniform
   for (int i = tid; i < kHistBins; i += kCompactThreads) h[i] = 0;
@@ -478,7 +476,7 @@ prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int sh
 
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                               hipStream_t s, const KEvents& ev, const KEvents& ev_product) {
+                               int cand_factor, hipStream_t s, const KEvents& ev, const KEvents& ev_product) {
   if (nq <= 0 || max_vis <= 0) {
     record_empty(ev, s);
     record_empty(ev_product, s);
@@ -490,7 +488,7 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
   const int64_t nqb = (nq + kPfTiles * qpt - 1) / (kPfTiles * qpt);
   const dim3 grid((unsigned)(8 * per_xcd * nqb)), block(kPfWaves * 64);
   const dim3 tgrid((unsigned)((nq + kTauWaves * qpt - 1) / (kTauWaves * qpt))), tblock(kTauWaves * 64);
-  const int factor = g_prefill_cand_factor;
+  const int factor = cand_factor;
   // threshold, candidates, compaction (which counts each query's
   // candidates), full rescore of the queries left short, their compaction
   if (qpt == 2) {

@@ -120,7 +120,7 @@ sparse_attn_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* _
     const int32_t* irow = idx + (int64_t)qi * k;
     for (int j = tid; j < per_split * kTileRows; j += kThreads) {
       const int t = irow[min(j0 + j, k - 1)];
-      if (j < n) S.row[j] = (uint32_t)entry_row(pt_row, t, c.lg_page);
+      if (j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, t, c);
     }
   }
   lds_barrier();
@@ -392,7 +392,7 @@ sparse_attn_hg_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
     const int32_t* irow = idx + (int64_t)qi * k;
     for (int j = tid; j < ntiles * kTileRows; j += 256 * kHg) {
       const int t = irow[min(j, k - 1)];
-      if (j < n) S.row[j] = (uint32_t)entry_row(pt_row, t, c.lg_page);
+      if (j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, t, c);
     }
   }
   lds_barrier();
@@ -569,7 +569,6 @@ attn_combine_kernel(int h, int nsplit, const float* __restrict__ part_o, const f
   if (lse != nullptr && tid == 0) lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
 }
 
-int g_attn_share_heads = 1;
 // Shared-row workgroups (sparse_attn_hg_kernel) need a batch that gives every
 // CU a few of them; below that the 16-head form spreads the work wider.
 constexpr int64_t kHgMinUnits = 512;
@@ -606,7 +605,7 @@ size_t attn_part_bytes(int nq, int h, int k) {
 
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, hipStream_t s, const KEvents& ev) {
+                              void* part, bool share_heads, hipStream_t s, const KEvents& ev) {
   if (nq <= 0 || h <= 0) {
     record_empty(ev, s);
     return hipSuccess;
@@ -619,7 +618,7 @@ hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32
   const int64_t npairs = (int64_t)nq * ns;
   const int64_t blocks = (npairs + 7) / 8 * 8 * ngroups;
   const int64_t hg_units = (h % (16 * kHg) == 0) ? (int64_t)nq * (h / (16 * kHg)) : 0;
-  if (g_attn_share_heads && ns == 1 && hg_units >= kHgMinUnits) {
+  if (share_heads && ns == 1 && hg_units >= kHgMinUnits) {
     const int per_xcd = (int)((hg_units + 7) / 8);
     launch(sparse_attn_hg_kernel, dim3((unsigned)(per_xcd * 8)), dim3(256 * kHg), s, ev, c, q, q_seq, idx, cnt, h, k,
            sm_scale, out, lse, (int)hg_units, per_xcd);

@@ -126,7 +126,7 @@ topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int ns
   __shared__ int count, base;
   const int q = blockIdx.x / nslices;
   const int slice = blockIdx.x - q * nslices;
-  const int V = q_vis[q];
+  const int V = clamp_vis(q_vis[q], ws);
   const int t0 = slice * kCollectSlice;
   if (V <= k || t0 >= V) return;                      // uniform
   const int tid = threadIdx.x;
@@ -210,7 +210,7 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
                   int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
   __shared__ SelShared S;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int V = q_vis[q];
+  const int V = clamp_vis(q_vis[q], ws);
   uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
   const int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
   const uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride;

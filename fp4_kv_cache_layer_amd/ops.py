@@ -37,6 +37,20 @@ def _need(t: torch.Tensor, dtypes, name: str):
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
 
 
+def _shape(t: Optional[torch.Tensor], dtypes, shape, name: str) -> None:
+    """t (if given) has one of dtypes and exactly this shape (the kernels read
+    the sizes the arguments imply, so a shorter or wider tensor would be read
+    out of bounds or misread)."""
+    if t is None:
+        return
+    _need(t, dtypes, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+_I32 = (torch.int32,)
+
+
 _BF16 = (torch.int16, torch.bfloat16, torch.uint16)
 
 
@@ -76,6 +90,13 @@ def csa2_workspace_bytes(mode: int, nq: int, max_vis: int, h_idx: int, h: int, k
     return int(L.load().csa2_workspace_bytes(mode, nq, max_vis, h_idx, h, k))
 
 
+def workspace_state_bytes(nq: int) -> int:
+    """Leading workspace bytes that carry state between calls (the per-query
+    histograms and candidate counters: round_up(nq * 2049 * 4, 256)); the
+    rest carries none (see csa2_workspace_bytes in include/csa2.h)."""
+    return (nq * 2049 * 4 + 255) // 256 * 256
+
+
 def csa2_workspace_init(ws: torch.Tensor, stream=None) -> None:
     L.check("csa2_workspace_init", L.load().csa2_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -107,8 +128,12 @@ def csa2_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_seq: t
     """Indexer scores + Top-K.  dense=True calls csa2_prefill_index_topk (every
     query in sequence q_seq[0]: one FP8 matrix product with a causal mask)."""
     nq, h_idx = q_idx.shape[0], q_idx.shape[1]
-    _need(q_idx, (torch.uint8,), "q_idx")
-    _need(w, (torch.float32,), "w")
+    _shape(q_idx, (torch.uint8,), (nq, h_idx, D_INDEX), "q_idx")
+    _shape(w, (torch.float32,), (nq, h_idx), "w")
+    _shape(q_seq, _I32, (nq,), "q_seq")
+    _shape(q_vis, _I32, (nq,), "q_vis")
+    _shape(out_idx, _I32, (nq, k), "out_idx")
+    _shape(out_cnt, _I32, (nq,), "out_cnt")
     if out_idx is None:
         out_idx = torch.empty((nq, k), dtype=torch.int32, device=q_idx.device)
     if out_cnt is None:
@@ -131,11 +156,14 @@ def csa2_pool_index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, q_s
                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Hierarchical indexer: Top-k of each query among its pool [nq][P]."""
     nq, h_idx = q_idx.shape[0], q_idx.shape[1]
-    _need(q_idx, (torch.uint8,), "q_idx")
-    _need(w, (torch.float32,), "w")
-    _need(pool, (torch.int32,), "pool")
-    _need(pool_cnt, (torch.int32,), "pool_cnt")
     p = pool.shape[1]
+    _shape(q_idx, (torch.uint8,), (nq, h_idx, D_INDEX), "q_idx")
+    _shape(w, (torch.float32,), (nq, h_idx), "w")
+    _shape(q_seq, _I32, (nq,), "q_seq")
+    _shape(pool, _I32, (nq, p), "pool")
+    _shape(pool_cnt, _I32, (nq,), "pool_cnt")
+    _shape(out_idx, _I32, (nq, k), "out_idx")
+    _shape(out_cnt, _I32, (nq,), "out_cnt")
     if ws is None:
         ws = csa2_pool_workspace(nq, p, device=q_idx.device)
     if out_idx is None:
@@ -152,9 +180,14 @@ def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: to
                      sm_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      with_lse: bool = True, ws: Optional[torch.Tensor] = None,
                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    _need(q, _BF16, "q")
     nq, h = q.shape[0], q.shape[1]
     k = idx.shape[1]
+    _shape(q, _BF16, (nq, h, D_LATENT), "q")
+    _shape(q_seq, _I32, (nq,), "q_seq")
+    _shape(idx, _I32, (nq, k), "idx")
+    _shape(cnt, _I32, (nq,), "cnt")
+    _shape(out, (torch.float32,), (nq, h, D_LATENT), "out")
+    _shape(lse, (torch.float32,), (nq, h), "lse")
     if out is None:
         out = torch.empty((nq, h, D_LATENT), dtype=torch.float32, device=q.device)
     if lse is None and with_lse:
@@ -163,14 +196,6 @@ def csa2_sparse_attn(cache: Cache, q: torch.Tensor, q_seq: torch.Tensor, idx: to
         ctypes.byref(cache.view), _ptr(q), _ptr(q_seq), _ptr(idx), _ptr(cnt), nq, h, k, float(sm_scale),
         _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse
-
-
-def csa2_set_prefill_candidate_factor(factor: int) -> None:
-    L.check("csa2_set_prefill_candidate_factor", L.load().csa2_set_prefill_candidate_factor(int(factor)))
-
-
-def csa2_set_attn_head_sharing(enable: bool) -> None:
-    L.check("csa2_set_attn_head_sharing", L.load().csa2_set_attn_head_sharing(int(enable)))
 
 
 class LayerCall:
@@ -183,11 +208,36 @@ class LayerCall:
                  q_idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
                  new_slots: Optional[torch.Tensor] = None, new_kv: Optional[torch.Tensor] = None,
                  new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                 dense: bool = False, pool: Optional[torch.Tensor] = None, pool_cnt: Optional[torch.Tensor] = None):
+                 dense: bool = False, pool: Optional[torch.Tensor] = None, pool_cnt: Optional[torch.Tensor] = None,
+                 dense_cand_factor: int = 0, attn_per_head_group: bool = False,
+                 timing: Optional["Timing"] = None):
         """pool / pool_cnt ([nq][P], [nq] int32): hierarchical indexer; a Full
-        layer writes its Top-P there, a Reindex layer scores only those."""
+        layer writes its Top-P there, a Reindex layer scores only those.
+        dense_cand_factor: the dense indexer's candidate factor (0 default,
+        L.DENSE_RESCORE_ALL rescores every query).  attn_per_head_group: one
+        attention workgroup per 16-head group even where the shared-row form
+        applies.  timing: device timestamps of this call's kernels."""
         self.mode = mode
         self.cache = cache
+        nq, h = q.shape[0], q.shape[1]
+        _shape(q, _BF16, (nq, h, D_LATENT), "q")
+        _shape(q_seq, _I32, (nq,), "q_seq")
+        _shape(q_vis, _I32, (nq,), "q_vis")
+        _shape(idx, _I32, (nq, k), "idx")
+        _shape(cnt, _I32, (nq,), "cnt")
+        _shape(out, (torch.float32,), (nq, h, D_LATENT), "out")
+        _shape(lse, (torch.float32,), (nq, h), "lse")
+        if mode in (FULL, REINDEX):
+            _shape(q_idx, (torch.uint8,), (nq, q_idx.shape[1], D_INDEX), "q_idx")
+            _shape(w, (torch.float32,), (nq, q_idx.shape[1]), "w")
+        if mode == FULL and new_slots is not None:
+            n_new = new_slots.numel()
+            _shape(new_slots, _I32, (n_new,), "new_slots")
+            _shape(new_kv, _BF16, (n_new, D_LATENT), "new_kv")
+            _shape(new_idxk, _BF16, (n_new, D_INDEX), "new_idxk")
+        if pool is not None:
+            _shape(pool, _I32, (nq, pool.shape[1]), "pool")
+            _shape(pool_cnt, _I32, (nq,), "pool_cnt")
         self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws, pool, pool_cnt)
         a = L.StepArgs()
         a.cache = ctypes.pointer(cache.view)
@@ -201,12 +251,22 @@ class LayerCall:
         a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = _ptr(q_seq), _ptr(q_vis), q.shape[0], k, max_vis
         a.idx, a.cnt, a.out, a.lse = _ptr(idx), _ptr(cnt), _ptr(out), _ptr(lse)
         a.flags = L.STEP_DENSE_INDEX if dense else 0
+        if attn_per_head_group:
+            a.flags |= L.STEP_ATTN_PER_HEAD_GROUP
+        a.dense_cand_factor = int(dense_cand_factor)
         if pool is not None:
             a.flags |= L.STEP_POOL
             a.pool, a.pool_cnt, a.pool_k = _ptr(pool), _ptr(pool_cnt), pool.shape[1]
         self.args = a
+        self.timing = None
+        self.set_timing(timing)
         self._ref = ctypes.byref(a)
         self._fn = L.load().csa2_layer_step
+
+    def set_timing(self, timing: Optional["Timing"]) -> None:
+        """Attach (or with None detach) device timestamps to later calls."""
+        self.timing = timing
+        self.args.timing = ctypes.pointer(timing.struct) if timing is not None else None
 
     def __call__(self, stream=None) -> None:
         st = self._fn(self.mode, self._ref, _stream(stream))
@@ -323,6 +383,12 @@ class GroupCall:
         self._n = n
         self._fn = lib.csa2_group_step
 
+    def set_timing(self, timing: Optional["Timing"]) -> None:
+        """Attach (or detach) device timestamps to every layer of later calls."""
+        for i, c in enumerate(self.calls):
+            c.set_timing(timing)
+            self.args[i].timing = c.args.timing
+
     def __call__(self, stream=None) -> None:
         ex = None
         if self.exs:
@@ -334,10 +400,10 @@ class GroupCall:
 
 
 class TimingRing:
-    """Device-event ring for one kernel class (see csa2_set_timing)."""
+    """Device-event ring for one kernel class: start/stop hipEvent pairs that
+    the library records through the launches of calls carrying it."""
 
-    def __init__(self, kernel_class: int, capacity: int):
-        self.kernel_class = kernel_class
+    def __init__(self, capacity: int):
         self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(capacity)]
         for a, b in self.events:          # materialise the hipEvent handles
@@ -349,13 +415,25 @@ class TimingRing:
         self.ring = L.TimingRing(ctypes.cast(self._start, ctypes.POINTER(ctypes.c_void_p)),
                                  ctypes.cast(self._stop, ctypes.POINTER(ctypes.c_void_p)), capacity, 0)
 
-    def install(self) -> None:
-        self.ring.count = 0
-        L.check("csa2_set_timing", L.load().csa2_set_timing(self.kernel_class, ctypes.byref(self.ring)))
-
-    def uninstall(self) -> None:
-        L.check("csa2_set_timing", L.load().csa2_set_timing(self.kernel_class, None))
-
     def durations_ms(self):
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in self.events[:self.ring.count]]
+
+
+class Timing:
+    """Per-call device timing (csa2_timing): one ring per kernel class named
+    in capacities ({kernel class: capacity}); attach it to LayerCalls with
+    set_timing (or the timing argument) before building a GroupCall on them."""
+
+    def __init__(self, capacities: dict):
+        self.rings = {cls: TimingRing(cap) for cls, cap in capacities.items()}
+        self.struct = L.Timing()
+        for cls, r in self.rings.items():
+            self.struct.ring[cls] = ctypes.pointer(r.ring)
+
+    def reset(self) -> None:
+        for r in self.rings.values():
+            r.ring.count = 0
+
+    def durations_ms(self, cls: int):
+        return self.rings[cls].durations_ms()

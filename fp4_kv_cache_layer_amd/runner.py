@@ -17,16 +17,34 @@ from . import ops
 APPEND_CHUNK = 1 << 20          # rows per bulk append call
 
 
+class _null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
 class DeviceCase:
     """dense: None -> the dense prefill indexer for prefill workloads (all
     queries in one sequence), the per-query scan otherwise.  group: 0 runs
     the layers as separate csa2_layer_step calls; n > 0 runs them as one
     csa2_group_step with n auxiliary streams, with a workspace of their own
-    for the Reuse layers so they overlap the layers after them."""
+    for the Reuse layers so they overlap the layers after them.
+    cand_factor / attn_per_head_group are the layer calls' dense-indexer
+    candidate factor and attention-form flag (see ops.LayerCall)."""
 
     def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda",
-                 dense: Optional[bool] = None, group: int = 0, shared_ws: bool = False):
+                 dense: Optional[bool] = None, group: int = 0, shared_ws: bool = False,
+                 cand_factor: int = 0, attn_per_head_group: bool = False, poison_ws: bool = False):
+        """poison_ws: before every layer call, fill the workspace bytes that
+        carry no state between calls with 0xFF (a check that no kernel reads
+        what the same call did not write)."""
         self.spec = spec
+        self.poison_ws = poison_ws
+        self.cand_factor = cand_factor if (spec.prefill if dense is None else dense) else 0
+        self.attn_per_head_group = attn_per_head_group
+        self.graph = None
         self.dense = spec.prefill if dense is None else dense
         self.group_aux = group
         self.shared_ws = shared_ws
@@ -122,15 +140,32 @@ class DeviceCase:
             pool, pool_cnt = self.pool, self.pool_cnt
         common = (self.cache, q, self.q_seq, self.q_vis, k, self.max_vis, spec.sm_scale, o["idx"], o["cnt"],
                   o["out"], o["lse"])
+        opts = dict(attn_per_head_group=self.attn_per_head_group)
         if mode == ops.REUSE:
-            return ops.LayerCall(mode, *common, ws=ws)
+            return ops.LayerCall(mode, *common, ws=ws, **opts)
+        opts.update(dense=self.dense, pool=pool, pool_cnt=pool_cnt, dense_cand_factor=self.cand_factor)
         if mode == ops.FULL:
             return ops.LayerCall(mode, *common, q_idx=qi, w=w, new_slots=self.new_slots, new_kv=self.new_kv,
-                                 new_idxk=self.new_ik, ws=ws, dense=self.dense, pool=pool, pool_cnt=pool_cnt)
-        return ops.LayerCall(mode, *common, q_idx=qi, w=w, ws=ws, dense=self.dense, pool=pool, pool_cnt=pool_cnt)
+                                 new_idxk=self.new_ik, ws=ws, **opts)
+        return ops.LayerCall(mode, *common, q_idx=qi, w=w, ws=ws, **opts)
+
+    def set_timing(self, timing) -> None:
+        """Attach an ops.Timing (or None) to the per-layer calls and the group step."""
+        for c in self.calls:
+            c.set_timing(timing)
+        if self.group is not None:
+            self.group.set_timing(timing)
+
+    def _poison(self, ws, stream=None) -> None:
+        z = ops.workspace_state_bytes(self.spec.nq)
+        with torch.cuda.stream(stream) if stream is not None else _null():
+            ws[z:].fill_(0xFF)
 
     def run_group(self, stream=None) -> None:
         if self.group is not None:
+            if self.poison_ws:
+                for ws in {id(w): w for w in self.group_ws}.values():
+                    self._poison(ws, stream)
             self.group(stream)
             return
         self.run_layers(stream)
@@ -138,7 +173,25 @@ class DeviceCase:
     def run_layers(self, stream=None) -> None:
         """The layers as separate csa2_layer_step calls, whatever `group` is."""
         for c in self.calls:
+            if self.poison_ws:
+                self._poison(self.ws, stream)
             c(stream)
+
+    def capture_graph(self) -> None:
+        """Captures one step's per-layer calls (in layer order, on one stream)
+        into a HIP graph; replay_graph() then launches the whole group with one
+        call.  The captured kernels read and write the same buffers as the
+        eager calls, so a replay gives exactly their results.  Calls must not
+        carry timing while captured."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_layers()
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def replay_graph(self) -> None:
+        self.graph.replay()
 
     def results_host(self) -> List[dict]:
         torch.cuda.synchronize()

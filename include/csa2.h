@@ -48,10 +48,13 @@
  *     errors are found on the host before anything is enqueued and return a
  *     status; execution errors surface at the caller's next stream sync.
  *   - Device-resident values (seq_lens, q_vis, q_seq, page-table entries,
- *     slots, idx, cnt) are trusted: the caller guarantees q_vis[i] <=
+ *     slots, idx, cnt, pool) are trusted: the caller guarantees q_vis[i] <=
  *     seq_len(q_seq[i]) <= max_pages * page_size and that every page-table
- *     entry a query can reach lies in [0, num_pages).  Out-of-range device
- *     data is undefined behaviour.
+ *     entry a query can reach lies in [0, num_pages).  The kernels still clamp
+ *     q_vis to [0, max_vis], counts to [0, k], selected and pool indices to
+ *     the page table's range and the page ids they read to [0, num_pages), so
+ *     such values give wrong results rather than stray memory accesses;
+ *     q_seq and slots are used as given.
  *   - Every pointer must be 16-byte aligned (w, q_seq, q_vis, cnt, lse,
  *     slots: 4-byte aligned suffices); a zero count (n == 0 or nq == 0)
  *     returns CSA2_OK and enqueues nothing.
@@ -123,10 +126,12 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
  * least nq * 8 KB so a
  * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk and
  * csa2_sparse_attn accept a
- * workspace sized by this call for the same shape.  The histogram part carries state:
- * every call leaves it zeroed for the next one, so zero the whole workspace
- * once after allocating it (csa2_workspace_init does this).  Calls that
- * share one workspace must not run concurrently. */
+ * workspace sized by this call for the same shape.  Only the first
+ * round_up(nq * 2049 * 4, 256) bytes (histograms and counters) carry state:
+ * every call leaves them zeroed for the next one, so zero the whole
+ * workspace once after allocating it (csa2_workspace_init does this); the
+ * rest is written before it is read within each call.  Calls that share one
+ * workspace must not run concurrently. */
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis,
                             int32_t h_idx, int32_t h, int32_t k);
 
@@ -163,25 +168,15 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
                                     int32_t* out_idx, int32_t* out_cnt,
                                     void* ws, size_t ws_bytes, hipStream_t s);
 
-/* Candidate target of the dense indexer, in units of k: each query keeps the
- * entries whose score reaches a threshold estimated from a 512-entry sample
- * so that about factor * k of them are expected to pass (default 4; the
- * selection is exact for every factor, queries left with fewer than k
- * candidates are rescored in full).  0 sends every query with more than k
- * visible entries through the full rescore.  Process-wide, not thread-safe:
- * meant for tuning and tests.  Returns CSA2_ERR_INVALID_ARG outside [0, 64]. */
-csa2_status csa2_set_prefill_candidate_factor(int32_t factor);
-
-/* Form of sparse attention for large batches (h a multiple of 64, at least
- * 512 (query, 64-head) units, unsplit): enable = 1 (default) serves the 64
- * heads of a query in one workgroup that gathers and dequantises each
- * selected row once for all of them; 0 keeps one workgroup per 16-head
- * group, which gathers the row once per group.  Both forms give identical
- * bits.  Process-wide, not thread-safe: meant for tests and measurement.
- * Returns CSA2_ERR_INVALID_ARG unless enable is 0 or 1. */
-csa2_status csa2_set_attn_head_sharing(int32_t enable);
-
-/* Sparse attention over the selected rows (all three modes end here).
+/* Sparse attention over the selected rows.  Every CSA2 mode ends here: Full
+ * and Reindex attend over the Top-512 entries they just selected, Reuse over
+ * the main KV and indices of an earlier layer ("Unlocking Extreme Context
+ * Scaling with DeepSeek-V4.1-Flash", section "Compressed Sparse Attention 2
+ * (CSA2)"); the cost is set by the selection, not by the context length
+ * ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+ * Introduction: near-constant single-token decode FLOPs from 4K to 1M).
+ * Keys and values are the same dequantised 512-wide latent row, shared by all
+ * heads (the reading stated at the top of this header).
  *   q   [nq][h][512] bf16 bit patterns, q_seq [nq],
  *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq]
  *   (a count outside [0, k] is taken as the nearest bound),
@@ -189,11 +184,49 @@ csa2_status csa2_set_attn_head_sharing(int32_t enable);
  * 1 <= h <= 128; sm_scale > 0 and finite.  ws may be NULL; with a
  * workspace of csa2_workspace_bytes(CSA2_REUSE, nq, 0, 1, h, k) bytes, small
  * batches split each query's rows across workgroups and merge the shares in
- * a second kernel. */
+ * a second kernel.  Selected indices are clamped to the page table's range and
+ * page ids to [0, num_pages) before any row is read.
+ * Errors: CSA2_ERR_INVALID_ARG for bad sizes, a bad sm_scale, null or
+ * misaligned pointers; CSA2_ERR_HIP if a launch fails. */
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq,
                              const int32_t* idx, const int32_t* cnt,
                              int32_t nq, int32_t h, int32_t k, float sm_scale,
                              float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Per-kernel device timing of one call, for measurement.  For each kernel
+ * class whose ring is set, the call's launches of that class record the
+ * hipEvent pair start[count] / stop[count] and increment count, until count
+ * reaches capacity.  The events are carried by the kernel dispatches
+ * themselves (start when the class's first kernel of the launch begins, stop
+ * when its last kernel ends), so no separate stream operations are added.
+ * Everything is caller memory: the events (hipEventCreate), the rings and
+ * this struct, which must stay valid until the call returns; the library
+ * writes only the rings' count fields.  Calls that run concurrently must not
+ * share a ring.  Classes: append, indexer scan (for the dense indexer:
+ * threshold, candidates, full rescore and compaction), Top-K select,
+ * attention, the dense indexer's matrix-product (candidate) kernel alone,
+ * hierarchical indexer pool scoring and pool select. */
+typedef struct {
+  hipEvent_t* start;     /* [capacity] */
+  hipEvent_t* stop;      /* [capacity] */
+  int32_t     capacity;
+  int32_t     count;     /* launches recorded so far */
+} csa2_timing_ring;
+
+#define CSA2_KCLASS_APPEND 0
+#define CSA2_KCLASS_SCAN   1
+#define CSA2_KCLASS_SELECT 2
+#define CSA2_KCLASS_ATTN   3
+#define CSA2_KCLASS_DENSE  4
+#define CSA2_KCLASS_POOL_SCAN   5   /* hierarchical indexer: pool scoring */
+#define CSA2_KCLASS_POOL_SELECT 6   /* hierarchical indexer: Top-k of the pool */
+#define CSA2_NUM_KCLASSES  7
+
+typedef struct csa2_timing {
+  csa2_timing_ring* ring[CSA2_NUM_KCLASSES];   /* NULL: that class untimed */
+} csa2_timing;
+
+#define CSA2_DENSE_RESCORE_ALL (-1)
 
 /* Arguments of one layer.  Fields a mode does not use must be NULL / 0. */
 typedef struct {
@@ -225,6 +258,15 @@ typedef struct {
                                     (Full: written; Reindex: read)           */
   int32_t*        pool_cnt;      /* [nq]                                      */
   int32_t         pool_k;        /* pool width P, k <= P <= CSA2_MAX_K        */
+  int32_t         dense_cand_factor;  /* CSA2_STEP_DENSE_INDEX: expected
+                                    candidates per query in units of k (the
+                                    selection is exact for every value): 0 =
+                                    default (4), 1..64 = that factor,
+                                    CSA2_DENSE_RESCORE_ALL = every query with
+                                    more than k visible entries is rescored in
+                                    full; must be 0 without the flag          */
+  struct csa2_timing* timing;    /* nullable: device timestamps of this call's
+                                    kernels (see csa2_timing)                  */
 } csa2_step_args;
 
 /* Full/Reindex: score as csa2_prefill_index_topk (all queries of the call
@@ -236,6 +278,11 @@ typedef struct {
  * Reindex: only the entries of pool (an earlier Full layer's) are scored.
  * Reuse: not allowed. */
 #define CSA2_STEP_POOL 2u
+/* Large batches of 64-head queries normally take the attention form that
+ * gathers and dequantises each selected row once for all 64 heads of a query;
+ * this flag keeps one workgroup per 16-head group instead.  Both forms give
+ * identical bits (it exists to test and measure that). */
+#define CSA2_STEP_ATTN_PER_HEAD_GROUP 4u
 
 /* Hierarchical indexer: the indexer of a later (Reindex) layer scores only
  * the shared candidate pool an earlier indexer chose, and keeps its Top-k
@@ -262,10 +309,22 @@ csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx,
                                  int32_t* out_idx, int32_t* out_cnt, void* ws, size_t ws_bytes, hipStream_t s);
 size_t csa2_pool_workspace_bytes(int32_t nq, int32_t p);
 
-/* One CSA2 layer in the given mode:
+/* One CSA2 layer in one of the three static modes of "Unlocking Extreme
+ * Context Scaling with DeepSeek-V4.1-Flash", section "Compressed Sparse
+ * Attention 2 (CSA2)" (the same modes in "DeepSeek-V4.1-Flash: Pushing the
+ * Limits of KV Cache Compression", Method):
  *   Full    = append (if n_new > 0) -> index_topk -> sparse_attn
- *   Reindex = index_topk on the source cache -> sparse_attn
- *   Reuse   = sparse_attn with the given idx/cnt */
+ *             (fresh entries, fresh scores and Top-k);
+ *   Reindex = index_topk with the layer's own indexer query on the source
+ *             Full layer's indexer-K -> sparse_attn over that layer's KV;
+ *   Reuse   = sparse_attn with the given idx/cnt (an earlier layer's KV and
+ *             indices; no indexing at all).
+ * Every argument is checked on the host before anything is enqueued: the
+ * checks of csa2_append_quant_fp4, csa2_index_topk (Full, Reindex) and
+ * csa2_sparse_attn, unknown flags, fields the mode does not use that are not
+ * NULL / 0, a workspace below csa2_workspace_bytes(mode, ...) for Full and
+ * Reindex.  Returns the first failing status (nothing enqueued), else
+ * CSA2_ERR_HIP if a launch fails, else CSA2_OK. */
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s);
 
 /* A group of layers that share caches and indices, run as one call.  The
@@ -357,37 +416,6 @@ csa2_status csa2_fake_quant_fp4(const void* x, void* y, int64_t n, int32_t dtype
 /* Static description of a status code. */
 const char* csa2_status_string(csa2_status st);
 
-/* Per-kernel device timing for measurement.  While a ring is installed for
- * a kernel class, every launch of that class records the hipEvent pair
- * start[count] / stop[count] and increments count, until count reaches
- * capacity.  The events are carried by the kernel dispatches themselves
- * (start when the class's first kernel begins, stop when its last kernel
- * ends), so no separate stream operations are added.  Events are created and
- * destroyed by the caller (hipEventCreate); the ring struct must outlive its
- * installation.  Classes: 0 append, 1 indexer scan (for the dense indexer:
- * threshold, candidates, full rescore and compaction), 2 Top-K select,
- * 3 attention, 4 the dense indexer's matrix-product (candidate) kernel
- * alone, 5 the branch merge, 6 the FP4 fake quantisation.  Pass ring = NULL
- * to uninstall.  Process-wide, not
- * thread-safe: meant for benchmarks. */
-typedef struct {
-  hipEvent_t* start;     /* [capacity] */
-  hipEvent_t* stop;      /* [capacity] */
-  int32_t     capacity;
-  int32_t     count;     /* launches recorded so far */
-} csa2_timing_ring;
-
-#define CSA2_KCLASS_APPEND 0
-#define CSA2_KCLASS_SCAN   1
-#define CSA2_KCLASS_SELECT 2
-#define CSA2_KCLASS_ATTN   3
-#define CSA2_KCLASS_DENSE  4
-#define CSA2_KCLASS_MERGE  5
-#define CSA2_KCLASS_QUANT  6
-#define CSA2_KCLASS_POOL_SCAN   7   /* hierarchical indexer: pool scoring */
-#define CSA2_KCLASS_POOL_SELECT 8   /* hierarchical indexer: Top-k of the pool */
-#define CSA2_NUM_KCLASSES  9
-csa2_status csa2_set_timing(int32_t kernel_class, csa2_timing_ring* ring);
 
 #ifdef __cplusplus
 }

@@ -22,8 +22,9 @@ def test_exports_every_header_function():
     lib = L.load()
     names = L.header_functions()
     assert set(names) >= {"csa2_append_quant_fp4", "csa2_index_topk", "csa2_prefill_index_topk", "csa2_sparse_attn",
-                          "csa2_layer_step", "csa2_workspace_bytes", "csa2_workspace_init", "csa2_status_string",
-                          "csa2_set_timing"}
+                          "csa2_layer_step", "csa2_workspace_bytes", "csa2_workspace_init", "csa2_status_string"}
+    # no process-wide setters: every knob is a per-call argument
+    assert not any(n.startswith("csa2_set_") for n in names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -118,35 +119,94 @@ def test_layer_step_mode_field_rules():
     assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG   # Full needs q_idx/w/ws
     a.nq = 0
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK              # nothing to do
-    a.flags = 4                                          # unknown flag bit
+    a.flags = 8                                          # unknown flag bit
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
     a.flags = L.STEP_DENSE_INDEX
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
     assert lib.csa2_layer_step(L.CSA2_REUSE, None, None) == L.CSA2_ERR_INVALID_ARG
 
 
-def test_prefill_candidate_factor_range():
+def _reuse_args(v):
+    a = L.StepArgs()
+    a.cache = ctypes.pointer(v)
+    a.q, a.h, a.sm_scale, a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = FAKE, 64, 0.04, FAKE, FAKE, 0, 512, 100
+    a.idx, a.cnt, a.out = FAKE, FAKE, FAKE
+    return a
+
+
+def test_layer_step_per_call_knobs():
+    """The dense indexer's candidate factor and the attention form are fields
+    of the call: the factor is only allowed with the dense flag and within
+    [-1, 64]; the attention-form flag is accepted in every mode."""
     lib = L.load()
-    assert lib.csa2_set_prefill_candidate_factor(-1) == L.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_set_prefill_candidate_factor(65) == L.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_set_prefill_candidate_factor(0) == L.CSA2_OK
-    assert lib.csa2_set_prefill_candidate_factor(4) == L.CSA2_OK
+    v = _view()
+    a = _reuse_args(v)
+    a.dense_cand_factor = 4                              # factor without the dense flag
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    a.flags = L.STEP_DENSE_INDEX
+    for bad in (-2, 65, 1000):
+        a.dense_cand_factor = bad
+        assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
+    for ok in (L.DENSE_RESCORE_ALL, 0, 1, 64):
+        a.dense_cand_factor = ok
+        assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
+    a.flags, a.dense_cand_factor = L.STEP_ATTN_PER_HEAD_GROUP, 0
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
+    a.flags = 8                                          # unknown bit
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
 
 
-def test_attn_head_sharing_switch():
+def test_layer_step_timing_is_per_call():
+    """A timing struct rides on the call; rings without events or with no room
+    are left alone (nothing is launched here: nq = 0)."""
     lib = L.load()
-    for bad in (-1, 2, 7):
-        assert lib.csa2_set_attn_head_sharing(bad) == L.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_set_attn_head_sharing(0) == L.CSA2_OK
-    assert lib.csa2_set_attn_head_sharing(1) == L.CSA2_OK
-
-
-def test_set_timing_validation():
-    lib = L.load()
-    assert lib.csa2_set_timing(9, None) == L.CSA2_ERR_INVALID_ARG
+    v = _view()
+    a = _reuse_args(v)
     r = L.TimingRing(None, None, 4, 0)
-    assert lib.csa2_set_timing(1, ctypes.byref(r)) == L.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_set_timing(1, None) == L.CSA2_OK
+    t = L.Timing()
+    t.ring[L.KCLASS_ATTN] = ctypes.pointer(r)
+    a.timing = ctypes.pointer(t)
+    assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
+    assert r.count == 0
+
+
+def test_ops_checks_dtypes_and_lengths():
+    """The binding rejects index and count tensors of the wrong dtype or
+    length before touching the library (int64 tensors would be read as pairs
+    of int32 words, short ones out of bounds)."""
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    nq, h, k = 3, 16, 8
+    q = torch.zeros((nq, h, 512), dtype=torch.int16)
+    good = dict(q_seq=torch.zeros(nq, dtype=torch.int32), idx=torch.zeros((nq, k), dtype=torch.int32),
+                cnt=torch.zeros(nq, dtype=torch.int32))
+    bad_cases = [("q_seq", torch.zeros(nq, dtype=torch.int64), TypeError),
+                 ("q_seq", torch.zeros(nq - 1, dtype=torch.int32), ValueError),
+                 ("idx", torch.zeros((nq, k), dtype=torch.int64), TypeError),
+                 ("idx", torch.zeros((nq - 1, k), dtype=torch.int32), ValueError),
+                 ("cnt", torch.tensor([1, 2, 3]), TypeError),
+                 ("cnt", torch.zeros(nq + 1, dtype=torch.int32), ValueError)]
+    for name, t, exc in bad_cases:
+        kw = dict(good)
+        kw[name] = t
+        with pytest.raises(exc):
+            ops.csa2_sparse_attn(None, q, kw["q_seq"], kw["idx"], kw["cnt"], 0.04)
+    qi = torch.zeros((nq, 8, 128), dtype=torch.uint8)
+    w = torch.zeros((nq, 8), dtype=torch.float32)
+    for name, t, exc in [("q_vis", torch.zeros(nq, dtype=torch.int64), TypeError),
+                         ("q_vis", torch.zeros(2 * nq, dtype=torch.int32), ValueError),
+                         ("q_seq", torch.zeros((nq, 1), dtype=torch.int32), ValueError),
+                         ("out_idx", torch.zeros((nq, k + 1), dtype=torch.int32), ValueError),
+                         ("out_cnt", torch.zeros(nq, dtype=torch.int64), TypeError)]:
+        kw = dict(q_seq=torch.zeros(nq, dtype=torch.int32), q_vis=torch.zeros(nq, dtype=torch.int32),
+                  out_idx=None, out_cnt=None)
+        kw[name] = t
+        with pytest.raises(exc):
+            ops.csa2_index_topk(None, qi, w, kw["q_seq"], kw["q_vis"], k, 100, None,
+                                out_idx=kw["out_idx"], out_cnt=kw["out_cnt"])
+    with pytest.raises(ValueError):                      # w of the wrong width
+        ops.csa2_index_topk(None, qi, torch.zeros((nq, 4)), good["q_seq"], good["q_seq"], k, 100, None)
 
 
 def test_group_step_validation():

@@ -123,6 +123,37 @@ def test_config4_ragged_paged():
     _check_sampled(spec, sample=sample)
 
 
+def test_config3_decode_1m_integer_exact():
+    """The 1M-entry decode workload on integer indexer inputs: the scan over
+    512 chunks per query, the chip-wide collect and the bitonic output path
+    (contexts past 262,144 entries), bit-exact against the oracle."""
+    _check_sampled(W.config(3, integer_indexer=True), sample=[0, 7], exact=True)
+
+
+def test_config4_ragged_paged_integer_exact():
+    """The ragged paged group on integer indexer inputs, bit-exact, on the
+    shortest and the longest sequence."""
+    spec = W.config(4, integer_indexer=True)
+    lens = np.array(spec.cached)
+    _check_sampled(spec, sample=sorted({int(lens.argmin()), int(lens.argmax())}), exact=True)
+
+
+def test_config2_prefill_integer_exact():
+    """The full prefill chunk through the dense indexer on integer inputs,
+    bit-exact on the first, second, middle and last rows."""
+    _check_sampled(W.config(2, integer_indexer=True), sample=[0, 1, 2047, 4095], exact=True)
+
+
+@pytest.mark.parametrize("k", [500, 2048])
+def test_long_context_bitonic_output_integer_exact(k):
+    """One query over about 300K entries (past the 262,144-entry bitmap, so
+    the select sorts its output bitonically) with integer indexer inputs, at
+    a k that is not a power of two (padding) and at the largest k."""
+    spec = W.small_case("bitonic", 90 + k, [300007], n_new=1, h_idx=8, h=16, k=k, modes=(O.FULL,),
+                        integer_indexer=True, page_size=4096, shuffle_pages=True)
+    _check_sampled(spec, sample=[0], exact=True)
+
+
 def test_config1_group_step_equals_layer_calls():
     """The benchmark's group step (Reuse attentions on an auxiliary stream)
     against the per-layer calls on the full decode workload: identical bits."""

@@ -74,17 +74,27 @@ def test_append_bit_exact_every_bf16(arrangement):
 # indexer + Top-K
 # ---------------------------------------------------------------------------
 
-def _run_case(spec, dense=None):
+def _run_case(spec, dense=None, poison_ws=True, **kw):
+    """Runs the case's layer group (workspaces poisoned before every call
+    unless told otherwise) and returns the device case and its results."""
     _, runner = _ops()
-    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense)
+    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense, poison_ws=poison_ws, **kw)
     dc.run_group()
     return dc, dc.results_host()
 
 
-def _compare_group(spec, exact_topk: bool, dense=None):
+def _compare_group(spec, exact_topk: bool, dense=None, group: int = 0):
     say(f"[group] {spec.name} seed={spec.seed} seqs={spec.num_seqs} cached={spec.cached[:6]} "
-        f"n_new={spec.n_new} h_idx={spec.h_idx} h={spec.h} k={spec.k} int={spec.integer_indexer} dense={dense}")
-    dc, got = _run_case(spec, dense)
+        f"n_new={spec.n_new} h_idx={spec.h_idx} h={spec.h} k={spec.k} int={spec.integer_indexer} dense={dense} "
+        f"group={group}")
+    dc, got = _run_case(spec, dense, group=group)
+    ref = _check_against_oracle(spec, got, exact_topk)
+    return dc, got, ref
+
+
+def _check_against_oracle(spec, got, exact_topk: bool):
+    """Every layer's selection (bit-exact, or valid up to near-ties) and its
+    attention over the GPU's own selection against the fp64 oracle."""
     case = CB.build(spec)
     ref = CB.run_group(case)
     # oracle cache after the Full layer's append, to evaluate attention over the GPU's selection
@@ -115,7 +125,41 @@ def _compare_group(spec, exact_topk: bool, dense=None):
         assert np.array_equal(np.isfinite(g["lse"]), fin)
         lerr = np.abs(g["lse"][fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
         assert lerr.size == 0 or lerr.max() <= LSE_RTOL, lerr.max()
-    return dc, got, ref
+    return ref
+
+
+@pytest.mark.parametrize("n_aux", [1, 2])
+def test_group_step_against_oracle(n_aux):
+    """The group step (Reuse attentions on auxiliary streams) checked against
+    the oracle directly, not only against the per-layer calls."""
+    spec = W.small_case("group_oracle", 64, [3000, 1200, 5000, 64], n_new=1, h_idx=8, h=64, k=512,
+                        integer_indexer=True)
+    _compare_group(spec, exact_topk=True, group=n_aux)
+
+
+def test_graph_replay_against_oracle_and_eager():
+    """The group's per-layer calls captured in one HIP graph: every replay,
+    with eager work (outputs clobbered) and synchronisations between replays,
+    gives exactly the eager results, which match the oracle."""
+    spec = W.small_case("graph", 65, [4096, 900, 2500], n_new=1, h_idx=8, h=64, k=512, integer_indexer=True)
+    say("[graph] capture and replay")
+    dc, eager = _run_case(spec)
+    _check_against_oracle(spec, eager, exact_topk=True)
+    dc.poison_ws = False                     # no fill kernels inside the captured graph
+    dc.capture_graph()
+    for rep in range(3):
+        for o in dc.outputs:
+            o["out"].fill_(float("nan"))
+            o["lse"].fill_(float("nan"))
+            o["idx"].fill_(-7)
+            o["cnt"].fill_(-7)
+        torch.cuda.synchronize()
+        dc.replay_graph()
+        got = dc.results_host()
+        for li, (x, y) in enumerate(zip(got, eager)):
+            for key in ("idx", "cnt", "out", "lse"):
+                assert np.array_equal(x[key], y[key]), (rep, li, key)
+    _check_against_oracle(spec, got, exact_topk=True)
 
 
 @pytest.mark.parametrize("seed,cached,h_idx,k", [
@@ -193,10 +237,10 @@ def test_prefill_dense_bit_identical_to_scan(seed, cached, n_new, h_idx, page_si
 def _group_vs_layers(spec, n_aux, dense=None, shared_ws=False, reps=2):
     _, runner = _ops()
     say(f"[group step] {spec.name} seed={spec.seed} modes={spec.modes} n_aux={n_aux} shared_ws={shared_ws}")
-    ref = runner.DeviceCase(spec, gen_device="cpu", dense=dense)
+    ref = runner.DeviceCase(spec, gen_device="cpu", dense=dense, poison_ws=True)
     ref.run_group()
     want = ref.results_host()
-    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense, group=n_aux, shared_ws=shared_ws)
+    dc = runner.DeviceCase(spec, gen_device="cpu", dense=dense, group=n_aux, shared_ws=shared_ws, poison_ws=True)
     for rep in range(reps):
         dc.run_group()
         got = dc.results_host()
@@ -233,16 +277,12 @@ def test_prefill_dense_candidate_factor(factor):
     """Candidate factor 0 sends every query through the full rescore, 1 makes
     short candidate lists (some queries rescored), 64 keeps every entry; the
     selection is the same in all cases."""
-    ops, _ = _ops()
+    from fp4_kv_cache_layer_amd import _lib as L
     spec = W.small_case("prefill_factor", 52, [24000], n_new=48, h_idx=8, h=16, k=256,
                         modes=(O.FULL,), prefill=True, page_size=128)
     say(f"[dense factor] factor={factor}")
     _, ref = _run_case(spec, dense=False)
-    try:
-        ops.csa2_set_prefill_candidate_factor(factor)
-        _, got = _run_case(spec, dense=True)
-    finally:
-        ops.csa2_set_prefill_candidate_factor(4)
+    _, got = _run_case(spec, dense=True, cand_factor=L.DENSE_RESCORE_ALL if factor == 0 else factor)
     for key in ("idx", "cnt", "out", "lse"):
         assert np.array_equal(got[0][key], ref[0][key]), key
 
@@ -314,15 +354,15 @@ def test_sparse_attn_large_batch_shared_rows(nq, h, k):
         idx[i, :c] = np.sort(rng.choice(n, c, replace=False))
     q = (rng.standard_normal((nq, h, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     q_seq = np.zeros(nq, dtype=np.int32)
-    args = (cache, torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda(),
-            torch.from_numpy(idx).cuda(), torch.from_numpy(cnts).cuda(), 1 / np.sqrt(512))
-    try:
-        ops.csa2_set_attn_head_sharing(False)
-        out0, lse0 = (x.cpu().numpy() for x in ops.csa2_sparse_attn(*args))
-        ops.csa2_set_attn_head_sharing(True)
-        out1, lse1 = (x.cpu().numpy() for x in ops.csa2_sparse_attn(*args))
-    finally:
-        ops.csa2_set_attn_head_sharing(True)
+    qd, sd = torch.from_numpy(q.view(np.int16)).cuda(), torch.from_numpy(q_seq).cuda()
+    idd, cd = torch.from_numpy(idx).cuda(), torch.from_numpy(cnts).cuda()
+    # the one-workgroup-per-16-heads form, through a Reuse layer step with the flag
+    out0 = torch.empty((nq, h, 512), dtype=torch.float32, device="cuda")
+    lse0 = torch.empty((nq, h), dtype=torch.float32, device="cuda")
+    ops.LayerCall(ops.REUSE, cache, qd, sd, sd, k, 0, 1 / np.sqrt(512), idd, cd, out0, lse0,
+                  attn_per_head_group=True)()
+    out0, lse0 = out0.cpu().numpy(), lse0.cpu().numpy()
+    out1, lse1 = (x.cpu().numpy() for x in ops.csa2_sparse_attn(cache, qd, sd, idd, cd, 1 / np.sqrt(512)))
     assert np.array_equal(out0.view(np.uint32), out1.view(np.uint32))
     assert np.array_equal(lse0.view(np.uint32), lse1.view(np.uint32))
     sample = [0, 1, 2, 3, 4, 5, 6, nq // 2, nq - 1]
