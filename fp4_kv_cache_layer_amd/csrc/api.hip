@@ -9,6 +9,7 @@
 
 using namespace csa2;
 
+
 namespace {
 
 // Takes the next slot of a kernel class's timing ring, if the call carries
@@ -114,14 +115,6 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   return r;
 }
 
-// Share buffers of the attention when the workspace holds them (else no split).
-void* attn_part(void* ws, size_t ws_bytes, int32_t nq, int32_t h, int32_t k) {
-  const size_t part = attn_part_bytes(nq, h, k);
-  const size_t z = zero_state_bytes(nq);
-  if (part == 0 || ws == nullptr || ws_bytes < z + part) return nullptr;
-  return reinterpret_cast<uint8_t*>(ws) + z;
-}
-
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
                       int32_t* out_cnt, const IndexWs& iw, bool dense, hipStream_t s) {
@@ -154,7 +147,6 @@ struct Step {
   const csa2_timing* tm;     // nullable
   IndexWs iw;
   float* pool_sc;            // pool scores, in the workspace's score region
-  void* part;
 };
 
 csa2_status validate_pool(const int32_t* pool, const int32_t* pool_cnt, int32_t nq, int32_t p, int32_t k,
@@ -214,19 +206,17 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
   p->tm = a->timing;
   p->iw = IndexWs{};
   p->pool_sc = nullptr;
-  p->part = nullptr;
   if (a->nq == 0) return CSA2_OK;
-  const size_t z = zero_state_bytes(a->nq), part = attn_part_bytes(a->nq, a->h, a->k);
+  const size_t z = zero_state_bytes(a->nq);
   if (mode != CSA2_REUSE) {
     // the pool scores reuse the exhaustive scores' region (dead once the pool is selected)
     const size_t need = std::max(index_score_bytes(a->nq, a->max_vis), pool ? pool_score_bytes(a->nq, a->pool_k) : 0);
-    if (a->ws_bytes < z + part + need) return CSA2_ERR_WORKSPACE;
-    p->iw = index_ws(a->ws, a->nq, a->max_vis, z + part);
-    if (pool) p->pool_sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a->ws) + z + part);
+    if (a->ws_bytes < z + need) return CSA2_ERR_WORKSPACE;
+    p->iw = index_ws(a->ws, a->nq, a->max_vis, z);
+    if (pool) p->pool_sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a->ws) + z);
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;
   }
-  p->part = attn_part(a->ws, a->ws_bytes, a->nq, a->h, a->k);
   return CSA2_OK;
 }
 
@@ -289,7 +279,7 @@ csa2_status stage_attn(const Step& p, hipStream_t s) {
   if (a->nq == 0) return CSA2_OK;
   TimedLaunch t(p.tm, CSA2_KCLASS_ATTN);
   return hip_status(launch_sparse_attn(p.ca, a->q, a->q_seq, a->idx, a->cnt, a->nq, a->h, a->k, a->sm_scale, a->out,
-                                       a->lse, p.part, p.share_heads, s, t.ev));
+                                       a->lse, p.share_heads, s, t.ev));
 }
 
 csa2_status run_step(const Step& p, hipStream_t s) {
@@ -345,7 +335,7 @@ const char* csa2_status_string(csa2_status st) {
 size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
   (void)h_idx; (void)k;
   if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;
-  size_t b = zero_state_bytes(nq) + attn_part_bytes(nq, h, k);
+  size_t b = zero_state_bytes(nq);
   if (mode != CSA2_REUSE) b += std::max(index_score_bytes(nq, max_vis), pool_score_bytes(nq, CSA2_MAX_K));
   return b;
 }
@@ -413,8 +403,8 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
   csa2_status st = validate_attn(c, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   if (ws && !aligned(ws, 16)) return CSA2_ERR_INVALID_ARG;
-  return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse,
-                                       attn_part(ws, ws_bytes, nq, h, k), true, s));
+  (void)ws_bytes;
+  return hip_status(launch_sparse_attn(ca, q, q_seq, idx, cnt, nq, h, k, sm_scale, out, lse, true, s));
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {

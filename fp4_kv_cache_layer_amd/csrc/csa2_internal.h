@@ -115,17 +115,11 @@ hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, in
 hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
                               int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 
-// Attention shares (small batches split their rows across workgroups):
-// [nq * ceil(h/16)][nsplit][16][512] fp32 partial outputs, then
-// [nq * ceil(h/16)][nsplit][32] fp32 (max, sum); no initial state needed.
-int attn_nsplit(int nq, int h, int k);
-size_t attn_part_bytes(int nq, int h, int k);
-
 // share_heads: large batches of 64-head queries take the form that gathers
 // each selected row once for all 64 heads of a query (identical bits).
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, bool share_heads, hipStream_t s, const KEvents& ev = {});
+                              bool share_heads, hipStream_t s, const KEvents& ev = {});
 
 // Hierarchical indexer: scores of each query's pool entries only (pool
 // [nq][p] ascending entry indices, pool_cnt valid; scores [nq][round_up(p, 64)]

@@ -538,99 +538,296 @@ sparse_attn_hg_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
     lse[(int64_t)qi * h + head] = l_run > 0.0f ? m_run * sm_scale + __logf(l_run) : -INFINITY;
 }
 
-// Merges the nsplit shares of one (query, head): O = sum_s e^(m_s - M) O_s / L,
-// L = sum_s e^(m_s - M) l_s, LSE = M + ln L.  One workgroup per head, one
-// float4 of the output per thread, so every share is read in one round trip.
-__global__ void __launch_bounds__(128)
-attn_combine_kernel(int h, int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                    float* __restrict__ out, float* __restrict__ lse) {
+// Decode batches: one workgroup per (query, 16-head group, half of the
+// latent's output dims), so a batch of 32 queries with 64 heads fills all 256
+// CUs, with the 8 workgroups of a query on one XCD (blocks go to XCDs
+// round-robin), where they share the gathered rows through its L2.  Each of
+// its W waves owns whole 32-row tiles (tiles wv, wv + W, ...):
+//   - Q.X^T over all 512 dims straight from registers: lane (row r, group g)
+//     gathers bytes [64c + 16g, +16) of chunk c of its row (dims
+//     [128c + 32g, +32), one scale block), dequantises 8 dims per K-step with
+//     V_CVT_SCALEF32_PK_BF16_FP4 into the A operand of a bf16 16x16x32 MFMA
+//     whose K order is permuted alike in the Q operand; no LDS, no exchange
+//     of partial scores, no barrier;
+//   - the online softmax of its rows in registers (as sparse_attn_kernel);
+//   - O[16 heads][its 256 dims] += P X with the dequantised rows of its half
+//     written to the wave's own LDS rows (the values the QK step converted)
+//     and read back transposed (DS_READ_B64_TR_B16), P split into bf16 hi+lo.
+// The waves merge their (O, running max, running sum) through LDS at the end,
+// each wave producing 16 / W n-tiles of the output.
+constexpr int kDsHalf = 256;                        // output dims per workgroup
+constexpr int kDsStride = 2 * kDsHalf + 32;         // bytes per staged bf16 row (512 + 32 pad)
+
+template <int W>
+struct AttnDsShared {
+  uint8_t xs[W][kTileRows * kDsStride];    // [wave] staged rows of its current tile, this half (17,408 B each)
+  uint32_t row[kMaxShareRows];             // physical row of every selected entry (8,192 B)
+  float m[W][16];
+  float l[W][16];
+};
+
+template <int W>
+__global__ void __launch_bounds__(64 * W, 1)
+sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t* __restrict__ q_seq,
+                      const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int nq, int h, int k,
+                      float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ AttnDsShared<W> S;
+  static_assert(sizeof(S.xs) >= (size_t)W * 16 * 64 * 16, "merge buffer aliases the staged rows");
   const int ngroups = (h + 15) >> 4;
-  const int unit = blockIdx.x >> 4, hh = blockIdx.x & 15;
-  const int qi = unit / ngroups, hg = unit - qi * ngroups;
-  const int hd = hg * 16 + hh;
-  if (hd >= h) return;
-  const int tid = threadIdx.x;
-  const float* ml = part_ml + (int64_t)unit * nsplit * 32;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ml[sp * 32 + hh]);
-  float L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4* po = reinterpret_cast<const float4*>(part_o + ((int64_t)unit * nsplit * 16 + hh) * kLatent);
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float ms = ml[sp * 32 + hh];
-    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
-    L += f * ml[sp * 32 + 16 + hh];
-    const float4 x = po[(int64_t)sp * 16 * kLatent / 4 + tid];
-    acc.x += f * x.x; acc.y += f * x.y; acc.z += f * x.z; acc.w += f * x.w;
+  const int upq = 2 * ngroups;                           // units per query: head groups x halves
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int qx = slot / upq, u = slot - qx * upq;
+  const int qi = qx * 8 + xcd;
+  if (qi >= nq) return;                                  // uniform
+  const int hg = u >> 1, half = u & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int head = hg * 16 + r;
+  const int n = max(0, min(cnt[qi], k));                // counts outside [0, k] are clamped
+  const int ntiles = (n + kTileRows - 1) / kTileRows;
+
+  // Q^T operand: head r; chunk ch, K-step t holds dims 128 ch + 32 g + 8 t .. +7
+  bf16x8 qop[4][4];
+  {
+    const bool ok = head < h;
+    const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)qi * h + (ok ? head : 0)) * kLatent + 32 * g);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        qop[ch][t] = __builtin_bit_cast(bf16x8, ok ? src[16 * ch + t] : make_uint4(0, 0, 0, 0));
   }
-  const float linv = L > 0.0f ? 1.0f / L : 0.0f;
-  acc.x *= linv; acc.y *= linv; acc.z *= linv; acc.w *= linv;
-  reinterpret_cast<float4*>(out + ((int64_t)qi * h + hd) * kLatent)[tid] = acc;
-  if (lse != nullptr && tid == 0) lse[(int64_t)qi * h + hd] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+  {
+    // physical rows of the selection, resolved once (index loads clamped to
+    // the row of k entries so they need not wait for the count)
+    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
+    const int32_t* irow = idx + (int64_t)qi * k;
+    for (int j = tid; j < ntiles * kTileRows; j += 64 * W) {
+      const int t = irow[min(j, k - 1)];
+      if (j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, t, c);
+    }
+  }
+  lds_barrier();
+
+  floatx4 oacc[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) oacc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -FLT_MAX, l_run = 0.0f;
+  const float c2 = sm_scale * 1.44269504088896341f;
+  const float slack = kRescaleSlack / sm_scale;
+  uint8_t* const xs = &S.xs[wv][0];
+  const int my_tiles = ntiles > wv ? (ntiles - wv + W - 1) / W : 0;
+
+  // Gathers of one tile (rows past the selection read physical row 0, which
+  // always exists): per M-tile, the row's four 16-byte code pieces of this
+  // lane's group and its 16 scale bytes.  Loads are unconditional.
+  struct Gath {
+    uint4 cd[2][4];
+    uint4 sc[2];
+  };
+  auto gather = [&](int tt, Gath& G) {
+    const int T = wv + W * min(tt, my_tiles - 1);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j = T * kTileRows + mt * 16 + r;
+      const uint8_t* src = c.kv + (size_t)(j < n ? S.row[j] : 0u) * kKvRowBytes;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) G.cd[mt][ch] = *reinterpret_cast<const uint4*>(src + 64 * ch + 16 * g);
+      G.sc[mt] = *reinterpret_cast<const uint4*>(src + kCodeBytes);
+    }
+  };
+  auto process = [&](int tt, const Gath& G) {
+    const int T = wv + W * tt;
+    const int lim = n - T * kTileRows;                   // rows of this tile inside the selection
+    floatx4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      // a row past the selection keeps its (finite) codes but gets scale 1:
+      // its logit is masked below, so it only ever meets a zero probability
+      const bool valid = mt * 16 + r < lim;
+      const uint32_t scw[4] = {G.sc[mt].x, G.sc[mt].y, G.sc[mt].z, G.sc[mt].w};
+      uint8_t* const rowp = xs + (mt * 16 + r) * kDsStride + 64 * g;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const float scale = e8m0_to_float(valid ? (scw[ch] >> (8 * g)) & 0xFFu : 127u);
+        const uint32_t wds[4] = {G.cd[mt][ch].x, G.cd[mt][ch].y, G.cd[mt][ch].z, G.cd[mt][ch].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 a = dequant8(wds[t], scale);
+          st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ch][t], st[mt], 0, 0, 0);
+          if ((ch >> 1) == half)                         // this half's dims go to the staged rows
+            *reinterpret_cast<bf16x8*>(rowp + 256 * (ch & 1) + 16 * t) = a;
+        }
+      }
+    }
+    float v[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[mt][i] = st[mt][i];
+    if (lim < kTileRows) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (mt * 16 + 4 * g + i >= lim) v[mt][i] = -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3])),
+                       fmaxf(fmaxf(v[1][0], v[1][1]), fmaxf(v[1][2], v[1][3])));
+    tmax = halves_max(rows_pair_max(tmax));
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + slack)) {
+      const float m_new = tmax > m_run + slack ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+      m_run = m_new;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
+    }
+    const float mc = -m_run * c2;
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[mt][i], c2, mc));
+        psum += p[mt][i];
+      }
+    psum = halves_sum(rows_pair_sum(psum));
+    l_run += psum;
+    uint32_t whi[4], wlo[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const float a = p[pr >> 1][2 * (pr & 1)], b2 = p[pr >> 1][2 * (pr & 1) + 1];
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{a, b2}), bf16x2));
+      const float ra = a - __uint_as_float(hi << 16), rb = b2 - __uint_as_float(hi & 0xFFFF0000u);
+      whi[pr] = hi;
+      wlo[pr] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{ra, rb}), bf16x2));
+    }
+    const bf16x8 pa_hi = __builtin_bit_cast(bf16x8, make_uint4(whi[0], whi[1], whi[2], whi[3]));
+    const bf16x8 pa_lo = __builtin_bit_cast(bf16x8, make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]));
+    // the staged rows were written by this wave: LDS keeps a wave's accesses
+    // in order, and the wave barrier keeps the compiler from moving the reads
+    // above the writes
+    __builtin_amdgcn_wave_barrier();
+    const int off_a = (4 * g + (r >> 2)) * kDsStride + 8 * (r & 3);
+    const int off_b = off_a + 16 * kDsStride;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+      const shortx4 lo = lds_read_tr16(xs, off_a + 32 * nt);
+      const shortx4 hi = lds_read_tr16(xs, off_b + 32 * nt);
+      typedef short shortx8 __attribute__((ext_vector_type(8)));
+      const shortx8 b8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, b8);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb, oacc[nt], 0, 0, 0);
+      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb, oacc[nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();                     // the next tile's row writes stay below these reads
+  };
+  if (my_tiles > 0) {
+    Gath ga, gb;
+    gather(0, ga);
+    for (int tt = 0; tt < my_tiles; tt += 2) {
+      gather(tt + 1, gb);
+      process(tt, ga);
+      if (tt + 1 >= my_tiles) break;
+      gather(tt + 2, ga);
+      process(tt + 1, gb);
+    }
+  }
+
+  // merge the waves: every wave publishes (O, m, l); wave wv then combines
+  // n-tiles [wv * 16 / W, (wv + 1) * 16 / W) of all of them
+  lds_barrier();                                         // every wave is done with its staged rows
+  floatx4* const mb = reinterpret_cast<floatx4*>(&S.xs[0][0]);
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) mb[(wv * 16 + nt) * 64 + lane] = oacc[nt];
+  if (g == 0) {
+    S.m[wv][r] = m_run;
+    S.l[wv][r] = l_run;
+  }
+  lds_barrier();
+  float Mx[4], linv[4], ap[W][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * g + i;                            // O rows of this lane are heads 4g + i
+    float M = -FLT_MAX;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) M = fmaxf(M, S.m[w2][hh]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+      ap[w2][i] = __builtin_amdgcn_exp2f((S.m[w2][hh] - M) * c2);
+      L += ap[w2][i] * S.l[w2][hh];
+    }
+    Mx[i] = M;
+    linv[i] = L > 0.0f ? 1.0f / L : 0.0f;
+    if (lse != nullptr && half == 0 && wv == 0 && r == 0 && hg * 16 + hh < h)
+      lse[(int64_t)qi * h + hg * 16 + hh] = L > 0.0f ? M * sm_scale + __logf(L) : -INFINITY;
+  }
+  (void)Mx;
+  constexpr int kNtPer = 16 / W;
+#pragma unroll
+  for (int u2 = 0; u2 < kNtPer; ++u2) {
+    const int nt = wv * kNtPer + u2;
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) {
+      const floatx4 o = mb[(w2 * 16 + nt) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += ap[w2][i] * o[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hd = hg * 16 + 4 * g + i;
+      if (hd < h) out[((int64_t)qi * h + hd) * kLatent + kDsHalf * half + 16 * nt + r] = acc[i] * linv[i];
+    }
+  }
 }
 
 // Shared-row workgroups (sparse_attn_hg_kernel) need a batch that gives every
 // CU a few of them; below that the 16-head form spreads the work wider.
 constexpr int64_t kHgMinUnits = 512;
-
-// Row groups per workgroup: small batches (decode) split each query's rows
-// among 2 row groups of 4 waves inside one workgroup, merged through LDS;
-// large batches already cover the chip with one 4-wave workgroup per unit.
-static int attn_rgroups(int nq, int h) {
-  const int units = nq * ((h + 15) / 16);
-  return units < 256 ? 2 : 1;
-}
-
-int attn_nsplit(int nq, int h, int k) {
-  const int units = nq * ((h + 15) / 16);
-  const int ntiles = (k + kTileRows - 1) / kTileRows;
-  const int rg = attn_rgroups(nq, h);
-  // Splitting pays only while few units run: a split halves the tile loop but
-  // adds the share write-out and a combine launch, which at 128 units (32
-  // decode queries x 64 heads) already cost more than they save.
-  const int target = rg > 1 ? 128 : 512;
-  int ns = 1;
-  // split across workgroups only while every row group keeps two tiles per share
-  while (ns < 16 && units * ns < target && ntiles >= 2 * rg * 2 * ns) ns *= 2;
-  while ((ntiles + ns - 1) / ns * kTileRows > kMaxShareRows) ns *= 2;   // shares must fit the row table
-  return ns;
-}
-
-size_t attn_part_bytes(int nq, int h, int k) {
-  const int ns = attn_nsplit(nq, h, k);
-  if (ns == 1 || nq <= 0) return 0;
-  const size_t units = (size_t)nq * ((h + 15) / 16);
-  return (units * ns * (16 * kLatent + 32) * 4 + 255) / 256 * 256;
-}
+// Batches of fewer (query, 16-head group) units than this (decode) take
+// sparse_attn_ds_kernel, with kDsWaves waves per workgroup; larger ones the
+// shared-row form or one workgroup per (query, 16-head group).
+constexpr int64_t kDsMaxUnits = 512;
+constexpr int kDsWaves = 4;
 
 hipError_t launch_sparse_attn(const CacheArgs& c, const uint16_t* q, const int32_t* q_seq, const int32_t* idx,
                               const int32_t* cnt, int nq, int h, int k, float sm_scale, float* out, float* lse,
-                              void* part, bool share_heads, hipStream_t s, const KEvents& ev) {
+                              bool share_heads, hipStream_t s, const KEvents& ev) {
   if (nq <= 0 || h <= 0) {
     record_empty(ev, s);
     return hipSuccess;
   }
   const int ngroups = (h + 15) / 16;
-  const int ns = part ? attn_nsplit(nq, h, k) : 1;
   const int64_t units = (int64_t)nq * ngroups;
-  float* part_o = reinterpret_cast<float*>(part);
-  float* part_ml = part_o ? part_o + units * ns * 16 * kLatent : nullptr;
-  const int64_t npairs = (int64_t)nq * ns;
-  const int64_t blocks = (npairs + 7) / 8 * 8 * ngroups;
+  if (units < kDsMaxUnits) {
+    // decode batches: (query, head group, half of the dims) workgroups
+    const int64_t blocks = (int64_t)((nq + 7) / 8) * 2 * ngroups * 8;
+    launch(sparse_attn_ds_kernel<kDsWaves>, dim3((unsigned)blocks), dim3(64 * kDsWaves), s, ev, c, q, q_seq, idx,
+           cnt, nq, h, k, sm_scale, out, lse);
+    return hipGetLastError();
+  }
   const int64_t hg_units = (h % (16 * kHg) == 0) ? (int64_t)nq * (h / (16 * kHg)) : 0;
-  if (share_heads && ns == 1 && hg_units >= kHgMinUnits) {
+  if (share_heads && hg_units >= kHgMinUnits) {
     const int per_xcd = (int)((hg_units + 7) / 8);
     launch(sparse_attn_hg_kernel, dim3((unsigned)(per_xcd * 8)), dim3(256 * kHg), s, ev, c, q, q_seq, idx, cnt, h, k,
            sm_scale, out, lse, (int)hg_units, per_xcd);
-  } else if (attn_rgroups(nq, h) == 2)
-    launch(sparse_attn_kernel<2>, dim3((unsigned)blocks), dim3(256 * 2), s, ns > 1 ? ev.first() : ev, c, q, q_seq,
-           idx, cnt, h, k, sm_scale, out, lse, ns, (int)npairs, part_o, part_ml);
-  else
-    launch(sparse_attn_kernel<1>, dim3((unsigned)blocks), dim3(256), s, ns > 1 ? ev.first() : ev, c, q, q_seq, idx,
-           cnt, h, k, sm_scale, out, lse, ns, (int)npairs, part_o, part_ml);
-  if (ns > 1)
-    launch(attn_combine_kernel, dim3((unsigned)(units * 16)), dim3(128), s, ev.last(), h, ns, part_o, part_ml, out,
-           lse);
+  } else {
+    const int64_t blocks = (int64_t)(nq + 7) / 8 * 8 * ngroups;
+    launch(sparse_attn_kernel<1>, dim3((unsigned)blocks), dim3(256), s, ev, c, q, q_seq, idx, cnt, h, k, sm_scale,
+           out, lse, 1, nq, static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+  }
   return hipGetLastError();
 }
 

@@ -119,14 +119,11 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
 
 /* Bytes of workspace a layer_step call of this shape needs.  Layout:
  * per-query histograms [nq][2048] u32 and candidate counters [nq] u32
- * first; then, for batches small enough that the attention splits each
- * query's rows across workgroups, the attention shares; then (Full and
- * Reindex) per-query scores [nq][round_up(max_vis, 64)] fp32, candidate
- * indices and their score keys of the same shape, that region being at
- * least nq * 8 KB so a
- * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk and
- * csa2_sparse_attn accept a
- * workspace sized by this call for the same shape.  Only the first
+ * first; then (Full and Reindex) per-query scores [nq][round_up(max_vis + 2,
+ * 64)] fp32, candidate indices and their score keys of the same shape and the
+ * dense indexer's candidate masks, that region being at least nq * 8 KB so a
+ * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk accepts a
+ * workspace sized by this call for the same shape; attention needs none.  Only the first
  * round_up(nq * 2049 * 4, 256) bytes (histograms and counters) carry state:
  * every call leaves them zeroed for the next one, so zero the whole
  * workspace once after allocating it (csa2_workspace_init does this); the
@@ -181,11 +178,10 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
  *   idx [nq][k] selected entry indices (first cnt[i] valid), cnt [nq]
  *   (a count outside [0, k] is taken as the nearest bound),
  *   out [nq][h][512] fp32, lse [nq][h] fp32 (nullable).
- * 1 <= h <= 128; sm_scale > 0 and finite.  ws may be NULL; with a
- * workspace of csa2_workspace_bytes(CSA2_REUSE, nq, 0, 1, h, k) bytes, small
- * batches split each query's rows across workgroups and merge the shares in
- * a second kernel.  Selected indices are clamped to the page table's range and
- * page ids to [0, num_pages) before any row is read.
+ * 1 <= h <= 128; sm_scale > 0 and finite.  The attention needs no
+ * workspace: ws may be NULL (a non-NULL ws must be 16-byte aligned and is
+ * left untouched).  Selected indices are clamped to the page table's range
+ * and page ids to [0, num_pages) before any row is read.
  * Errors: CSA2_ERR_INVALID_ARG for bad sizes, a bad sm_scale, null or
  * misaligned pointers; CSA2_ERR_HIP if a launch fails. */
 csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const int32_t* q_seq,
