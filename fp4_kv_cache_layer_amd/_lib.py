@@ -18,6 +18,7 @@ KCLASS_POOL_SCAN, KCLASS_POOL_SELECT = 5, 6
 NUM_KCLASSES = 7
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
+STATIC_SCRATCH_BYTES = 64 << 20
 STEP_DENSE_INDEX, STEP_POOL, STEP_ATTN_PER_HEAD_GROUP = 1, 2, 4
 DENSE_RESCORE_ALL = -1
 
@@ -82,6 +83,7 @@ def load() -> ctypes.CDLL:
     lib.csa2_sparse_attn.argtypes = [P(CacheView), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.csa2_layer_step.argtypes = [c_int32, P(StepArgs), c_void_p]
+    lib.csa2_layer_step_static.argtypes = [c_int32, P(StepArgs), c_void_p]
     lib.csa2_lse_merge.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                    c_void_p]
     lib.csa2_fake_quant_fp4.argtypes = [c_void_p, c_void_p, ctypes.c_int64, c_int32, c_void_p]
@@ -92,7 +94,7 @@ def load() -> ctypes.CDLL:
     lib.csa2_status_string.restype = ctypes.c_char_p
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_pool_index_topk", "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4"):
+               "csa2_layer_step", "csa2_layer_step_static", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

@@ -6,9 +6,15 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 using namespace csa2;
 
+// Workspace of csa2_layer_step_static: a fixed array in device memory, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never uses the name itself (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[CSA2_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -410,6 +416,39 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
   Step p;
   csa2_status st = prepare_step(mode, a, &p);
+  if (st != CSA2_OK) return st;
+  return run_step(p, s);
+}
+
+csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
+  // The scratch array's address on the current device, looked up once per
+  // device with that device current.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  if (!a) return CSA2_ERR_INVALID_ARG;
+  if (a->ws || a->ws_bytes) return CSA2_ERR_INVALID_ARG;     // the workspace is the library's own
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_ERR_HIP;
+  void* ptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_ERR_HIP;
+      dev_ptr[dev] = p;
+    }
+    ptr = dev_ptr[dev];
+  }
+  csa2_step_args b = *a;
+  b.ws = ptr;
+  b.ws_bytes = CSA2_STATIC_SCRATCH_BYTES;
+  Step p;
+  csa2_status st = prepare_step(mode, &b, &p);              // CSA2_ERR_WORKSPACE: the shape needs more
+  if (st != CSA2_OK || b.nq == 0) return st;
+  // the state-carrying head of the workspace starts at zero (a fill kernel,
+  // which a graph capture may record; no memset node)
+  st = hip_status(launch_fill_zero(ptr, zero_state_bytes(b.nq), s));
   if (st != CSA2_OK) return st;
   return run_step(p, s);
 }

@@ -323,6 +323,26 @@ size_t csa2_pool_workspace_bytes(int32_t nq, int32_t p);
  * CSA2_ERR_HIP if a launch fails, else CSA2_OK. */
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s);
 
+/* csa2_layer_step for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same layer step, with the workspace taken from a fixed array of
+ * CSA2_STATIC_SCRATCH_BYTES bytes of device memory that the library holds on
+ * each GPU it runs on until the process ends, instead of a->ws.  Allocates
+ * nothing (no hipMalloc, hipFree or allocating library call).  a->ws must be
+ * NULL and a->ws_bytes 0; every other field is as for csa2_layer_step, whose
+ * results it gives bit for bit.  The stream must belong to the current
+ * device; the first call on a device looks up that device's array.  Every
+ * call clears the array's state-carrying head (the per-query histograms and
+ * counters) before its kernels run, so a call never depends on an earlier
+ * one.  All calls on one GPU share its array: calls that overlap in time on
+ * one GPU race, so serialise them (one stream, or events).  Errors: those of
+ * csa2_layer_step; CSA2_ERR_WORKSPACE when the shape needs more than
+ * CSA2_STATIC_SCRATCH_BYTES (csa2_workspace_bytes(mode, ...) gives the need);
+ * CSA2_ERR_INVALID_ARG for a non-NULL ws; CSA2_ERR_HIP if the array's address
+ * cannot be found or a launch fails. */
+#define CSA2_STATIC_SCRATCH_BYTES (64u << 20)
+csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_step_args* a, hipStream_t s);
+
 /* A group of layers that share caches and indices, run as one call.  The
  * layers' results are exactly those of calling csa2_layer_step on each in
  * order on s (same kernels, same inputs); the group only overlaps work that
