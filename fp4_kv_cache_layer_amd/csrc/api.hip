@@ -107,7 +107,7 @@ csa2_status validate_append(const csa2_cache_view* c, const int32_t* slots, cons
   return CSA2_OK;
 }
 
-IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
+IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool dense) {
   IndexWs r;
   r.vis_cap = max_vis;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
@@ -118,26 +118,24 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off) {
   r.cand = reinterpret_cast<int32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
   r.ckey = reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
   r.mask = reinterpret_cast<uint64_t*>(p + score_off + 3 * (size_t)nq * (size_t)r.vstride * 4);
+  // the per-query scan keeps no scores: its per-chunk key floors use the region
+  r.floor = dense ? nullptr : reinterpret_cast<uint32_t*>(r.scores);
+  r.fstride = (max_vis + kScanChunk - 1) / kScanChunk;
   return r;
 }
 
 csa2_status run_index(const CacheArgs& ca, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                       const int32_t* q_vis, int32_t nq, int32_t h_idx, int32_t k, int32_t max_vis, int32_t* out_idx,
                       int32_t* out_cnt, const IndexWs& iw, bool dense, hipStream_t s) {
-  if (dense) {
-    // the dense indexer leaves a compacted candidate list: only the final select remains
-    if (max_vis > 0) {
-      csa2_status st = hip_status(
-          launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, kDefaultCandFactor, s));
-      if (st != CSA2_OK) return st;
-    }
-    return hip_status(launch_topk_final(iw, q_vis, nq, k, out_idx, out_cnt, s));
-  }
+  // both indexers leave a candidate list: the final select completes the Top-k
   if (max_vis > 0) {
-    csa2_status st = hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, max_vis, iw, s));
+    csa2_status st =
+        dense ? hip_status(launch_prefill_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw,
+                                               kDefaultCandFactor, s))
+              : hip_status(launch_index_scan(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, iw, s));
     if (st != CSA2_OK) return st;
   }
-  return hip_status(launch_topk_select(iw, q_vis, nq, k, max_vis, out_idx, out_cnt, s));
+  return hip_status(launch_topk_final(iw, ScanArgs{ca, q_idx, w, q_seq, h_idx}, q_vis, nq, k, out_idx, out_cnt, s));
 }
 
 // One layer of a step, validated, split into the stages that the group
@@ -218,7 +216,7 @@ csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
     // the pool scores reuse the exhaustive scores' region (dead once the pool is selected)
     const size_t need = std::max(index_score_bytes(a->nq, a->max_vis), pool ? pool_score_bytes(a->nq, a->pool_k) : 0);
     if (a->ws_bytes < z + need) return CSA2_ERR_WORKSPACE;
-    p->iw = index_ws(a->ws, a->nq, a->max_vis, z);
+    p->iw = index_ws(a->ws, a->nq, a->max_vis, z, p->dense);
     if (pool) p->pool_sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a->ws) + z);
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;
@@ -244,8 +242,8 @@ csa2_status stage_scan(const Step& p, hipStream_t s) {
                                           tp.ev));
   }
   TimedLaunch t(p.tm, CSA2_KCLASS_SCAN);
-  return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->max_vis, p.iw, s,
-                                      t.ev));
+  return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx,
+                                      p.pool ? a->pool_k : a->k, a->max_vis, p.iw, s, t.ev));
 }
 
 csa2_status run_pool(const Step& p, hipStream_t s) {
@@ -270,14 +268,11 @@ csa2_status stage_select(const Step& p, hipStream_t s) {
   csa2_status st;
   {
     TimedLaunch t(p.tm, CSA2_KCLASS_SELECT);
-    st = p.dense ? hip_status(launch_topk_final(p.iw, a->q_vis, a->nq, k, idx, cnt, s, t.ev))
-                 : hip_status(launch_topk_select(p.iw, a->q_vis, a->nq, k, a->max_vis, idx, cnt, s, t.ev));
+    st = hip_status(launch_topk_final(p.iw, ScanArgs{p.ca, a->q_idx, a->w, a->q_seq, a->h_idx}, a->q_vis, a->nq, k,
+                                      idx, cnt, s, t.ev));
   }
   if (st != CSA2_OK || !to_pool) return st;
-  if (p.dense) return run_pool(p, s);         // the dense indexer keeps candidate scores only: rescore the pool
-  TimedLaunch t(p.tm, CSA2_KCLASS_POOL_SELECT);   // every visible entry's score is in the workspace
-  return hip_status(launch_pool_select_by_entry(a->pool, a->pool_cnt, a->nq, a->pool_k, p.iw.scores, p.iw.vstride,
-                                                a->k, a->idx, a->cnt, s, t.ev));
+  return run_pool(p, s);                      // the indexers keep no score rows: score the pool again
 }
 
 csa2_status stage_attn(const Step& p, hipStream_t s) {
@@ -372,7 +367,7 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
-                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), false, s);
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), false), false, s);
 }
 
 csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
@@ -382,7 +377,7 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
-                   index_ws(ws, nq, max_vis, zero_state_bytes(nq)), true, s);
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), true), true, s);
 }
 
 csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,

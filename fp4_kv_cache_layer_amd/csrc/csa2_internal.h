@@ -48,6 +48,12 @@ struct IndexWs {
   uint64_t* mask;
   int64_t vstride;
   int32_t vis_cap;       // max_vis of the call: visible counts are clamped to it
+  // Per-query scan: the key floor below which each 2,048-entry chunk kept no
+  // candidate, [nq][fstride] u32 (in the score region, which that path does
+  // not use otherwise); NULL for the dense indexer, whose candidates are
+  // exact above its threshold.
+  uint32_t* floor;
+  int32_t fstride;
 };
 
 // A query's visible count as the indexer kernels use it: clamped to [0, max_vis].
@@ -92,9 +98,22 @@ hipError_t launch_append_quant(uint8_t* kv, uint8_t* idx_k, const int32_t* slots
                                const uint16_t* idxk_rows, int n, hipStream_t s, const KEvents& ev = {});
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// Per-query scan: scores every visible entry and keeps, per 2,048-entry chunk,
+// the entries at or above the chunk's local rank threshold as candidates
+// (indices, score keys, their histogram, and the chunk's key floor); the final
+// select then completes the exact Top-k (k is needed for the local rank).
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
-                             const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                             const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                              hipStream_t s, const KEvents& ev = {});
+// Inputs of the final select's repair of a chunk whose local threshold lies
+// above the k-th key's bin (per-query scan only).
+struct ScanArgs {
+  CacheArgs c;
+  const uint8_t* q_idx;
+  const float* w;
+  const int32_t* q_seq;
+  int h_idx;
+};
 
 // Dense form for many queries of one sequence (q_seq[0]): leaves the same
 // inputs for the final select (candidate list, candidate histogram, scores of
@@ -108,12 +127,10 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                                int cand_factor, hipStream_t s, const KEvents& ev = {},
                                const KEvents& ev_product = {});
-// Launches of the final select alone (the dense indexer compacts its own candidates).
-hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
-                             int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
-
-hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
-                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
+// The final select over a query's candidate list (the dense indexer's, or the
+// per-query scan's, which sa and ws.floor let it repair).
+hipError_t launch_topk_final(const IndexWs& ws, const ScanArgs& sa, const int32_t* q_vis, int nq, int k,
+                             int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
 
 // share_heads: large batches of 64-head queries take the form that gathers
 // each selected row once for all 64 heads of a query (identical bits).
@@ -129,12 +146,6 @@ hipError_t launch_pool_index(const CacheArgs& c, const uint8_t* q_idx, const flo
                              const int32_t* pool, const int32_t* pool_cnt, int nq, int h_idx, int p, int k,
                              int32_t* out_idx, int32_t* out_cnt, float* sc, hipStream_t s,
                              const KEvents& ev_scan = {}, const KEvents& ev_select = {});
-// Top-k of each query's pool from an exhaustive scan's score rows (score of
-// entry t at scores[q * vstride + t]): no rescoring.
-hipError_t launch_pool_select_by_entry(const int32_t* pool, const int32_t* pool_cnt, int nq, int p,
-                                       const float* scores, int64_t vstride, int k, int32_t* out_idx,
-                                       int32_t* out_cnt, hipStream_t s, const KEvents& ev = {});
-
 // Branch merge: O and LSE of one softmax over the union of two key sets
 // ([rows][dim] fp32 outputs, [rows] LSEs; dim a multiple of 4).
 hipError_t launch_lse_merge(const float* oa, const float* la, const float* ob, const float* lb, int rows, int dim,

@@ -1,6 +1,6 @@
 // Indexer scan: s_t = sum_h w_h * max(0, q_h . k_t) over every visible entry
-// of a query's sequence, with the scores written to the workspace and a
-// histogram of their top 11 key bits accumulated for the Top-K select.
+// of a query's sequence, and the first half of the exact Top-k: each
+// 2,048-entry chunk keeps its own top entries as candidates.
 //
 // The scan over the cached indexer-K is the step the Full and Reindex modes
 // spend their indexing compute on ("Unlocking Extreme Context Scaling with
@@ -14,8 +14,22 @@
 // layout through the wave's LDS slot.  The result puts entry (l % 16) and
 // heads 4*(l/16)+i in lane l, so the ReLU * w reduction is 4 FMAs and two
 // lane-swap adds.
+//
+// Scores stay in LDS (no score is written to memory).  When the chunk is
+// done, a two-level radix search over its 2,048-bin histogram of score-key
+// prefixes finds the key of its L-th largest entry to 22 bits (L from
+// scan_local_rank), and every entry whose key reaches that floor is appended
+// to the query's candidate list (index and key, one reservation per
+// workgroup); the floor is stored per chunk.  (Counting the candidates into a
+// per-query histogram here, one global atomic per candidate, cost more than
+// the whole scan: the candidates of all chunks fall into the same few top
+// bins.  The final select counts them from the list instead.)  The final select takes the k-th key among the
+// candidates; every chunk whose floor lies at or below that key's bin kept
+// all entries that can belong to the Top-k, and any other chunk is rescored
+// there (rare: it needs more than L of the Top-k in one chunk).
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
@@ -40,16 +54,23 @@ size_t index_score_bytes(int32_t nq, int32_t max_vis) {
 __global__ void __launch_bounds__(kScanWaves * 64)
 index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
-                  int nq, int h_idx, IndexWs ws) {
+                  int nq, int h_idx, int k, IndexWs ws) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];
-  // chunk-major: the short last chunks of equal-length queries come last, so
-  // a grid larger than one round leaves only short work for the second round
-  const int chunk = blockIdx.x / nq;
-  const int q = blockIdx.x - chunk * nq;
+  __shared__ float sc[kScanChunk + 1];                // the chunk's scores (+ a sink slot)
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];   // then the candidate list
+  __shared__ uint32_t res[2];
+  __shared__ int nlist, base;
+  // query-major: the chunks of one query are consecutive blocks.  On ragged
+  // batches the grid is sized by the longest query and most blocks of the
+  // short ones exit at once; in this order the working blocks of every query
+  // are dispatched together (chunk-major order left the long queries' chunks
+  // to a thin tail: 0.43 -> 0.62 of HBM on the ragged decode workload)
+  const int nch = gridDim.x / nq;
+  const int q = blockIdx.x / nch;
+  const int chunk = blockIdx.x - q * nch;
   const int vis = clamp_vis(q_vis[q], ws);
   const int t0 = chunk * kScanChunk;
-  if (t0 >= vis) return;                              // uniform for the block
+  if (t0 >= vis || vis <= k) return;                  // uniform; with V <= k the select takes everything
   const int t1 = min(vis, t0 + kScanChunk);
   const int tid = threadIdx.x;
   for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
@@ -72,16 +93,13 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int pg0 = t0 >> c.lg_page;
   const int npg = ((t1 - 1) >> c.lg_page) - pg0 + 1;
   const int page_of_lane = lane < npg ? clamp_page(pt_row[pg0 + lane], c) : 0;
-  float* srow = ws.scores + (int64_t)q * ws.vstride;
   const int ntiles = (t1 - t0 + 15) >> 4;
   lds_barrier();
 
   // Tiles j = wave, wave + 4, ... of this wave, kScanDepth - 1 in flight ahead
   // of the one in use (a ring of buffers addressed by name after unrolling).  A tile's 16 rows are 2 KB of
   // contiguous memory: loaded coalesced, turned into the MFMA operand through
-  // the wave's LDS slot.  Loads past the end re-read the last tile; stores are
-  // unconditional (lanes with nothing to write use the sink slot past every
-  // visible entry), so the compiler can count loads in flight past them.
+  // the wave's LDS slot.  Loads past the end re-read the last tile.
   uint8_t* const slot = stage[wave];
   auto load = [&](int j, intx8& lin) {
     j = min(j, ntiles - 1);
@@ -90,17 +108,13 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
     lin = load_fp8_tile_linear(c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim,
                                lane);
   };
-  const int sink = (int)ws.vstride - 1;
   auto process = [&](int j, const intx8& lin) {
-    const intx8 b = fp8_tile_operand(slot, lin, lane);
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
-    const float part = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));   // every lane: entry r's score
-    const int t = t0 + 16 * j + r;
-    uint32_t u32 = __float_as_uint(part);
-    if ((u32 << 1) == 0) u32 = 0;                     // -0 -> +0
-    srow[t < t1 ? t : sink] = __uint_as_float(u32);
-    if (g == 0 && t < t1) atomicAdd(&hist[score_key(__uint_as_float(u32)) >> (32 - kHistBits)], 1u);
+    const float sv = tile_score(a, wv, slot, lin, lane);   // every lane: entry r's score
+    const int i = 16 * j + r;                         // position in the chunk
+    if (g == 0) {
+      sc[t0 + i < t1 ? i : kScanChunk] = sv;
+      if (t0 + i < t1) atomicAdd(&hist[score_key(sv) >> (32 - kHistBits)], 1u);
+    }
   };
   intx8 buf[kScanDepth];
 #pragma unroll
@@ -125,15 +139,65 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
     }
   }
   lds_barrier();
-  uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
-  for (int i = tid; i < kHistBins; i += kScanWaves * 64) {
-    const uint32_t v = hist[i];
-    if (v) atomicAdd(&gh[i], v);
+
+  // the chunk's local threshold: key floor of its L-th largest entry, to 22 bits
+  const int nloc = t1 - t0;
+  const int L = scan_local_rank(k, vis);
+  uint32_t floor_key = 0;                             // a chunk of at most L entries keeps them all
+  if (nloc > L) {
+    find_digit(hist, kHistBins, (uint32_t)L, res);    // ends with a barrier
+    const uint32_t d1 = res[0], need2 = (uint32_t)L - res[1];
+    for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
+    lds_barrier();
+    for (int i = tid; i < nloc; i += kScanWaves * 64) {
+      const uint32_t key = score_key(sc[i]);
+      if ((key >> (32 - kHistBits)) == d1) atomicAdd(&hist[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+    }
+    lds_barrier();
+    find_digit(hist, kHistBins, need2, res);
+    floor_key = (d1 << (32 - kHistBits)) | (res[0] << (32 - 2 * kHistBits));
+  }
+  // candidates: every entry whose key reaches the floor, listed in LDS (one
+  // scan and one reservation per wave), then one reservation per workgroup
+  int32_t* const list = reinterpret_cast<int32_t*>(&stage[0][0]);
+  if (tid == 0) nlist = 0;
+  lds_barrier();
+  constexpr int kPer = kScanChunk / (kScanWaves * 64);
+  uint32_t mine = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = u * kScanWaves * 64 + tid;
+    mine += (i < nloc && score_key(sc[i]) >= floor_key) ? 1u : 0u;
+  }
+  const uint32_t x = wave_incl_sum(mine);
+  int wbase = 0;
+  if (lane == 63 && x) wbase = atomicAdd(&nlist, (int)x);
+  int pos = __shfl(wbase, 63) + (int)(x - mine);
+  if (mine) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kScanWaves * 64 + tid;
+      if (i < nloc && score_key(sc[i]) >= floor_key) list[pos++] = i;
+    }
+  }
+  lds_barrier();
+  const int n = nlist;
+  if (tid == 0) {
+    base = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
+    ws.floor[(int64_t)q * ws.fstride + chunk] = floor_key;
+  }
+  lds_barrier();
+  int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
+  uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride + base;
+  for (int j = tid; j < n; j += kScanWaves * 64) {
+    const int i = list[j];
+    cand[j] = t0 + i;
+    ckey[j] = score_key(sc[i]);
   }
 }
 
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
-                             const int32_t* q_vis, int nq, int h_idx, int max_vis, const IndexWs& ws,
+                             const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                              hipStream_t s, const KEvents& ev) {
   const int nchunks = (max_vis + kScanChunk - 1) / kScanChunk;
   const int64_t blocks = (int64_t)nq * nchunks;
@@ -142,7 +206,7 @@ hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const flo
     return hipSuccess;
   }
   launch(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, nq,
-         h_idx, ws);
+         h_idx, k, ws);
   return hipGetLastError();
 }
 

@@ -79,11 +79,10 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* part) {
   return base + x - v;
 }
 
-// Scores: by_entry == 0: sc[q * sstride + position] (the pool scan's output);
-// by_entry != 0: sc[q * sstride + entry] (an exhaustive scan's score row).
+// Scores: sc[q * sstride + position] (the pool scan's output).
 __global__ void __launch_bounds__(kPoolSelThreads)
 pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__ pool_cnt, int p,
-                   const float* __restrict__ sc, int64_t sstride, int by_entry, int k, int32_t* __restrict__ out_idx,
+                   const float* __restrict__ sc, int64_t sstride, int k, int32_t* __restrict__ out_idx,
                    int32_t* __restrict__ out_cnt) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t res[2];
@@ -103,13 +102,8 @@ pool_select_kernel(const int32_t* __restrict__ pool, const int32_t* __restrict__
   }
 #pragma unroll
   for (int i = 0; i < kPoolPer; ++i) ent[i] = prow[min(kPoolPer * tid + i, n - 1)];
-  if (by_entry) {
 #pragma unroll
-    for (int i = 0; i < kPoolPer; ++i) key[i] = score_key(srow[ent[i]]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kPoolPer; ++i) key[i] = score_key(srow[min(kPoolPer * tid + i, n - 1)]);
-  }
+  for (int i = 0; i < kPoolPer; ++i) key[i] = score_key(srow[min(kPoolPer * tid + i, n - 1)]);
   auto valid = [&](int i) { return kPoolPer * tid + i < n; };
   // threshold T: the kp-th largest key; need: how many keys equal to T are taken
   uint32_t T = 0, need = 0;
@@ -189,19 +183,7 @@ hipError_t launch_pool_index(const CacheArgs& c, const uint8_t* q_idx, const flo
   launch(pool_scan_kernel, dim3((unsigned)((int64_t)nq * nchunks)), dim3(kPoolWaves * 64), s, ev_scan, c, q_idx, w,
          q_seq, pool, pool_cnt, nq, h_idx, p, nchunks, sc, pstride);
   launch(pool_select_kernel, dim3((unsigned)nq), dim3(kPoolSelThreads), s, ev_select, pool, pool_cnt, p,
-         (const float*)sc, (int64_t)pstride, 0, k, out_idx, out_cnt);
-  return hipGetLastError();
-}
-
-hipError_t launch_pool_select_by_entry(const int32_t* pool, const int32_t* pool_cnt, int nq, int p,
-                                       const float* scores, int64_t vstride, int k, int32_t* out_idx,
-                                       int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
-  if (nq <= 0) {
-    record_empty(ev, s);
-    return hipSuccess;
-  }
-  launch(pool_select_kernel, dim3((unsigned)nq), dim3(kPoolSelThreads), s, ev, pool, pool_cnt, p, scores, vstride, 1,
-         k, out_idx, out_cnt);
+         (const float*)sc, (int64_t)pstride, k, out_idx, out_cnt);
   return hipGetLastError();
 }
 

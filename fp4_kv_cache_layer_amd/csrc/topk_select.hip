@@ -8,95 +8,35 @@
 //
 // Every entry gets the unique 64-bit key C = (orderable score << 32) |
 // (0xFFFFFFFF - index), so "score descending, index ascending" is "C
-// descending" and no two entries tie.  The indexer scan has already
-// histogrammed the top 11 bits of every key; a block scan over that histogram
-// fixes the 11-bit prefix P holding the k-th key.  Then:
-//
-//  collect (one workgroup per 8K-entry slice of a query, so the score pass is
-//          spread over the whole chip): every entry whose score reaches the
-//          lowest score of prefix P is appended to an LDS list, which is
-//          copied to the query's candidate list after one global atomic
-//          reserves its place;
-//  final   (one workgroup per query): candidates above P are selected, those
-//          equal to P are parked in LDS and refined digit by digit (heavily
-//          tied inputs first refine over the candidate list in global memory),
-//          the chosen indices are marked in an LDS bitmap over the context
-//          and written in index order by a block-wide prefix count (a bitonic
-//          sort when the context is too long for the bitmap).  It leaves the
-//          query's histogram row and candidate counter zeroed for the next call.
+// descending" and no two entries tie.  The indexer has left a candidate list
+// per query (indices and 32-bit score keys) that holds every entry at or
+// above a key floor; the histogram of the candidates' top 11 key bits is
+// counted here from the list (per-query scan) or left by the indexer (dense):
+//   - per-query scan: each 2,048-entry chunk kept its entries at or above its
+//     own floor; a chunk whose floor lies above the bin of the k-th candidate
+//     key may have left out entries of the Top-k, so this kernel scores that
+//     chunk again (the scan's arithmetic, identical bits) and adds its
+//     entries at or above that bin before selecting;
+//   - dense prefill indexer: every entry at or above a sampled threshold, and
+//     every entry of queries the threshold left short.
+// One workgroup per query: a block scan over the histogram fixes the 11-bit
+// prefix P holding the k-th key; candidates above P are selected, those equal
+// to P are parked in LDS and refined digit by digit (heavily tied inputs
+// first refine over the candidate list in global memory), the chosen indices
+// are marked in an LDS bitmap over the context and written in index order by
+// a block-wide prefix count (a bitonic sort when the context is too long for
+// the bitmap).  It leaves the query's histogram row and candidate counter
+// zeroed for the next call.
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
 namespace {
 
 constexpr int kSelCap = 2048;
-constexpr int kCollectThreads = 256;
-
-// Lowest float whose orderable key is >= key (scores are canonical: no -0, no NaN).
-__device__ __forceinline__ float key_floor_float(uint32_t key) {
-  if (key == 0) return -INFINITY;
-  const uint32_t bits = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-  return __uint_as_float(bits);
-}
-
-// Search over a descending-ordered histogram h[0..nb) (nb <= 2048): the
-// largest digit d* whose suffix count reaches need (1 <= need <= total), and
-// the count strictly above it, written to result[0..1].  One wave does the
-// search; the workgroup barrier at the end publishes the result.  Callers
-// have h complete (a barrier) first.
-__device__ void find_digit(const uint32_t* h, int nb, uint32_t need, uint32_t* result) {
-  if ((threadIdx.x >> 6) == 0) {
-    const int lane = threadIdx.x & 63;
-    if (nb == kHistBins) {
-      // Lane l sums the digits [base, base + 32), base = nb - 32 (l + 1)
-      // (descending positions 32l .. 32l+31), reading its eight 16-byte
-      // pieces in a lane-rotated order so the wave's reads spread over the
-      // banks; a wave scan finds the lane L whose range holds d*.  Then lanes
-      // 0..31 take one digit each of L's range, descending, and a second scan
-      // finds d* itself.
-      const int base = nb - 32 * (lane + 1);
-      uint32_t mine = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint4 w = *reinterpret_cast<const uint4*>(h + base + 4 * ((j + lane) & 7));
-        mine += (w.x + w.y) + (w.z + w.w);
-      }
-      const uint32_t x = wave_incl_sum(mine);
-      const uint64_t hm = __builtin_amdgcn_ballot_w64(x - mine < need && need <= x);
-      const int L = __builtin_ctzll(hm);
-      const uint32_t run0 = __builtin_amdgcn_readlane(x - mine, L);
-      const int dig = nb - 1 - 32 * L - lane;                 // lanes 0..31: L's digits, descending
-      const uint32_t hv = h[lane < 32 ? dig : 0];
-      const uint32_t c = lane < 32 ? hv : 0u;
-      const uint32_t y = wave_incl_sum(c) + run0;
-      const uint64_t dm = __builtin_amdgcn_ballot_w64(lane < 32 && need <= y && y - c < need);
-      const int L2 = __builtin_ctzll(dm);
-      const uint32_t above = __builtin_amdgcn_readlane(y - c, L2);
-      if (lane == 0) {
-        result[0] = (uint32_t)(nb - 1 - 32 * L - L2);
-        result[1] = above;
-      }
-    } else {
-      const int per = (nb + 63) >> 6;
-      const int p0 = min(nb, lane * per), p1 = min(nb, p0 + per);
-      uint32_t mine = 0;
-      for (int p = p0; p < p1; ++p) mine += h[nb - 1 - p];
-      const uint32_t x = wave_incl_sum(mine);
-      const uint32_t excl = x - mine;
-      if (excl < need && need <= x) {
-        uint32_t run = excl;
-        for (int p = p0; p < p1; ++p) {
-          const uint32_t c = h[nb - 1 - p];
-          if (need <= run + c) { result[0] = (uint32_t)(nb - 1 - p); result[1] = run; break; }
-          run += c;
-        }
-      }
-    }
-  }
-  lds_barrier();
-}
+constexpr int kRepairWaves = 8;             // waves of the final workgroup that rescore a chunk
 
 // Appends value for every lane where flag holds, one atomic per wave.
 template <typename T>
@@ -115,80 +55,6 @@ __device__ __forceinline__ void wave_append(bool flag, T value, int* counter, T*
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// collect
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kCollectThreads)
-topk_collect_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k, int nslices) {
-  __shared__ __attribute__((aligned(16))) uint32_t h[kHistBins];
-  __shared__ int32_t list[kCollectSlice];             // this slice's candidates
-  __shared__ uint32_t klist[kCollectSlice];           // and their score keys
-  __shared__ uint32_t res[2];
-  __shared__ int count, base;
-  const int q = blockIdx.x / nslices;
-  const int slice = blockIdx.x - q * nslices;
-  const int V = clamp_vis(q_vis[q], ws);
-  const int t0 = slice * kCollectSlice;
-  if (V <= k || t0 >= V) return;                      // uniform
-  const int tid = threadIdx.x;
-  const int t1 = min(V, t0 + kCollectSlice);
-  // the histogram row first, then the slice's scores (indices clamped, entries past t1 ignored)
-  const uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
-  for (int i = tid; i < kHistBins; i += kCollectThreads) h[i] = gh[i];
-  constexpr int kPer = kCollectSlice / (4 * kCollectThreads);   // float4 loads per thread
-  const float4* sc4 = reinterpret_cast<const float4*>(ws.scores + (int64_t)q * ws.vstride + t0);
-  const int nvec = (t1 - t0 + 3) >> 2;
-  float4 v[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = sc4[min(u * kCollectThreads + tid, nvec - 1)];
-  if (tid == 0) count = 0;
-  lds_barrier();
-  find_digit(h, kHistBins, (uint32_t)k, res);
-  const float floor_s = key_floor_float(res[0] << (32 - kHistBits));
-  // count this thread's candidates, one scan and one reservation per wave,
-  // then write them in order
-  uint32_t mine = 0;
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int vi = u * kCollectThreads + tid;
-    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) mine += (t0 + 4 * vi + c < t1 && e[c] >= floor_s) ? 1u : 0u;
-  }
-  const int lane = tid & 63;
-  const uint32_t x = wave_incl_sum(mine);
-  int wbase = 0;
-  if (lane == 63 && x) wbase = atomicAdd(&count, (int)x);
-  int pos = __shfl(wbase, 63) + (int)(x - mine);
-  if (mine) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int vi = u * kCollectThreads + tid;
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 4 * vi + c;
-        if (t < t1 && e[c] >= floor_s) {                  // at most kCollectSlice entries in all
-          list[pos] = t;
-          klist[pos++] = score_key(e[c]);
-        }
-      }
-    }
-  }
-  lds_barrier();
-  // one global reservation per workgroup, then a coalesced copy of the list
-  const int n = count;
-  if (n == 0) return;
-  if (tid == 0) base = atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
-  lds_barrier();
-  int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
-  uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride + base;
-  for (int i = tid; i < n; i += kCollectThreads) {
-    cand[i] = list[i];
-    ckey[i] = klist[i];
-  }
-}
-
-// ---------------------------------------------------------------------------
 // final
 // ---------------------------------------------------------------------------
 namespace {
@@ -199,14 +65,18 @@ struct SelShared {
   uint64_t tie[kTieCap];                        // parked keys; reused as the output bitmap
   uint32_t scratch[kSelectThreads / 64];
   uint32_t res[2];
+  uint32_t res2[2];
   int32_t selcnt;
   int32_t tiecnt;
+  int32_t repair;
 };
+static_assert(sizeof(uint64_t) * kTieCap >= (size_t)kRepairWaves * kFp8SlotBytes,
+              "the parking buffer holds the repairing waves' operand slots");
 
 }  // namespace
 
 __global__ void __launch_bounds__(kSelectThreads)
-topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
+topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, int k,
                   int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
   __shared__ SelShared S;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -222,15 +92,104 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
     if (tid == 0) { out_cnt[q] = V; ws.cand_cnt[q] = 0; }
     return;
   }
-  const int ncand = ws.cand_cnt[q];
-  for (int i = tid; i < kHistBins; i += kSelectThreads) { S.h[i] = gh[i]; gh[i] = 0; }
-  if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; }
+  if (ws.floor != nullptr) {
+    // per-query scan: the histogram of the candidates' keys, counted here
+    const int nc = ws.cand_cnt[q];
+    for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
+    lds_barrier();
+    for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
+  } else {
+    for (int i = tid; i < kHistBins; i += kSelectThreads) { S.h[i] = gh[i]; gh[i] = 0; }
+  }
+  if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; S.repair = 0; }
   lds_barrier();
 
   uint32_t need = (uint32_t)k;
   int nbits = kHistBits;
   find_digit(S.h, kHistBins, need, S.res);
   int dstar = (int)S.res[0];
+
+  if (ws.floor != nullptr) {
+    // The k-th candidate key to 22 bits: a second digit over the candidates
+    // in its 11-bit bin (counted into the parking buffer, free until later).
+    const int ncand0 = ws.cand_cnt[q];
+    const uint32_t* ckey_r = ws.ckey + (int64_t)q * ws.vstride;
+    uint32_t* const h2 = reinterpret_cast<uint32_t*>(S.tie);
+    for (int i = tid; i < kHistBins; i += kSelectThreads) h2[i] = 0;
+    lds_barrier();
+    for (int i = tid; i < ncand0; i += kSelectThreads) {
+      const uint32_t key = ckey_r[i];
+      if ((int)(key >> (32 - kHistBits)) == dstar) atomicAdd(&h2[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+    }
+    lds_barrier();
+    find_digit(h2, kHistBins, need - S.res[1], S.res2);
+    // Every entry a chunk left out has a key below the chunk's floor.  A chunk
+    // whose floor lies above the k-th candidate key's 22-bit prefix pfloor may
+    // have left out entries at or above the k-th key: rescore it (same
+    // arithmetic as the scan) and add its entries in [pfloor, floor); the k-th
+    // key can only rise, so afterwards every entry at or above it is a
+    // candidate (rare: it takes more of the Top-k in one chunk than it keeps).
+    const uint32_t pfloor = ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
+    const int nch = (V + kScanChunk - 1) / kScanChunk;
+    const uint32_t* fl = ws.floor + (int64_t)q * ws.fstride;
+    for (int cc = tid; cc < nch; cc += kSelectThreads)
+      if (fl[cc] > pfloor) atomicOr(&S.repair, 1);
+    lds_barrier();
+    if (S.repair) {
+      const int lane_r = tid & 63, wave_r = tid >> 6;
+      const int g = lane_r >> 4, r = lane_r & 15;
+      intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+      float wv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (wave_r < kRepairWaves) {
+        if (r < sa.h_idx) a = load_fp8_operand(sa.q_idx + ((int64_t)q * sa.h_idx + r) * kIndexDim, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          wv[i] = (4 * g + i < sa.h_idx) ? sa.w[(int64_t)q * sa.h_idx + 4 * g + i] : 0.0f;
+      }
+      // the parking buffer is free until the candidates are read: it holds
+      // the repairing waves' operand slots
+      uint8_t* const slot = reinterpret_cast<uint8_t*>(S.tie) + wave_r * kFp8SlotBytes;
+      const int32_t* pt_row = sa.c.page_table + (int64_t)sa.q_seq[q] * sa.c.max_pages;
+      int32_t* cand_w = ws.cand + (int64_t)q * ws.vstride;
+      uint32_t* ckey_w = ws.ckey + (int64_t)q * ws.vstride;
+      for (int cc = 0; cc < nch; ++cc) {
+        const uint32_t fc = fl[cc];                   // uniform
+        if (fc <= pfloor || wave_r >= kRepairWaves) continue;
+        const int c0 = cc * kScanChunk, c1 = min(V, c0 + kScanChunk);
+        const int ntl = (c1 - c0 + 15) >> 4;
+        for (int j = wave_r; j < ntl; j += kRepairWaves) {
+          const int ts = c0 + 16 * j;                 // tiles never straddle pages
+          const int page = clamp_page(pt_row[ts >> sa.c.lg_page], sa.c);
+          const intx8 lin = load_fp8_tile_linear(
+              sa.c.idx_k + (((int64_t)page << sa.c.lg_page) + (ts & ((1 << sa.c.lg_page) - 1))) * kIndexDim, lane_r);
+          const float sv = tile_score(a, wv, slot, lin, lane_r);
+          const uint32_t key = score_key(sv);
+          const int t = ts + r;
+          // entries below the chunk's floor that reach the k-th candidate's bin
+          const bool add = g == 0 && t < c1 && key >= pfloor && key < fc;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(add);
+          if (m) {
+            const int leader = __builtin_ctzll(m);
+            int b0 = 0;
+            if (lane_r == leader) b0 = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)__builtin_popcountll(m));
+            b0 = __builtin_amdgcn_readlane(b0, leader);
+            const int pos = b0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (add) {
+              cand_w[pos] = t;
+              ckey_w[pos] = key;
+              atomicAdd(&S.h[key >> (32 - kHistBits)], 1u);
+            }
+          }
+        }
+      }
+      __syncthreads();                                // new candidates (global) and histogram counts complete
+      find_digit(S.h, kHistBins, need, S.res);
+      dstar = (int)S.res[0];
+    }
+  }
+  // the count as the repair left it (an atomic load: other waves added to it)
+  const int ncand = (int)__hip_atomic_load(&ws.cand_cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint64_t P = (uint64_t)dstar;
   need -= S.res[1];
   uint32_t cnt_eq = S.h[dstar];
@@ -380,26 +339,13 @@ topk_final_kernel(IndexWs ws, const int32_t* __restrict__ q_vis, int k,
   if (tid == 0) { out_cnt[q] = k; ws.cand_cnt[q] = 0; }
 }
 
-hipError_t launch_topk_select(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int max_vis,
-                              int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
+hipError_t launch_topk_final(const IndexWs& ws, const ScanArgs& sa, const int32_t* q_vis, int nq, int k,
+                             int32_t* out_idx, int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
   if (nq <= 0) {
     record_empty(ev, s);
     return hipSuccess;
   }
-  const int nslices = max(1, (max_vis + kCollectSlice - 1) / kCollectSlice);
-  launch(topk_collect_kernel, dim3((unsigned)((int64_t)nq * nslices)), dim3(kCollectThreads), s, ev.first(), ws,
-         q_vis, k, nslices);
-  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev.last(), ws, q_vis, k, out_idx, out_cnt);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_final(const IndexWs& ws, const int32_t* q_vis, int nq, int k, int32_t* out_idx,
-                             int32_t* out_cnt, hipStream_t s, const KEvents& ev) {
-  if (nq <= 0) {
-    record_empty(ev, s);
-    return hipSuccess;
-  }
-  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev, ws, q_vis, k, out_idx, out_cnt);
+  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev, ws, sa, q_vis, k, out_idx, out_cnt);
   return hipGetLastError();
 }
 

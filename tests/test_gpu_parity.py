@@ -453,3 +453,45 @@ def test_peaked_softmax_stays_within_tolerance():
     err = np.abs(out.cpu().numpy() - o_ref).max()
     say(f"[attn peaked] max|dO| {err:.2e}")
     assert err <= OUT_ATOL
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_scan_chunk_repair_when_topk_concentrates(k):
+    """Indexer-K rows 2,048..4,095 of sequence 0 point along the query's
+    weighted heads, so that chunk holds far more of its Top-k than its local
+    share: the
+    per-query scan keeps only its local top entries there, and the final
+    select must find the chunk's floor above the k-th key's bin and rescore
+    it.  The selection stays bit-exact against the oracle."""
+    ops, runner = _ops()
+    spec = W.small_case("repair", 81 + k, [20000, 7000], n_new=1, h_idx=8, h=16, k=k,
+                        modes=(O.FULL, O.REINDEX), integer_indexer=True)
+    # rows along sign(sum_h w_h q_h) of the Full layer's query 0, magnitudes 4..8:
+    # their scores dominate that query's Top-k
+    qi, w, _ = W.layer_queries(spec, 0, "cpu")
+    qv = qi[0].view(torch.float8_e4m3fn).float().numpy()                # [h_idx][128]
+    u = (w[0].numpy()[:, None] * qv).sum(0)
+    rng = np.random.default_rng(k)
+    hot = (np.where(u >= 0, 1.0, -1.0)[None, :] * rng.integers(4, 9, (2048, 128))).astype(np.float32)
+    hot_bits = (hot.view(np.uint32) >> 16).astype(np.uint16)           # small integers are exact in bf16
+    say(f"[repair] k={k}")
+    dc = runner.DeviceCase(spec, gen_device="cpu", poison_ws=True)
+    pt = W.page_table(spec)
+    slots = torch.from_numpy(W.slots_for(spec, pt, 0, 2048, 4096)).cuda()
+    kv_bits = W.kv_rows(spec, 0, "cpu")[2048:4096].contiguous().cuda()
+    ops.csa2_append_quant_fp4(dc.cache, slots, kv_bits, torch.from_numpy(hot_bits.view(np.int16)).cuda())
+    dc.run_layers()
+    got = dc.results_host()
+    case = CB.build(spec)
+    case.ik_src[0] = case.ik_src[0].copy()
+    case.ik_src[0][2048:4096] = hot_bits
+    ref = CB.run_group(case)
+    # the case does exercise the repair: the chunk holds more of the Top-k than it keeps
+    share = -(-k * 2048 // int(spec.q_vis()[0]))
+    local = min(2048, max(16, 4 * share))
+    in_chunk = int(((ref[0]["idx"][0] >= 2048) & (ref[0]["idx"][0] < 4096)).sum())
+    say(f"  Top-{k} entries in the hot chunk: {in_chunk} (the chunk keeps about {local})")
+    assert in_chunk > local
+    for li in range(2):
+        assert np.array_equal(got[li]["cnt"], ref[li]["cnt"]), li
+        assert np.array_equal(got[li]["idx"], ref[li]["idx"]), li
