@@ -30,6 +30,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 SOURCE_FLAGS = {s: [] for s in SOURCES}
+# the scan's one-lane reservation atomic is waited on only after the candidate
+# listing; the atomic optimizer would rewrite it into a wave-wide form whose
+# result is needed (waited on) at once
+SOURCE_FLAGS["index_scan.hip"] = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 

@@ -59,7 +59,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   __shared__ float sc[kScanChunk + 1];                // the chunk's scores (+ a sink slot)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];   // then the candidate list
   __shared__ uint32_t res[2];
-  __shared__ int nlist, base;
+  __shared__ int nlist, base;                          // listed candidates, their place in the query's list
   // query-major: the chunks of one query are consecutive blocks.  On ragged
   // batches the grid is sized by the longest query and most blocks of the
   // short ones exit at once; in this order the working blocks of every query
@@ -144,9 +144,10 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int nloc = t1 - t0;
   const int L = scan_local_rank(k, vis);
   uint32_t floor_key = 0;                             // a chunk of at most L entries keeps them all
+  int n = nloc;                                       // entries at or above the floor
   if (nloc > L) {
     find_digit(hist, kHistBins, (uint32_t)L, res);    // ends with a barrier
-    const uint32_t d1 = res[0], need2 = (uint32_t)L - res[1];
+    const uint32_t d1 = res[0], above1 = res[1];
     for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
     lds_barrier();
     for (int i = tid; i < nloc; i += kScanWaves * 64) {
@@ -154,11 +155,19 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       if ((key >> (32 - kHistBits)) == d1) atomicAdd(&hist[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
     }
     lds_barrier();
-    find_digit(hist, kHistBins, need2, res);
+    find_digit(hist, kHistBins, (uint32_t)L - above1, res);
     floor_key = (d1 << (32 - kHistBits)) | (res[0] << (32 - 2 * kHistBits));
+    n = (int)(above1 + res[1] + hist[res[0]]);
+  }
+  // The count is known from the histograms: reserve the candidates' place in
+  // the query's list now, so the atomic's round trip overlaps the listing.
+  int my_base = 0;                                    // (thread 0) waited on only after the listing
+  if (tid == 0) {
+    my_base = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
+    ws.floor[(int64_t)q * ws.fstride + chunk] = floor_key;
   }
   // candidates: every entry whose key reaches the floor, listed in LDS (one
-  // scan and one reservation per wave), then one reservation per workgroup
+  // scan and one reservation per wave)
   int32_t* const list = reinterpret_cast<int32_t*>(&stage[0][0]);
   if (tid == 0) nlist = 0;
   lds_barrier();
@@ -180,13 +189,8 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       if (i < nloc && score_key(sc[i]) >= floor_key) list[pos++] = i;
     }
   }
-  lds_barrier();
-  const int n = nlist;
-  if (tid == 0) {
-    base = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
-    ws.floor[(int64_t)q * ws.fstride + chunk] = floor_key;
-  }
-  lds_barrier();
+  if (tid == 0) base = my_base;
+  lds_barrier();                                     // the list and the reservation
   int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
   uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride + base;
   for (int j = tid; j < n; j += kScanWaves * 64) {
