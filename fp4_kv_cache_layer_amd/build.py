@@ -2,6 +2,11 @@
 in-tree with hipcc.
 
     python -m fp4_kv_cache_layer_amd.build
+    python -m fp4_kv_cache_layer_amd.build --sanitized DIR
+
+The second form builds a copy of the library whose host code carries
+AddressSanitizer and UndefinedBehaviorSanitizer (the device code is built as
+usual) into DIR, for running the host-side tests under the sanitizers.
 """
 from __future__ import annotations
 
@@ -84,5 +89,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# host-only sanitizers: each -fsanitize= applies to the host pass alone
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SANITIZED_NAME = "libcsa2_sanitized.so"
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime that a host process must preload to
+    load the sanitized library, or None when the toolchain has none."""
+    import glob
+    for d in sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux")):
+        p = os.path.join(d, "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return None
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Builds the library with host-side ASan and UBSan into out_dir (not the
+    package: the product library is never replaced by it); returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs, procs = [], []
+    for s in SOURCES:
+        obj = os.path.join(out_dir, s.replace(".hip", ".o"))
+        objs.append(obj)
+        procs.append((s, _run([hipcc(), *FLAGS, *SOURCE_FLAGS[s], *SANITIZE, *inc, "-c", os.path.join(CSRC, s),
+                               "-o", obj], verbose)))
+    for s, p in procs:
+        _finish(p, verbose, s)
+    lib = os.path.join(out_dir, SANITIZED_NAME)
+    _finish(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE, *objs, "-o", lib], verbose),
+            verbose, "sanitized link")
+    return lib
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(sys.argv[sys.argv.index("--sanitized") + 1], verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <mutex>
 
 using namespace csa2;
@@ -37,6 +38,17 @@ struct TimedLaunch {
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The value of an enum argument as an integer.  A caller may pass any int
+// (the header is C, where enums are ints); read as the C++ enum type, a value
+// outside its range would be undefined, so its bytes are copied instead.
+template <typename E>
+int32_t enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "C enums are int-sized");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 int ilog2_pow2(int x) {
   if (x <= 0 || (x & (x - 1))) return -1;
@@ -164,8 +176,10 @@ csa2_status validate_pool(const int32_t* pool, const int32_t* pool_cnt, int32_t 
 }
 
 // Every check of csa2_layer_step, before anything is launched.
-csa2_status prepare_step(csa2_mode mode, const csa2_step_args* a, Step* p) {
-  if (!a || (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE)) return CSA2_ERR_INVALID_ARG;
+csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
+  if (!a || (mode_value != CSA2_FULL && mode_value != CSA2_REINDEX && mode_value != CSA2_REUSE))
+    return CSA2_ERR_INVALID_ARG;
+  const csa2_mode mode = static_cast<csa2_mode>(mode_value);
   if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL | CSA2_STEP_ATTN_PER_HEAD_GROUP)) return CSA2_ERR_INVALID_ARG;
   if (a->flags & CSA2_STEP_DENSE_INDEX) {
     if (a->dense_cand_factor < CSA2_DENSE_RESCORE_ALL || a->dense_cand_factor > 64) return CSA2_ERR_INVALID_ARG;
@@ -323,7 +337,7 @@ bool layers_conflict(const Step& i, const Step& j) {
 extern "C" {
 
 const char* csa2_status_string(csa2_status st) {
-  switch (st) {
+  switch (enum_value(st)) {
     case CSA2_OK: return "ok";
     case CSA2_ERR_INVALID_ARG: return "invalid argument";
     case CSA2_ERR_UNSUPPORTED: return "unsupported request";
@@ -333,7 +347,8 @@ const char* csa2_status_string(csa2_status st) {
   return "unknown status";
 }
 
-size_t csa2_workspace_bytes(csa2_mode mode, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
+size_t csa2_workspace_bytes(csa2_mode mode_arg, int32_t nq, int32_t max_vis, int32_t h_idx, int32_t h, int32_t k) {
+  const int32_t mode = enum_value(mode_arg);
   (void)h_idx; (void)k;
   if (nq <= 0 || max_vis < 0 || h < 1 || h > CSA2_MAX_H || k < 1 || k > CSA2_MAX_K) return 0;
   size_t b = zero_state_bytes(nq);
@@ -410,7 +425,7 @@ csa2_status csa2_sparse_attn(const csa2_cache_view* c, const uint16_t* q, const 
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_step_args* a, hipStream_t s) {
   Step p;
-  csa2_status st = prepare_step(mode, a, &p);
+  csa2_status st = prepare_step(enum_value(mode), a, &p);
   if (st != CSA2_OK) return st;
   return run_step(p, s);
 }
@@ -439,7 +454,7 @@ csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_step_args* a, hipS
   b.ws = ptr;
   b.ws_bytes = CSA2_STATIC_SCRATCH_BYTES;
   Step p;
-  csa2_status st = prepare_step(mode, &b, &p);              // CSA2_ERR_WORKSPACE: the shape needs more
+  csa2_status st = prepare_step(enum_value(mode), &b, &p);   // CSA2_ERR_WORKSPACE: the shape needs more
   if (st != CSA2_OK || b.nq == 0) return st;
   // the state-carrying head of the workspace starts at zero (a fill kernel,
   // which a graph capture may record; no memset node)
@@ -491,7 +506,7 @@ csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_a
   }
   Step steps[CSA2_GROUP_MAX_LAYERS];
   for (int i = 0; i < n; ++i) {
-    csa2_status st = prepare_step(modes[i], &layers[i], &steps[i]);
+    csa2_status st = prepare_step(enum_value(modes[i]), &layers[i], &steps[i]);
     if (st != CSA2_OK) return st;
   }
   if (n_aux == 0) {
