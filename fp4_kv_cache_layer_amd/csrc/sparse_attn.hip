@@ -588,28 +588,48 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
   const int n = max(0, min(cnt[qi], k));                // counts outside [0, k] are clamped
   const int ntiles = (n + kTileRows - 1) / kTileRows;
 
-  // Q^T operand: head r; chunk ch, K-step t holds dims 128 ch + 32 g + 8 t .. +7
+  // The four 128-dim chunks of the latent in slot order: slots 0 and 1 are
+  // this workgroup's half (their dequantised rows are staged for P.V), slots
+  // 2 and 3 the other half (Q.X^T only).  chunk(s) = (s + 2 half) mod 4.
+  const int ch_of[4] = {2 * half, 2 * half + 1, 2 - 2 * half, 3 - 2 * half};
+  // Q^T operand: head r; slot s, K-step t holds dims 128 chunk(s) + 32 g + 8 t .. +7
   bf16x8 qop[4][4];
   {
     const bool ok = head < h;
     const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)qi * h + (ok ? head : 0)) * kLatent + 32 * g);
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+    for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        qop[ch][t] = __builtin_bit_cast(bf16x8, ok ? src[16 * ch + t] : make_uint4(0, 0, 0, 0));
+        qop[sl][t] = __builtin_bit_cast(bf16x8, ok ? src[16 * ch_of[sl] + t] : make_uint4(0, 0, 0, 0));
   }
   {
-    // physical rows of the selection, resolved once (index loads clamped to
-    // the row of k entries so they need not wait for the count)
+    // physical rows of this wave's own tiles (wv, wv + W, ...; half a wave
+    // per tile), resolved by the wave itself, so no workgroup barrier stands
+    // between a wave's lookups and its first gathers.  The index loads run
+    // over the k-entry row (clamped to it) and are issued four at a time, so
+    // they wait neither for the count nor for each other; only the
+    // page-table lookups need the count.
     const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
     const int32_t* irow = idx + (int64_t)qi * k;
-    for (int j = tid; j < ntiles * kTileRows; j += 64 * W) {
-      const int t = irow[min(j, k - 1)];
-      if (j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, t, c);
+    const int ktiles = (k + kTileRows - 1) / kTileRows;
+    for (int i0 = lane >> 5; wv + W * i0 < ktiles; i0 += 8) {
+      int tv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int T = wv + W * (i0 + 2 * u);
+        const int j = T * kTileRows + (lane & 31);
+        tv[u] = T < ktiles ? irow[min(j, k - 1)] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int T = wv + W * (i0 + 2 * u);
+        const int j = T * kTileRows + (lane & 31);
+        if (T < ktiles && j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, tv[u], c);
+      }
     }
   }
-  lds_barrier();
+  __builtin_amdgcn_wave_barrier();                       // the wave's row writes stay above its gathers
 
   floatx4 oacc[16];
 #pragma unroll
@@ -622,7 +642,8 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
 
   // Gathers of one tile (rows past the selection read physical row 0, which
   // always exists): per M-tile, the row's four 16-byte code pieces of this
-  // lane's group and its 16 scale bytes.  Loads are unconditional.
+  // lane's group, in slot order, and its 16 scale bytes.  Loads are
+  // unconditional.
   struct Gath {
     uint4 cd[2][4];
     uint4 sc[2];
@@ -634,40 +655,53 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
       const int j = T * kTileRows + mt * 16 + r;
       const uint8_t* src = c.kv + (size_t)(j < n ? S.row[j] : 0u) * kKvRowBytes;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) G.cd[mt][ch] = *reinterpret_cast<const uint4*>(src + 64 * ch + 16 * g);
+      for (int sl = 0; sl < 4; ++sl)
+        G.cd[mt][sl] = *reinterpret_cast<const uint4*>(src + 64 * ch_of[sl] + 16 * g);
       G.sc[mt] = *reinterpret_cast<const uint4*>(src + kCodeBytes);
     }
   };
   auto process = [&](int tt, const Gath& G) {
     const int T = wv + W * tt;
     const int lim = n - T * kTileRows;                   // rows of this tile inside the selection
-    floatx4 st[2];
+    // S^T = X Q^T as four independent accumulator chains (M-tile, K-step
+    // parity), so consecutive matrix-core ops never wait on each other;
+    // straight-line code (no branch per K-step) lets the conversions of the
+    // next step run under the current one
+    floatx4 st[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) st[mt][0] = st[mt][1] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float scale[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      st[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       // a row past the selection keeps its (finite) codes but gets scale 1:
       // its logit is masked below, so it only ever meets a zero probability
       const bool valid = mt * 16 + r < lim;
       const uint32_t scw[4] = {G.sc[mt].x, G.sc[mt].y, G.sc[mt].z, G.sc[mt].w};
-      uint8_t* const rowp = xs + (mt * 16 + r) * kDsStride + 64 * g;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        const float scale = e8m0_to_float(valid ? (scw[ch] >> (8 * g)) & 0xFFu : 127u);
-        const uint32_t wds[4] = {G.cd[mt][ch].x, G.cd[mt][ch].y, G.cd[mt][ch].z, G.cd[mt][ch].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 a = dequant8(wds[t], scale);
-          st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ch][t], st[mt], 0, 0, 0);
-          if ((ch >> 1) == half)                         // this half's dims go to the staged rows
-            *reinterpret_cast<bf16x8*>(rowp + 256 * (ch & 1) + 16 * t) = a;
-        }
+      for (int sl = 0; sl < 4; ++sl) {
+        // dword chunk(s) of the scale bytes, picked without dynamic indexing
+        const uint32_t d = half ? scw[(sl + 2) & 3] : scw[sl];
+        scale[mt][sl] = e8m0_to_float(valid ? (d >> (8 * g)) & 0xFFu : 127u);
       }
     }
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const uint32_t wd = t == 0 ? G.cd[mt][sl].x : t == 1 ? G.cd[mt][sl].y : t == 2 ? G.cd[mt][sl].z
+                                                                                          : G.cd[mt][sl].w;
+          const bf16x8 a = dequant8(wd, scale[mt][sl]);
+          st[mt][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[sl][t], st[mt][t & 1], 0, 0, 0);
+          if (sl < 2)                                    // this half's dims go to the staged rows
+            *reinterpret_cast<bf16x8*>(xs + (mt * 16 + r) * kDsStride + 64 * g + 256 * sl + 16 * t) = a;
+        }
     float v[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[mt][i] = st[mt][i];
+      for (int i = 0; i < 4; ++i) v[mt][i] = st[mt][0][i] + st[mt][1][i];
     if (lim < kTileRows) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -720,15 +754,25 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
     __builtin_amdgcn_wave_barrier();
     const int off_a = (4 * g + (r >> 2)) * kDsStride + 8 * (r & 3);
     const int off_b = off_a + 16 * kDsStride;
+    // groups of four n-tiles: their hi terms, then their lo terms, so each
+    // accumulator's two updates are four matrix-core ops apart
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      const shortx4 lo = lds_read_tr16(xs, off_a + 32 * nt);
-      const shortx4 hi = lds_read_tr16(xs, off_b + 32 * nt);
-      typedef short shortx8 __attribute__((ext_vector_type(8)));
-      const shortx8 b8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, b8);
-      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb, oacc[nt], 0, 0, 0);
-      oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb, oacc[nt], 0, 0, 0);
+    for (int n0 = 0; n0 < 16; n0 += 4) {
+      bf16x8 xb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const shortx4 lo = lds_read_tr16(xs, off_a + 32 * (n0 + u));
+        const shortx4 hi = lds_read_tr16(xs, off_b + 32 * (n0 + u));
+        typedef short shortx8 __attribute__((ext_vector_type(8)));
+        const shortx8 b8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        xb[u] = __builtin_bit_cast(bf16x8, b8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        oacc[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, xb[u], oacc[n0 + u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        oacc[n0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, xb[u], oacc[n0 + u], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();                     // the next tile's row writes stay below these reads
   };
