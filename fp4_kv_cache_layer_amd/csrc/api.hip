@@ -123,16 +123,14 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool d
   IndexWs r;
   r.vis_cap = max_vis;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
-  r.hist = reinterpret_cast<uint32_t*>(p);
-  r.cand_cnt = reinterpret_cast<uint32_t*>(p + (size_t)nq * kHistBins * 4);
+  r.cand_cnt = reinterpret_cast<uint32_t*>(p);
+  r.tau = reinterpret_cast<float*>(p + (size_t)nq * 4);
+  r.cnt2 = reinterpret_cast<uint32_t*>(p + (size_t)nq * 8);
   r.vstride = index_vstride(max_vis);
-  r.scores = reinterpret_cast<float*>(p + score_off);
-  r.cand = reinterpret_cast<int32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
-  r.ckey = reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
-  r.mask = reinterpret_cast<uint64_t*>(p + score_off + 3 * (size_t)nq * (size_t)r.vstride * 4);
-  // the per-query scan keeps no scores: its per-chunk key floors use the region
-  r.floor = dense ? nullptr : reinterpret_cast<uint32_t*>(r.scores);
+  r.cand = reinterpret_cast<int32_t*>(p + score_off);
+  r.ckey = reinterpret_cast<uint32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
   r.fstride = (max_vis + kScanChunk - 1) / kScanChunk;
+  r.floor = dense ? nullptr : reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
   return r;
 }
 
@@ -227,7 +225,7 @@ csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
   if (a->nq == 0) return CSA2_OK;
   const size_t z = zero_state_bytes(a->nq);
   if (mode != CSA2_REUSE) {
-    // the pool scores reuse the exhaustive scores' region (dead once the pool is selected)
+    // the pool scores reuse the candidate region (dead once the pool is selected)
     const size_t need = std::max(index_score_bytes(a->nq, a->max_vis), pool ? pool_score_bytes(a->nq, a->pool_k) : 0);
     if (a->ws_bytes < z + need) return CSA2_ERR_WORKSPACE;
     p->iw = index_ws(a->ws, a->nq, a->max_vis, z, p->dense);

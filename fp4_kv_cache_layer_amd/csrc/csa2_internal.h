@@ -32,26 +32,24 @@ __device__ __forceinline__ int64_t entry_row_clamped(const int32_t* __restrict__
 }
 
 // Workspace of the indexer (byte offsets):
-//   [0, Z)      zero-state: histograms [nq][2048] u32, then candidate
-//               counters [nq] u32; the final select kernel leaves every row
-//               it used zeroed again.
-//   [Z, ...)    scores [nq][vstride] fp32, then candidate indices
-//               [nq][vstride] i32, then (dense prefill indexer) candidate
-//               masks, round_up(nq, 16) * vstride / 8 bytes; no initial
-//               state needed.
+//   [0, Z)      zero-state, three [nq] u32 arrays: candidate counters, the
+//               dense indexer's thresholds (fp32 bits) and its full-rescore
+//               counters; the final select kernel zeroes a query's three
+//               words again.
+//   [Z, ...)    candidate indices [nq][vstride] i32, their score keys
+//               [nq][vstride] u32, then (per-query scan) the chunk key floors
+//               [nq][fstride] u32; no initial state needed.
 struct IndexWs {
-  uint32_t* hist;
   uint32_t* cand_cnt;
-  float* scores;
+  float* tau;            // dense indexer: the query's candidate threshold
+  uint32_t* cnt2;        // dense indexer: candidates the full rescore added after cand_cnt
   int32_t* cand;
   uint32_t* ckey;        // score key of cand[i], stored beside it (the final select reads no scores)
-  uint64_t* mask;
   int64_t vstride;
   int32_t vis_cap;       // max_vis of the call: visible counts are clamped to it
   // Per-query scan: the key floor below which each 2,048-entry chunk kept no
-  // candidate, [nq][fstride] u32 (in the score region, which that path does
-  // not use otherwise); NULL for the dense indexer, whose candidates are
-  // exact above its threshold.
+  // candidate, [nq][fstride] u32; NULL for the dense indexer, whose
+  // candidates are exact above its threshold.
   uint32_t* floor;
   int32_t fstride;
 };
@@ -115,11 +113,11 @@ struct ScanArgs {
   int h_idx;
 };
 
-// Dense form for many queries of one sequence (q_seq[0]): leaves the same
-// inputs for the final select (candidate list, candidate histogram, scores of
-// the candidates), with scores bit-identical to the per-query scan.  ev covers
-// the threshold, candidate, full-rescore and compaction kernels, ev_product
-// the candidate (matrix-product) kernel alone.
+// Dense form for many queries of one sequence (q_seq[0]): leaves a candidate
+// list (indices and score keys) per query for the final select, with scores
+// bit-identical to the per-query scan.  ev covers the threshold, candidate
+// and full-rescore kernels, ev_product the candidate (matrix-product) kernel
+// alone.
 // cand_factor: expected candidates per query in units of k (0 sends every
 // query through the full rescore).
 constexpr int kDefaultCandFactor = 4;

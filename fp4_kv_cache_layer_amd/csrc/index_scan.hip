@@ -42,13 +42,13 @@ constexpr int kScanDepth = 6;           // tiles per wave in the load ring
 int64_t index_vstride(int32_t max_vis) { return ((int64_t)max_vis + 2 + 63) / 64 * 64; }
 
 size_t zero_state_bytes(int32_t nq) {
-  return ((size_t)nq * (kHistBins + 1) * 4 + 255) / 256 * 256;
+  return ((size_t)nq * 3 * 4 + 255) / 256 * 256;      // candidate counters, thresholds, rescore counters
 }
 
 size_t index_score_bytes(int32_t nq, int32_t max_vis) {
   const size_t v = (size_t)index_vstride(max_vis);
-  const size_t nq16 = ((size_t)nq + 15) / 16 * 16;      // candidate masks cover whole 16-query blocks
-  return (size_t)nq * 12 * v + nq16 * v / 8;           // scores, candidates, candidate keys, masks
+  const size_t fstride = ((size_t)max_vis + kScanChunk - 1) / kScanChunk;
+  return (size_t)nq * 8 * v + (size_t)nq * fstride * 4;   // candidates, candidate keys, chunk floors
 }
 
 __global__ void __launch_bounds__(kScanWaves * 64)

@@ -16,17 +16,19 @@
 //     threshold, r chosen so that about factor * k entries are expected to
 //     pass.  Queries with V <= k need no threshold; short contexts keep all.
 //  2. candidates (prefill_scan_kernel, first pass): the product itself; an
-//     entry whose score reaches the threshold has its score stored at its
-//     position and its bit set in a per-(query, 16-entry tile) mask.
-//  3. compaction (prefill_compact_kernel): masks -> ordered candidate list
-//     and its count, plus the 2,048-bin histogram of the candidates' score
-//     keys, which is all the final select needs: every entry at or above the
-//     k-th key is a candidate, so the k-th key and the entries above it are
-//     the same as over all entries.
-//  4. exactness (the scan kernel again, then the compaction again): a query
-//     with fewer than k candidates (the sample was unlucky) is rescored in
-//     full with every visible entry a candidate and compacted anew; blocks
-//     without such a query exit at once.
+//     entry whose score reaches the threshold joins its query's candidate
+//     list (index and score key).  Each wave gathers its candidates per query
+//     in LDS and flushes a query's batch with one reservation on the query's
+//     counter, so the lists are written contiguously and nothing else (no
+//     score rows, no masks) leaves the kernel.  Every entry at or above the
+//     k-th key is then a candidate whenever at least k entries reached the
+//     threshold, so the final select sees the same k-th key and the same
+//     entries above it as over all entries.
+//  3. exactness (the scan kernel again): a query left with fewer than k
+//     candidates (the sample was unlucky) is rescored in full, and its
+//     entries below the threshold are appended after the first pass's, so
+//     its list then holds every visible entry once; workgroups without such
+//     a query exit at once.
 //
 // Matrix product: A = the queries' indexer heads ([nq * h_idx] x 128 E4M3),
 // B = the sequence's indexer-K rows (128 x V E4M3).  A workgroup of 4 waves
@@ -52,13 +54,22 @@ constexpr int kPfMaxChunk = 16384;      // entries per workgroup at most
 constexpr int kTauWaves = 4;
 constexpr int kSampleTiles = 32;        // 512 sampled entries per query
 constexpr int kMaxRank = 64;
-constexpr int kCompactThreads = 512;
 
-// Per-wave LDS of the candidate pass: the staged B tile.
+constexpr int kPfCap = 1024;            // LDS candidate slots per wave
+constexpr int kPfMaxQ = 2 * kPfTiles;   // queries per workgroup at most
+
+// LDS of the candidate pass: per wave its staged B tile, the candidates not
+// yet flushed to the lists (word 0: entry offset in the chunk in bits 0-13,
+// query of the workgroup in bits 14-17, its rank among the flush's
+// candidates of that query in bits 18-27; word 1: the score's bits) and
+// per-query counters of a flush.
 struct PfShared {
   uint8_t tile[kPfWaves][kFp8SlotBytes];
   float4 w[kPfTiles][4];             // head weights of A tile t's output rows 4g .. 4g+3 (row group g)
+  uint2 pend[kPfWaves][kPfCap + 64];   // + one sink slot per lane
+  uint32_t qcnt[kPfWaves][kPfMaxQ];
 };
+static_assert(kPfMaxChunk <= (1 << 14) && kPfMaxQ <= 16 && kPfCap <= (1 << 10), "candidate word fields");
 
 // Entries per chunk and chunks per XCD for a given visible range; chunks never
 // span more than 64 pages (one page id per lane).
@@ -193,18 +204,21 @@ prefill_tau_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* 
     }
   }
   const bool writer = r == 0 && (QPT == 1 ? g == 0 : (g & 1) == 0);
-  if (writer && valid) ws.hist[(int64_t)qrow * kHistBins] = __float_as_uint(tau);
+  if (writer && valid) ws.tau[qrow] = tau;
 }
 
 // ---------------------------------------------------------------------------
 // 2./3. candidate pass (RESCORE = false) and full rescore of short queries
 // ---------------------------------------------------------------------------
+// Three workgroups per CU; the one-query-per-tile form (more than 8 indexer
+// heads) holds four partial sums per set and runs two, so it needs no spills.
 template <int QPT, bool RESCORE>
-__global__ void __launch_bounds__(kPfWaves * 64, 3)
+__global__ void __launch_bounds__(kPfWaves * 64, QPT == 2 ? 3 : 2)
 prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
                     int nq, int h_idx, int k, int chunk, int per_xcd, IndexWs ws) {
   constexpr int kQ = kPfTiles * QPT;                 // queries per workgroup
+  static_assert(kQ <= kPfMaxQ && kQ <= 64, "one lane per query in the flushes");
   __shared__ PfShared S;
   const int b = blockIdx.x;
   const int chunk_id = (b & 7) + 8 * ((b >> 3) % per_xcd);
@@ -212,7 +226,8 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   const int e0 = chunk_id * chunk;
 
   // visible range of the block's queries; the rescore pass only serves
-  // queries left with fewer than k candidates (uniform loads)
+  // queries left with fewer than k candidates (uniform loads; the rescore
+  // never changes the first pass's counters, so every block reads the same)
   int vmax = 0;
   bool any_fail = false;
 #pragma unroll
@@ -240,43 +255,24 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   }
   lds_barrier();
 
-
   // After the head sums, output set p puts query ql = 4p + g in lane row g
   // (QPT = 2: tiles 2p and 2p+1; QPT = 1: tiles 4p .. 4p+3).
-  // Candidate masks: per (query block, set, 16-entry tile) one 64-bit word
-  // whose bit 16g + r marks entry 16*tile + r of query ql(p, g).
   constexpr int kSets = kPfTiles * QPT / 4;
   int vis_of[kSets];
   float tau_of[kSets];
-  uint32_t soff[kSets];                              // byte offset of (query ql, entry r) in the block's score rows
-  uint64_t own_rows[kSets];                          // rows whose query this pass writes
+  int npend = 0;                                     // this wave's unflushed candidates (uniform)
+  if (lane < kPfMaxQ) S.qcnt[wave][lane] = 0;
 #pragma unroll
   for (int p = 0; p < kSets; ++p) {
-    const int ql = 4 * p + g;
-    const int qg = q0 + ql;
+    const int qg = q0 + 4 * p + g;
     const bool valid = qg < nq;
     const int v = valid ? clamp_vis(q_vis[qg], ws) : 0;
-    bool own;
-    if (RESCORE) {
-      own = valid && v > k && (int)ws.cand_cnt[qg] < k;
-      tau_of[p] = -INFINITY;
-    } else {
-      own = valid;
-      tau_of[p] = valid ? __uint_as_float(ws.hist[(int64_t)qg * kHistBins]) : INFINITY;
-    }
+    const bool own = RESCORE ? (valid && v > k && (int)ws.cand_cnt[qg] < k) : valid;
     vis_of[p] = own ? v : 0;
-    soff[p] = (uint32_t)(ql * (int)ws.vstride + r) * 4u;
-    own_rows[p] = __builtin_amdgcn_ballot_w64(own);
+    tau_of[p] = valid ? ws.tau[qg] : INFINITY;
   }
-  auto own_rows_of = [&](int ps) {
-    uint64_t o = own_rows[0];
-#pragma unroll
-    for (int p = 1; p < kSets; ++p) o = ps == p ? own_rows[p] : o;
-    return o;
-  };
-  float* const sblock = ws.scores + (int64_t)q0 * ws.vstride;
-  const int64_t mtiles = ws.vstride >> 4;
-  uint64_t* const mblock = ws.mask + (int64_t)(q0 / kQ) * mtiles * kSets;
+  // the rescore appends after the first pass's candidates (lane ql: query q0 + ql)
+  const int list_base = (RESCORE && lane < kQ && q0 + lane < nq) ? (int)ws.cand_cnt[q0 + lane] : 0;
 
   // page ids of the chunk, one per lane
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q0] * c.max_pages;
@@ -295,11 +291,15 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
   };
   // A tile's 16 rows are 2 KB of contiguous memory, loaded coalesced and
   // turned into the MFMA operand through the wave's LDS slot.
+  // The scheduling barrier after each tile's loads keeps them in program
+  // order, so the wait before a tile's use counts exactly the loads issued
+  // after it and the two tiles ahead stay in flight.
   auto load = [&](int j, intx8& lin) {
     const int ts = e0 + 16 * tile_at(j);
     const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
     lin = load_fp8_tile_linear(
         c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim, lane);
+    __builtin_amdgcn_sched_barrier(0);
   };
   uint8_t* const slot = S.tile[wave];
   auto to_operand = [&](const intx8& lin) { return fp8_tile_operand(slot, lin, lane); };
@@ -331,61 +331,79 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     }
   };
 
-  // sink: last score slot of the block's first row, never read
-  const uint32_t sink_off = (uint32_t)(ws.vstride - 1) * 4u;
+  // Flush: the wave's pending candidates go to their queries' lists.  Each
+  // takes its rank among the flush's candidates of its query (LDS counters);
+  // lane ql then reserves query ql's place with one atomic (all queries in one
+  // round trip), and every candidate is stored at its query's base + rank.
+  auto flush = [&]() {
+    uint2* const pl = S.pend[wave];
+    uint32_t* const qc = S.qcnt[wave];
+    for (int i = lane; i < npend; i += 64) {
+      const uint32_t w0 = pl[i].x;
+      const uint32_t rank = atomicAdd(&qc[(w0 >> 14) & 15u], 1u);
+      pl[i].x = w0 | (rank << 18);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // the bases go through LDS (a lane permute would read 0 from lanes the
+    // copy loop's last, partial round leaves inactive)
+    if (lane < kQ) {
+      const uint32_t n = qc[lane];
+      uint32_t* const ctr = RESCORE ? ws.cnt2 : ws.cand_cnt;
+      qc[lane] = n ? (uint32_t)list_base + atomicAdd(&ctr[q0 + lane], n) : 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < npend; i += 64) {
+      const uint2 v = pl[i];
+      const int ql = (int)((v.x >> 14) & 15u), rank = (int)(v.x >> 18);
+      const int64_t at = (int64_t)(q0 + ql) * ws.vstride + (int)qc[ql] + rank;
+      ws.cand[at] = e0 + (int)(v.x & 0x3FFFu);
+      ws.ckey[at] = score_key(__uint_as_float(v.y));
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < kQ) qc[lane] = 0;
+    npend = 0;
+    // the list stores complete here (vmcnt 0, other counters untouched), so
+    // after a flush no store is in flight: the compiler's count of the loads
+    // in flight stays exact across the loop's back edge and its waits keep
+    // the two tiles ahead in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_wave_barrier();                 // the copies' LDS reads stay above later appends
+  };
 
+  // candidate word of this lane's entry in output set 0, less the tile offset
+  // (set p adds p << 16: its query is 4p + g)
+  const uint32_t word0 = (uint32_t)r | ((uint32_t)g << 14);
   auto process = [&](int j, const intx8& lin) {
     const int te = e0 + 16 * tile_at(j);
     const int e = te + r;
     const intx8 bop = to_operand(lin);
-    char* const st = reinterpret_cast<char*>(sblock) + (uint32_t)te * 4u;
-    // lanes without a candidate store into the sink slot (last slot of the
-    // block's first row, never read), so every store is unconditional and
-    // the compiler can count the loads in flight past them
-    const uint32_t sink = sink_off - (uint32_t)te * 4u;
-    uint64_t masks[kSets];
     floatx4 cur[kPerSet], nxt[kPerSet];
     products(bop, 0, cur);
 #pragma unroll
     for (int p = 0; p < kSets; ++p) {
       if (p + 1 < kSets) products(bop, p + 1, nxt);
       const float sc = finish(p, cur);
-      const bool c1 = e < vis_of[p], c2 = sc >= tau_of[p];   // causal mask, threshold
-      const uint64_t m = __builtin_amdgcn_ballot_w64(c1) & __builtin_amdgcn_ballot_w64(c2);
-      masks[p] = m;
-      *reinterpret_cast<float*>(st + (c1 && c2 ? soff[p] : sink)) = sc;
+      // the rescore takes exactly the entries the first pass did not
+      const bool reach = sc >= tau_of[p];
+      const bool keep = e < vis_of[p] && (RESCORE ? !reach : reach);
+      // every lane stores (no branch): a kept entry at its place in the
+      // wave's list, the others into their lane's sink slot past the list
+      const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+      const int pos = keep ? npend + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))
+                           : kPfCap + lane;
+      S.pend[wave][pos] = make_uint2(word0 + ((uint32_t)(te - e0) + ((uint32_t)p << 16)), __float_as_uint(sc));
+      npend += __builtin_popcountll(m);
 #pragma unroll
       for (int i = 0; i < kPerSet; ++i) cur[i] = nxt[i];
     }
-    // one store for the tile's masks: lane l writes the word of set l % kSets
-    uint64_t* const mt = mblock + (te >> 4);
-    const int ps = lane & (kSets - 1);
-    uint64_t mw = masks[0];
-#pragma unroll
-    for (int p = 1; p < kSets; ++p) mw = ps == p ? masks[p] : mw;
-    if (RESCORE) {
-      const uint64_t orow = own_rows_of(ps);
-      mt[ps * mtiles] = (mt[ps * mtiles] & ~orow) | mw;   // every lane of set ps writes the same word
-    } else {
-      mt[ps * mtiles] = mw;
-    }
+    if (npend > kPfCap - 64 * kSets) flush();        // a tile adds at most 64 per set
   };
   // B tiles j = wave, wave + 4, ...; two tiles in flight ahead of the one in
   // use, in three buffers that rotate by name (unrolled by three)
-  // Before the loop, each ring load is followed by the stores of one tile
-  // (into sink slots), as in the loop, so the loop entry and back edge carry
-  // the same memory operations and the compiler's waits stay exact.
-  char* const sink2 = reinterpret_cast<char*>(sblock) + (uint32_t)(ws.vstride - 2) * 4u;
-  auto sink_stores = [&]() {
-#pragma unroll
-    for (int p = 0; p < kSets; ++p) *reinterpret_cast<float*>(sink2 + 4) = 0.0f;
-    *reinterpret_cast<uint64_t*>(sink2) = 0ull;
-  };
   intx8 l0, l1, l2;
   load(wave, l0);
-  sink_stores();
   load(wave + kPfWaves, l1);
-  sink_stores();
   for (int j = wave; j < ntiles; j += 3 * kPfWaves) {
     load(j + 2 * kPfWaves, l2);
     process(j, l0);
@@ -396,82 +414,7 @@ prefill_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float*
     load(j + 4 * kPfWaves, l1);
     process(j + 2 * kPfWaves, l2);
   }
-}
-
-// ---------------------------------------------------------------------------
-// 4. compaction: masks -> candidate list + key histogram (list order is free:
-//    the final select orders its output itself)
-// ---------------------------------------------------------------------------
-// short_only: the pass after the full rescore, for the queries the first
-// compaction left with fewer than k candidates (their masks now hold every
-// visible entry); every other query keeps its list.
-__global__ void __launch_bounds__(kCompactThreads)
-prefill_compact_kernel(const int32_t* __restrict__ q_vis, int k, int qpt, int short_only, IndexWs ws) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t total;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const int V = clamp_vis(q_vis[q], ws);
-  if (V <= k) return;                                // the final select needs no candidates
-  if (short_only && (int)ws.cand_cnt[q] >= k) return;   // uniform
-  for (int i = tid; i < kHistBins; i += kCompactThreads) h[i] = 0;
-  if (tid == 0) total = 0;
-  const int kq = kPfTiles * qpt, nsets = kPfTiles * qpt / 4;
-  const int ql = q % kq, p = ql >> 2;
-  const int g = ql & 3;
-  const int64_t mtiles = ws.vstride >> 4;
-  const uint64_t* mq = ws.mask + ((int64_t)(q / kq) * nsets + p) * mtiles;
-  const float* sc = ws.scores + (int64_t)q * ws.vstride;
-  int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
-  const int nt = (V + 15) >> 4;
-  lds_barrier();
-  constexpr int kBatch = 4;
-  for (int j0 = 0; j0 < nt; j0 += kCompactThreads * kBatch) {
-    uint32_t bits[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int j = j0 + u * kCompactThreads + tid;
-      bits[u] = j < nt ? (uint32_t)(mq[j] >> (16 * g)) & 0xFFFFu : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t n = __builtin_popcount(bits[u]);
-      const uint32_t x = wave_incl_sum(n);
-      uint32_t wbase = 0;
-      if (lane == 63 && x) wbase = atomicAdd(&total, x);
-      wbase = __shfl(wbase, 63);
-      uint32_t pos = wbase + x - n;
-      const int j = j0 + u * kCompactThreads + tid;
-      uint32_t b = bits[u];
-      while (b) {
-        cand[pos++] = (j << 4) + __builtin_ctz(b);
-        b &= b - 1;
-      }
-    }
-  }
-  __syncthreads();                                   // the list is complete (global writes included)
-  const uint32_t n = total;
-  uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride;
-  for (uint32_t i0 = 0; i0 < n; i0 += kCompactThreads * kBatch) {
-    float sv[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t i = i0 + u * kCompactThreads + tid;
-      sv[u] = i < n ? sc[cand[i]] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t i = i0 + u * kCompactThreads + tid;
-      if (i < n) {
-        const uint32_t key = score_key(sv[u]);
-        ckey[i] = key;
-        atomicAdd(&h[key >> (32 - kHistBits)], 1u);
-      }
-    }
-  }
-  lds_barrier();
-  uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
-  for (int i = tid; i < kHistBins; i += kCompactThreads) gh[i] = h[i];
-  if (tid == 0) ws.cand_cnt[q] = n;
+  if (npend > 0) flush();
 }
 
 hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
@@ -489,25 +432,21 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
   const dim3 grid((unsigned)(8 * per_xcd * nqb)), block(kPfWaves * 64);
   const dim3 tgrid((unsigned)((nq + kTauWaves * qpt - 1) / (kTauWaves * qpt))), tblock(kTauWaves * 64);
   const int factor = cand_factor;
-  // threshold, candidates, compaction (which counts each query's
-  // candidates), full rescore of the queries left short, their compaction
+  // threshold, candidates (which count each query's candidates), full
+  // rescore of the queries left short
   if (qpt == 2) {
     launch(prefill_tau_kernel<2>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
     launch(prefill_scan_kernel<2, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+           per_xcd, ws);
+    launch(prefill_scan_kernel<2, true>, grid, block, s, ev.last(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
   } else {
     launch(prefill_tau_kernel<1>, tgrid, tblock, s, ev.first(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, factor, ws);
     launch(prefill_scan_kernel<1, false>, grid, block, s, ev_product, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
            per_xcd, ws);
+    launch(prefill_scan_kernel<1, true>, grid, block, s, ev.last(), c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
+           per_xcd, ws);
   }
-  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, KEvents{}, q_vis, k, qpt, 0, ws);
-  if (qpt == 2)
-    launch(prefill_scan_kernel<2, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
-           per_xcd, ws);
-  else
-    launch(prefill_scan_kernel<1, true>, grid, block, s, KEvents{}, c, q_idx, w, q_seq, q_vis, nq, h_idx, k, chunk,
-           per_xcd, ws);
-  launch(prefill_compact_kernel, dim3((unsigned)nq), dim3(kCompactThreads), s, ev.last(), q_vis, k, qpt, 1, ws);
   return hipGetLastError();
 }
 

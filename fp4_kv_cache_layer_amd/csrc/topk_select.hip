@@ -11,7 +11,7 @@
 // descending" and no two entries tie.  The indexer has left a candidate list
 // per query (indices and 32-bit score keys) that holds every entry at or
 // above a key floor; the histogram of the candidates' top 11 key bits is
-// counted here from the list (per-query scan) or left by the indexer (dense):
+// counted here from the list:
 //   - per-query scan: each 2,048-entry chunk kept its entries at or above its
 //     own floor; a chunk whose floor lies above the bin of the k-th candidate
 //     key may have left out entries of the Top-k, so this kernel scores that
@@ -25,8 +25,8 @@
 // first refine over the candidate list in global memory), the chosen indices
 // are marked in an LDS bitmap over the context and written in index order by
 // a block-wide prefix count (a bitonic sort when the context is too long for
-// the bitmap).  It leaves the query's histogram row and candidate counter
-// zeroed for the next call.
+// the bitmap).  It leaves the query's counters and threshold zeroed for the
+// next call.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 #include "csa2_select.h"
@@ -81,26 +81,22 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   __shared__ SelShared S;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = clamp_vis(q_vis[q], ws);
-  uint32_t* gh = ws.hist + (int64_t)q * kHistBins;
   const int32_t* cand = ws.cand + (int64_t)q * ws.vstride;
   const uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride;
   int32_t* oi = out_idx + (int64_t)q * k;
 
   if (V <= k) {                                       // everything visible is selected
-    for (int i = tid; i < kHistBins; i += kSelectThreads) gh[i] = 0;
     for (int i = tid; i < k; i += kSelectThreads) oi[i] = i < V ? i : -1;
-    if (tid == 0) { out_cnt[q] = V; ws.cand_cnt[q] = 0; }
+    if (tid == 0) { out_cnt[q] = V; ws.cand_cnt[q] = 0; ws.tau[q] = 0.0f; ws.cnt2[q] = 0; }
     return;
   }
-  if (ws.floor != nullptr) {
-    // per-query scan: the histogram of the candidates' keys, counted here
-    const int nc = ws.cand_cnt[q];
-    for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
-    lds_barrier();
-    for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
-  } else {
-    for (int i = tid; i < kHistBins; i += kSelectThreads) { S.h[i] = gh[i]; gh[i] = 0; }
-  }
+  // the candidate count: the dense indexer's full rescore appended after its
+  // first pass's candidates
+  const int nc = (int)ws.cand_cnt[q] + (ws.floor != nullptr ? 0 : (int)ws.cnt2[q]);
+  // the histogram of the candidates' keys
+  for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
+  lds_barrier();
+  for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
   if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; S.repair = 0; }
   lds_barrier();
 
@@ -189,7 +185,9 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     }
   }
   // the count as the repair left it (an atomic load: other waves added to it)
-  const int ncand = (int)__hip_atomic_load(&ws.cand_cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int ncand = ws.floor != nullptr
+                        ? (int)__hip_atomic_load(&ws.cand_cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : nc;
   uint64_t P = (uint64_t)dstar;
   need -= S.res[1];
   uint32_t cnt_eq = S.h[dstar];
@@ -336,7 +334,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     }
     for (int i = tid; i < k; i += kSelectThreads) oi[i] = S.sel[i];
   }
-  if (tid == 0) { out_cnt[q] = k; ws.cand_cnt[q] = 0; }
+  if (tid == 0) { out_cnt[q] = k; ws.cand_cnt[q] = 0; ws.tau[q] = 0.0f; ws.cnt2[q] = 0; }
 }
 
 hipError_t launch_topk_final(const IndexWs& ws, const ScanArgs& sa, const int32_t* q_vis, int nq, int k,

@@ -91,10 +91,10 @@ def csa2_workspace_bytes(mode: int, nq: int, max_vis: int, h_idx: int, h: int, k
 
 
 def workspace_state_bytes(nq: int) -> int:
-    """Leading workspace bytes that carry state between calls (the per-query
-    histograms and candidate counters: round_up(nq * 2049 * 4, 256)); the
-    rest carries none (see csa2_workspace_bytes in include/csa2.h)."""
-    return (nq * 2049 * 4 + 255) // 256 * 256
+    """Leading workspace bytes that carry state between calls (three
+    per-query counters: round_up(nq * 12, 256)); the rest carries none (see
+    csa2_workspace_bytes in include/csa2.h)."""
+    return (nq * 12 + 255) // 256 * 256
 
 
 def csa2_workspace_init(ws: torch.Tensor, stream=None) -> None:

@@ -117,15 +117,16 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
                                   const uint16_t* kv_rows, const uint16_t* idxk_rows,
                                   int32_t n, hipStream_t s);
 
-/* Bytes of workspace a layer_step call of this shape needs.  Layout:
- * per-query histograms [nq][2048] u32 and candidate counters [nq] u32
- * first; then (Full and Reindex) per-query scores [nq][round_up(max_vis + 2,
- * 64)] fp32, candidate indices and their score keys of the same shape and the
- * dense indexer's candidate masks, that region being at least nq * 8 KB so a
- * CSA2_STEP_POOL layer can score its pool there.  csa2_index_topk accepts a
- * workspace sized by this call for the same shape; attention needs none.  Only the first
- * round_up(nq * 2049 * 4, 256) bytes (histograms and counters) carry state:
- * every call leaves them zeroed for the next one, so zero the whole
+/* Bytes of workspace a layer_step call of this shape needs.  Layout: three
+ * per-query u32 arrays [nq] first (candidate counters, the dense indexer's
+ * thresholds, its full-rescore counters), padded to 256 bytes; then (Full
+ * and Reindex) per-query candidate indices [nq][round_up(max_vis + 2, 64)]
+ * i32, their score keys of the same shape and the per-query scan's chunk key
+ * floors [nq][ceil(max_vis / 2048)] u32, that region being at least
+ * nq * 8 KB so a CSA2_STEP_POOL layer can score its pool there.
+ * csa2_index_topk accepts a workspace sized by this call for the same shape;
+ * attention needs none.  Only the first round_up(nq * 12, 256) bytes carry
+ * state: every call leaves them zeroed for the next one, so zero the whole
  * workspace once after allocating it (csa2_workspace_init does this); the
  * rest is written before it is read within each call.  Calls that share one
  * workspace must not run concurrently. */

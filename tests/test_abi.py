@@ -39,10 +39,11 @@ def test_status_strings():
 def test_workspace_bytes():
     lib = L.load()
     reuse = lib.csa2_workspace_bytes(L.CSA2_REUSE, 32, 65537, 8, 64, 512)
-    assert reuse >= 32 * 2048 * 4                     # histograms (+ attention shares for small batches)
+    assert reuse == 512                               # three per-query counters, padded to 256 bytes
     full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
     assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
-    assert full >= reuse + 2 * 32 * 65537 * 4
+    vstride = (65537 + 2 + 63) // 64 * 64
+    assert full == reuse + 2 * 32 * vstride * 4 + 32 * 33 * 4   # candidates, keys, chunk floors
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4, 100, 8, 0, 512) == 0          # invalid h
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4096, 70000, 8, 64, 512) >= 4096 * 70000 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0

@@ -305,10 +305,19 @@ def test_all_equal_scores_take_lowest_indices():
             assert list(got["idx"][i, :kp]) == list(range(kp))
 
 
-def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
-    spec = W.small_case("repeat", 61, [3000, 900], n_new=1, h_idx=8, h=16, k=512)
-    _, runner = _ops()
-    dc = runner.DeviceCase(spec, gen_device="cpu")
+@pytest.mark.parametrize("prefill", [False, True])
+def test_repeat_calls_are_deterministic_and_workspace_self_cleans(prefill):
+    """Repeated calls give the same bits and leave the workspace's state head
+    zeroed; the prefill case takes the dense indexer with a candidate factor
+    of 1, so some queries go through the full rescore (its counters, too,
+    must be cleared)."""
+    if prefill:
+        spec = W.small_case("repeat_prefill", 62, [9000], n_new=40, h_idx=8, h=16, k=256, modes=(O.FULL,),
+                            prefill=True, page_size=128)
+    else:
+        spec = W.small_case("repeat", 61, [3000, 900], n_new=1, h_idx=8, h=16, k=512)
+    ops, runner = _ops()
+    dc = runner.DeviceCase(spec, gen_device="cpu", dense=prefill, cand_factor=1 if prefill else 0)
     dc.run_group()
     a = dc.results_host()
     for _ in range(3):
@@ -317,7 +326,8 @@ def test_repeat_calls_are_deterministic_and_workspace_self_cleans():
     for x, y in zip(a, b):
         for key in ("idx", "cnt", "out", "lse"):
             assert np.array_equal(x[key], y[key]), key
-    assert int(dc.ws[: 2 * 2048 * 4].view(torch.int32).abs().sum().item()) == 0
+    state = ops.workspace_state_bytes(spec.nq)           # counters and thresholds carry state
+    assert int(dc.ws[:state].view(torch.int32).abs().sum().item()) == 0
 
 
 # ---------------------------------------------------------------------------
