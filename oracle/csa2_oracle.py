@@ -38,6 +38,17 @@ What is computed, and where it comes from:
   is chosen are not given; the reading used: the earlier (Full) layer's own
   Top-P under the same order (P >= k), and a later (Reindex) layer scores only
   the pool's entries and keeps its Top-k among them (pool_index_topk).
+* Block-level pruning, the other half of the hierarchical indexer: the
+  indexer it is informed by scores token-level entries and prunes them by
+  block-level representations ("DeepSeek-V4.1-Flash: Pushing the Limits of
+  KV Cache Compression", Related Work).  No block summary or pruning rule is
+  given; the reading used keeps the Top-K exact: a block is 64 consecutive
+  cache rows, its representation the per-dimension maximum and minimum of
+  its indexer-K (block_bounds), which bounds every score in the block from
+  above (block_score_bound); a query's threshold is the k-th largest score
+  among k or more distinct entries it has scored already (a seed, such as
+  its previous Top-K), and blocks whose bound lies below the threshold are
+  never scored (pruned_index_topk), which cannot change the Top-K.
 * FP4 for the global KV during training, by quantization-aware training:
   "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression".  The
   fake-quantization forward (fake_quant_e2m1) applies the cache's own E2M1 +
@@ -334,6 +345,86 @@ def pool_index_topk(cache: Cache, q_idx, w, q_seq, pool, pool_cnt, k: int):
         idx[i, :kp] = np.sort(t[order[:kp]])
         cnt[i] = kp
     return idx, cnt
+
+
+PRUNE_BLOCK = 64                        # cache rows per block-level representation
+
+
+def block_bounds(cache: Cache) -> Tuple[np.ndarray, np.ndarray]:
+    """Block-level representation of the indexer-K: for every block of 64
+    consecutive physical rows, the per-dimension maximum and minimum of the
+    decoded E4M3 values -> ([n_blocks][128], [n_blocks][128])."""
+    k = e4m3fn_decode(cache.idx_k.reshape(-1, PRUNE_BLOCK, D_INDEX))
+    return k.max(axis=1), k.min(axis=1)
+
+
+def block_score_bound(qi_bytes, w, bmax, bmin) -> np.ndarray:
+    """An upper bound of s_t = sum_h w_h * max(0, q_h . k_t) over every k_t
+    with bmin <= k_t <= bmax in every dimension ([..., 128] boxes -> [...]).
+    q_h . k lies in [lo_h, hi_h], hi_h = sum_d max(q_hd bmax_d, q_hd bmin_d),
+    lo_h = sum_d min(q_hd bmax_d, q_hd bmin_d); max(0, x) never decreases, so
+    w_h max(0, q_h . k) <= w_h max(0, hi_h) when w_h >= 0 and
+    <= w_h max(0, lo_h) when w_h < 0."""
+    qi = e4m3fn_decode(np.asarray(qi_bytes, np.uint8)).reshape(-1, D_INDEX)   # [H_I][128]
+    w = np.asarray(w, dtype=np.float64).reshape(-1)
+    bmax = np.asarray(bmax, np.float64)
+    bmin = np.asarray(bmin, np.float64)
+    total = np.zeros(bmax.shape[:-1], dtype=np.float64)
+    for h in range(qi.shape[0]):
+        a, b = qi[h] * bmax, qi[h] * bmin
+        hi = np.maximum(a, b).sum(axis=-1)
+        lo = np.minimum(a, b).sum(axis=-1)
+        total += w[h] * np.maximum(hi if w[h] >= 0 else lo, 0.0)
+    return total
+
+
+def prune_threshold(cache: Cache, seq: int, vis: int, qi_bytes, w, seed_row, k: int) -> float:
+    """The k-th largest score among the distinct entries of seed_row inside
+    [0, vis) (negative or out-of-range entries ignored), or -inf when fewer
+    than k such entries are given: at least k visible entries score at or
+    above it, so it never exceeds the k-th largest score of the query."""
+    t = np.unique(np.asarray(seed_row, np.int64))
+    t = t[(t >= 0) & (t < vis)]
+    if t.size < k:
+        return -np.inf
+    qi = e4m3fn_decode(np.asarray(qi_bytes, np.uint8)).reshape(-1, D_INDEX)
+    kt = e4m3fn_decode(cache.idxk_rows(seq, t))
+    s = np.maximum(kt @ qi.T, 0.0) @ np.asarray(w, np.float64).reshape(-1) + 0.0
+    return float(np.sort(s)[::-1][k - 1])
+
+
+def pruned_index_topk(cache: Cache, q_idx, w, q_seq, q_vis, seed, seed_cnt, k: int):
+    """index_topk with block-level pruning: per query the threshold T of its
+    seed (prune_threshold over seed[i][:seed_cnt[i]]); the logical 64-entry
+    blocks of its visible range whose bound (block_score_bound over the
+    block's physical rows) lies below T are not scored, and the Top-K is
+    taken over the entries of the other blocks.  Returns idx, cnt and the
+    per-query boolean mask of pruned logical blocks."""
+    q_idx = np.asarray(q_idx, np.uint8)
+    w = np.asarray(w, np.float64)
+    bmax, bmin = block_bounds(cache)
+    ps = cache.page_size
+    nq = len(q_seq)
+    idx = np.full((nq, k), -1, dtype=np.int32)
+    cnt = np.zeros(nq, dtype=np.int32)
+    masks = []
+    for i in range(nq):
+        s, v = int(q_seq[i]), int(q_vis[i])
+        thr = prune_threshold(cache, s, v, q_idx[i], w[i], np.asarray(seed[i])[:int(seed_cnt[i])], k)
+        nb = (v + PRUNE_BLOCK - 1) // PRUNE_BLOCK
+        first = np.arange(nb, dtype=np.int64) * PRUNE_BLOCK               # logical first entry of each block
+        phys = (cache.page_table[s, first // ps].astype(np.int64) * ps + first % ps) // PRUNE_BLOCK
+        ub = block_score_bound(q_idx[i], w[i], bmax[phys], bmin[phys])
+        pruned = ub < thr
+        sc = index_scores(cache, s, v, q_idx[i], w[i])
+        keep = ~np.repeat(pruned, PRUNE_BLOCK)[:v]
+        t = np.nonzero(keep)[0]
+        kp = min(k, t.size)
+        order = np.lexsort((t, -sc[t]))
+        idx[i, :kp] = np.sort(t[order[:kp]])
+        cnt[i] = kp
+        masks.append(pruned)
+    return idx, cnt, masks
 
 
 def attend(cache: Cache, seq: int, q_bits, idx_row, cnt: int, sm_scale: float):

@@ -34,7 +34,8 @@ FULL, REINDEX, REUSE = 0, 1, 2
 MODE_NAMES = {FULL: "full", REINDEX: "reindex", REUSE: "reuse"}
 
 # purpose tags for the per-piece generators
-_TAG_KV, _TAG_IK, _TAG_QI, _TAG_W, _TAG_Q, _TAG_LEN, _TAG_PERM = 1, 2, 3, 4, 5, 6, 7
+_TAG_KV, _TAG_IK, _TAG_QI, _TAG_W, _TAG_Q, _TAG_LEN, _TAG_PERM, _TAG_CTR = 1, 2, 3, 4, 5, 6, 7, 8
+CLUSTER_BLOCK = 64      # entries per centre of a clustered indexer-K
 
 
 def _seed_of(seed: int, tag: int, index: int) -> int:
@@ -76,6 +77,7 @@ class CaseSpec:
     prefill: bool = False           # queries are the n_new appended rows (causal), else one query per sequence
     extra_pages: int = 0            # unused pages in the pool (exercise page ids beyond the used range)
     pool_k: int = 0                 # > 0: hierarchical indexer, the Full layer's Top-pool_k is the Reindex pool
+    clustered: bool = False         # indexer-K rows near a per-64-entry-block centre (block structure to prune on)
 
     @property
     def num_seqs(self) -> int:
@@ -143,10 +145,27 @@ def kv_rows(spec: CaseSpec, s: int, device="cpu") -> torch.Tensor:
 
 
 def idxk_rows(spec: CaseSpec, s: int, device="cpu") -> torch.Tensor:
-    """bf16 bits [seq_len_after(s)][128] of sequence s: integers in [-8, 8] or N(0,1)."""
+    """bf16 bits [seq_len_after(s)][128] of sequence s: integers in [-8, 8] or N(0,1).
+
+    Clustered: entry t lies near the centre of its 64-entry block t // 64
+    (one centre per block and dimension): integer centres in [-6, 6], with an
+    integer offset in {-1, 0, 1} in the eighth of the (block, dimension)
+    pairs drawn to vary; or N(0,1) centres plus N(0, 0.02^2) offsets."""
     n = spec.seq_len_after(s)
     g = _gen(spec.seed, _TAG_IK, s, device)
-    if spec.integer_indexer:
+    if spec.clustered:
+        nb = (n + CLUSTER_BLOCK - 1) // CLUSTER_BLOCK
+        gc = _gen(spec.seed, _TAG_CTR, s, device)
+        if spec.integer_indexer:
+            ctr = torch.randint(-6, 7, (nb, D_INDEX), generator=gc, device=device).to(torch.float32)
+            vary = (torch.randint(0, 8, (nb, D_INDEX), generator=gc, device=device) == 0).to(torch.float32)
+            off = torch.randint(-1, 2, (n, D_INDEX), generator=g, device=device).to(torch.float32)
+            off = off * vary.repeat_interleave(CLUSTER_BLOCK, dim=0)[:n]
+        else:
+            ctr = torch.randn(nb, D_INDEX, generator=gc, device=device)
+            off = 0.02 * torch.randn(n, D_INDEX, generator=g, device=device)
+        x = ctr.repeat_interleave(CLUSTER_BLOCK, dim=0)[:n] + off
+    elif spec.integer_indexer:
         x = torch.randint(-8, 9, (n, D_INDEX), generator=g, device=device).to(torch.float32)
     else:
         x = torch.randn(n, D_INDEX, generator=g, device=device)
@@ -228,8 +247,9 @@ def config(i: int, integer_indexer: Optional[bool] = None) -> CaseSpec:
 def small_case(name: str, seed: int, cached: List[int], n_new: int = 1, h_idx: int = 8, h: int = 16,
                k: int = 512, modes=(FULL, REINDEX, REUSE, REUSE), integer_indexer: bool = False,
                page_size: int = 64, shuffle_pages: bool = True, prefill: bool = False,
-               extra_pages: int = 3, pool_k: int = 0) -> CaseSpec:
+               extra_pages: int = 3, pool_k: int = 0, clustered: bool = False) -> CaseSpec:
     """A reduced workload for oracle-checked parity: same structure, small sizes."""
     return CaseSpec(name, seed, list(cached), n_new, h_idx, h, k=k, modes=tuple(modes),
                     integer_indexer=integer_indexer, page_size=page_size,
-                    shuffle_pages=shuffle_pages, prefill=prefill, extra_pages=extra_pages, pool_k=pool_k)
+                    shuffle_pages=shuffle_pages, prefill=prefill, extra_pages=extra_pages, pool_k=pool_k,
+                    clustered=clustered)
