@@ -19,13 +19,15 @@ NUM_KCLASSES = 7
 DTYPE_F32, DTYPE_BF16 = 0, 1
 MAX_K, MAX_H_IDX, MAX_H, MIN_PAGE_SIZE = 2048, 16, 128, 64
 STATIC_SCRATCH_BYTES = 64 << 20
-STEP_DENSE_INDEX, STEP_POOL, STEP_ATTN_PER_HEAD_GROUP = 1, 2, 4
+STEP_DENSE_INDEX, STEP_POOL, STEP_ATTN_PER_HEAD_GROUP, STEP_PRUNE = 1, 2, 4, 8
+PRUNE_BLOCK, PRUNE_BOUND_BYTES = 64, 256
 DENSE_RESCORE_ALL = -1
 
 
 class CacheView(ctypes.Structure):
     _fields_ = [("kv", c_void_p), ("idx_k", c_void_p), ("page_table", c_void_p), ("seq_lens", c_void_p),
-                ("num_pages", c_int32), ("page_size", c_int32), ("num_seqs", c_int32), ("max_pages", c_int32)]
+                ("num_pages", c_int32), ("page_size", c_int32), ("num_seqs", c_int32), ("max_pages", c_int32),
+                ("idxk_bounds", c_void_p)]
 
 
 class TimingRing(ctypes.Structure):
@@ -46,7 +48,8 @@ class StepArgs(ctypes.Structure):
                 ("idx", c_void_p), ("cnt", c_void_p), ("out", c_void_p), ("lse", c_void_p),
                 ("ws", c_void_p), ("ws_bytes", c_size_t), ("flags", ctypes.c_uint32),
                 ("pool", c_void_p), ("pool_cnt", c_void_p), ("pool_k", c_int32),
-                ("dense_cand_factor", c_int32), ("timing", ctypes.POINTER(Timing))]
+                ("dense_cand_factor", c_int32), ("timing", ctypes.POINTER(Timing)),
+                ("seed", c_void_p), ("seed_cnt", c_void_p)]
 
 
 GROUP_MAX_LAYERS, GROUP_MAX_AUX = 64, 4
@@ -90,11 +93,13 @@ def load() -> ctypes.CDLL:
     lib.csa2_group_events.argtypes = [c_int32, c_int32]
     lib.csa2_group_events.restype = c_int32
     lib.csa2_group_step.argtypes = [c_int32, P(c_int32), P(StepArgs), c_void_p, P(GroupExec)]
+    lib.csa2_idxk_bounds_build.argtypes = [P(CacheView), c_int32, c_int32, c_void_p]
     lib.csa2_status_string.argtypes = [c_int32]
     lib.csa2_status_string.restype = ctypes.c_char_p
     for fn in ("csa2_append_quant_fp4", "csa2_workspace_init", "csa2_index_topk", "csa2_prefill_index_topk",
                "csa2_pool_index_topk", "csa2_sparse_attn",
-               "csa2_layer_step", "csa2_layer_step_static", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4"):
+               "csa2_layer_step", "csa2_layer_step_static", "csa2_group_step", "csa2_lse_merge", "csa2_fake_quant_fp4",
+               "csa2_idxk_bounds_build"):
         getattr(lib, fn).restype = c_int32
     _lib = lib
     return lib

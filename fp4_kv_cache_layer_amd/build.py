@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libcsa2.so")
 PROBE_LIB = os.path.join(PKG, "libcsa2_probe.so")
 PROBE_SOURCE = "probe.hip"
 SOURCES = ["api.hip", "append_quant.hip", "index_scan.hip", "prefill_scan.hip", "topk_select.hip", "sparse_attn.hip",
-           "lse_merge.hip", "fake_quant.hip", "pool_index.hip"]
+           "lse_merge.hip", "fake_quant.hip", "pool_index.hip", "prune.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

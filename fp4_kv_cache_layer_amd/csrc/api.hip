@@ -119,7 +119,7 @@ csa2_status validate_append(const csa2_cache_view* c, const int32_t* slots, cons
   return CSA2_OK;
 }
 
-IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool dense) {
+IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool dense, bool prune) {
   IndexWs r;
   r.vis_cap = max_vis;
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
@@ -131,6 +131,9 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool d
   r.ckey = reinterpret_cast<uint32_t*>(p + score_off + (size_t)nq * (size_t)r.vstride * 4);
   r.fstride = (max_vis + kScanChunk - 1) / kScanChunk;
   r.floor = dense ? nullptr : reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4);
+  r.prune = prune ? reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4 +
+                                                (size_t)nq * (size_t)r.fstride * 4)
+                  : nullptr;
   return r;
 }
 
@@ -156,6 +159,7 @@ struct Step {
   CacheArgs ca;
   bool dense;
   bool pool;                 // hierarchical indexer (Full: writes the pool; Reindex: reads it)
+  bool prune;                // block-level pruning of the per-query indexer
   bool share_heads;          // attention: shared-row form for large 64-head batches
   int cand_factor;           // dense indexer candidate factor
   const csa2_timing* tm;     // nullable
@@ -178,7 +182,17 @@ csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
   if (!a || (mode_value != CSA2_FULL && mode_value != CSA2_REINDEX && mode_value != CSA2_REUSE))
     return CSA2_ERR_INVALID_ARG;
   const csa2_mode mode = static_cast<csa2_mode>(mode_value);
-  if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL | CSA2_STEP_ATTN_PER_HEAD_GROUP)) return CSA2_ERR_INVALID_ARG;
+  if (a->flags & ~(CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL | CSA2_STEP_ATTN_PER_HEAD_GROUP | CSA2_STEP_PRUNE))
+    return CSA2_ERR_INVALID_ARG;
+  const bool prune = (a->flags & CSA2_STEP_PRUNE) != 0;
+  if (prune) {
+    if (mode == CSA2_REUSE || (a->flags & (CSA2_STEP_DENSE_INDEX | CSA2_STEP_POOL))) return CSA2_ERR_INVALID_ARG;
+    if (!a->cache || !a->cache->idxk_bounds || !aligned(a->cache->idxk_bounds, 16)) return CSA2_ERR_INVALID_ARG;
+    if (a->nq > 0 && (!a->seed || !a->seed_cnt || !aligned(a->seed, 4) || !aligned(a->seed_cnt, 4)))
+      return CSA2_ERR_INVALID_ARG;
+  } else if (a->seed || a->seed_cnt) {
+    return CSA2_ERR_INVALID_ARG;
+  }
   if (a->flags & CSA2_STEP_DENSE_INDEX) {
     if (a->dense_cand_factor < CSA2_DENSE_RESCORE_ALL || a->dense_cand_factor > 64) return CSA2_ERR_INVALID_ARG;
   } else if (a->dense_cand_factor != 0) {
@@ -216,6 +230,7 @@ csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
   p->a = a;
   p->dense = (a->flags & CSA2_STEP_DENSE_INDEX) != 0;
   p->pool = pool;
+  p->prune = prune;
   p->share_heads = (a->flags & CSA2_STEP_ATTN_PER_HEAD_GROUP) == 0;
   p->cand_factor = a->dense_cand_factor == 0 ? kDefaultCandFactor
                    : a->dense_cand_factor == CSA2_DENSE_RESCORE_ALL ? 0 : a->dense_cand_factor;
@@ -228,7 +243,7 @@ csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
     // the pool scores reuse the candidate region (dead once the pool is selected)
     const size_t need = std::max(index_score_bytes(a->nq, a->max_vis), pool ? pool_score_bytes(a->nq, a->pool_k) : 0);
     if (a->ws_bytes < z + need) return CSA2_ERR_WORKSPACE;
-    p->iw = index_ws(a->ws, a->nq, a->max_vis, z, p->dense);
+    p->iw = index_ws(a->ws, a->nq, a->max_vis, z, p->dense, prune);
     if (pool) p->pool_sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a->ws) + z);
   } else if (a->ws && !aligned(a->ws, 16)) {
     return CSA2_ERR_INVALID_ARG;
@@ -240,7 +255,15 @@ csa2_status stage_append(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
   if (p.mode != CSA2_FULL || a->n_new == 0) return CSA2_OK;
   TimedLaunch t(p.tm, CSA2_KCLASS_APPEND);
-  return hip_status(launch_append_quant(p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
+  uint8_t* const bounds = a->cache->idxk_bounds;
+  if (!bounds)
+    return hip_status(launch_append_quant(p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new, s, t.ev));
+  // the appended rows' blocks get their representation recomputed
+  csa2_status st = hip_status(launch_append_quant(p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new,
+                                                  s, t.ev.first()));
+  if (st != CSA2_OK) return st;
+  return hip_status(launch_idxk_bounds(p.ca.idx_k, bounds, a->new_slots, 0, a->n_new,
+                                       (int64_t)p.ca.num_pages << p.ca.lg_page, s, t.ev.last()));
 }
 
 csa2_status stage_scan(const Step& p, hipStream_t s) {
@@ -254,6 +277,13 @@ csa2_status stage_scan(const Step& p, hipStream_t s) {
                                           tp.ev));
   }
   TimedLaunch t(p.tm, CSA2_KCLASS_SCAN);
+  if (p.prune) {
+    csa2_status st = hip_status(launch_prune_mask(p.ca, a->cache->idxk_bounds, a->q_idx, a->w, a->q_seq, a->q_vis,
+                                                  a->seed, a->seed_cnt, a->nq, a->h_idx, a->k, p.iw, s, t.ev.first()));
+    if (st != CSA2_OK) return st;
+    return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis,
+                                        p.iw, s, t.ev.last()));
+  }
   return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx,
                                       p.pool ? a->pool_k : a->k, a->max_vis, p.iw, s, t.ev));
 }
@@ -354,6 +384,17 @@ size_t csa2_workspace_bytes(csa2_mode mode_arg, int32_t nq, int32_t max_vis, int
   return b;
 }
 
+csa2_status csa2_idxk_bounds_build(const csa2_cache_view* c, int32_t first_block, int32_t n_blocks, hipStream_t s) {
+  CacheArgs ca;
+  csa2_status st = check_cache(c, &ca);
+  if (st != CSA2_OK) return st;
+  if (!c->idxk_bounds || !aligned(c->idxk_bounds, 16)) return CSA2_ERR_INVALID_ARG;
+  const int64_t nblocks = ((int64_t)c->num_pages << ca.lg_page) / CSA2_PRUNE_BLOCK;
+  if (first_block < 0 || n_blocks < 0 || (int64_t)first_block + n_blocks > nblocks) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_idxk_bounds(ca.idx_k, c->idxk_bounds, nullptr, first_block, n_blocks,
+                                       (int64_t)c->num_pages << ca.lg_page, s));
+}
+
 size_t csa2_pool_workspace_bytes(int32_t nq, int32_t p) {
   if (nq <= 0 || p < 1 || p > CSA2_MAX_K) return 0;
   return pool_score_bytes(nq, p);
@@ -380,7 +421,7 @@ csa2_status csa2_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, cons
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
-                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), false), false, s);
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), false, false), false, s);
 }
 
 csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
@@ -390,7 +431,7 @@ csa2_status csa2_prefill_index_topk(const csa2_cache_view* c, const uint8_t* q_i
   csa2_status st = validate_index(c, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt, ws, ws_bytes, &ca);
   if (st != CSA2_OK || nq == 0) return st;
   return run_index(ca, q_idx, w, q_seq, q_vis, nq, h_idx, k, max_vis, out_idx, out_cnt,
-                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), true), true, s);
+                   index_ws(ws, nq, max_vis, zero_state_bytes(nq), true, false), true, s);
 }
 
 csa2_status csa2_pool_index_topk(const csa2_cache_view* c, const uint8_t* q_idx, const float* w,

@@ -38,7 +38,8 @@ __device__ __forceinline__ int64_t entry_row_clamped(const int32_t* __restrict__
 //               words again.
 //   [Z, ...)    candidate indices [nq][vstride] i32, their score keys
 //               [nq][vstride] u32, then (per-query scan) the chunk key floors
-//               [nq][fstride] u32; no initial state needed.
+//               [nq][fstride] u32 and the pruned-block masks [nq][fstride]
+//               u32; no initial state needed.
 struct IndexWs {
   uint32_t* cand_cnt;
   float* tau;            // dense indexer: the query's candidate threshold
@@ -52,7 +53,15 @@ struct IndexWs {
   // candidates are exact above its threshold.
   uint32_t* floor;
   int32_t fstride;
+  // Block-level pruning: per (query, chunk) the mask of its 64-entry blocks
+  // that cannot hold an entry of the Top-k, [nq][fstride] u32 (bit i: block
+  // 32 * chunk + i); NULL when the call prunes nothing.  The query's
+  // threshold is in tau.
+  uint32_t* prune;
 };
+
+constexpr int kPruneBlockRows = 64;          // cache rows per block-level representation
+constexpr int kPruneBoundBytes = 256;        // per block: 128 maximum codes, 128 minimum codes
 
 // A query's visible count as the indexer kernels use it: clamped to [0, max_vis].
 __device__ __forceinline__ int clamp_vis(int v, const IndexWs& ws) { return min(max(v, 0), ws.vis_cap); }
@@ -125,6 +134,14 @@ hipError_t launch_prefill_scan(const CacheArgs& c, const uint8_t* q_idx, const f
                                const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
                                int cand_factor, hipStream_t s, const KEvents& ev = {},
                                const KEvents& ev_product = {});
+// Block-level pruning: the bounds of the blocks holding the given slots
+// (slots != NULL, n slots) or of blocks first_block .. first_block + n - 1;
+// and per query the threshold of its seed and the mask of pruned blocks.
+hipError_t launch_idxk_bounds(const uint8_t* idx_k, uint8_t* bounds, const int32_t* slots, int first_block,
+                              int n, int64_t n_rows, hipStream_t s, const KEvents& ev = {});
+hipError_t launch_prune_mask(const CacheArgs& c, const uint8_t* bounds, const uint8_t* q_idx, const float* w,
+                             const int32_t* q_seq, const int32_t* q_vis, const int32_t* seed, const int32_t* seed_cnt,
+                             int nq, int h_idx, int k, const IndexWs& ws, hipStream_t s, const KEvents& ev = {});
 // The final select over a query's candidate list (the dense indexer's, or the
 // per-query scan's, which sa and ws.floor let it repair).
 hipError_t launch_topk_final(const IndexWs& ws, const ScanArgs& sa, const int32_t* q_vis, int nq, int k,

@@ -48,7 +48,7 @@ size_t zero_state_bytes(int32_t nq) {
 size_t index_score_bytes(int32_t nq, int32_t max_vis) {
   const size_t v = (size_t)index_vstride(max_vis);
   const size_t fstride = ((size_t)max_vis + kScanChunk - 1) / kScanChunk;
-  return (size_t)nq * 8 * v + (size_t)nq * fstride * 4;   // candidates, candidate keys, chunk floors
+  return (size_t)nq * 8 * v + (size_t)nq * fstride * 8;   // candidates, candidate keys, chunk floors, prune masks
 }
 
 __global__ void __launch_bounds__(kScanWaves * 64)
@@ -73,6 +73,19 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   if (t0 >= vis || vis <= k) return;                  // uniform; with V <= k the select takes everything
   const int t1 = min(vis, t0 + kScanChunk);
   const int tid = threadIdx.x;
+  // block-level pruning: blocks of this chunk that cannot hold a Top-k entry
+  const uint32_t pmask = ws.prune ? ws.prune[(int64_t)q * ws.fstride + chunk] : 0u;
+  const int nblk = (t1 - t0 + kPruneBlockRows - 1) / kPruneBlockRows;
+  const uint32_t inrange = nblk >= 32 ? 0xFFFFFFFFu : ((1u << nblk) - 1u);
+  if (pmask != 0 && (pmask & inrange) == inrange) {
+    // nothing here reaches the threshold: no candidates; the floor is the
+    // threshold's 22-bit prefix, so the final select never rescores the chunk
+    // unless its k-th key falls below the threshold
+    if (tid == 0)
+      ws.floor[(int64_t)q * ws.fstride + chunk] = score_key(ws.tau[q]) & ~((1u << (32 - 2 * kHistBits)) - 1u);
+    return;
+  }
+  auto pruned_tile = [&](int j) { return ((pmask >> (j >> 2)) & 1u) != 0u; };   // 4 tiles per block
   for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
 
   const int lane = tid & 63;
@@ -119,7 +132,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   intx8 buf[kScanDepth];
 #pragma unroll
   for (int d = 0; d + 1 < kScanDepth; ++d) load(wave + d * kScanWaves, buf[d]);
-  if (ntiles == kScanChunk / 16) {
+  if (ntiles == kScanChunk / 16 && pmask == 0) {
     // full chunk: a fixed schedule, unrolled, so every wait on the ring is exact
     constexpr int kSteps = kScanChunk / 16 / kScanWaves;
 #pragma unroll
@@ -129,12 +142,14 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       process(wave + u * kScanWaves, buf[u % kScanDepth]);
     }
   } else {
+    // (tiles of pruned blocks are neither loaded nor scored)
     for (int j = wave; j < ntiles; j += kScanDepth * kScanWaves) {
 #pragma unroll
       for (int u = 0; u < kScanDepth; ++u) {
-        load(j + (u + kScanDepth - 1) * kScanWaves, buf[(u + kScanDepth - 1) % kScanDepth]);
+        const int jl = j + (u + kScanDepth - 1) * kScanWaves;
+        if (!pruned_tile(min(jl, ntiles - 1))) load(jl, buf[(u + kScanDepth - 1) % kScanDepth]);
         if (j + u * kScanWaves >= ntiles) break;
-        process(j + u * kScanWaves, buf[u]);
+        if (!pruned_tile(j + u * kScanWaves)) process(j + u * kScanWaves, buf[u]);
       }
     }
   }
@@ -142,17 +157,24 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 
   // the chunk's local threshold: key floor of its L-th largest entry, to 22 bits
   const int nloc = t1 - t0;
+  // entries of unpruned blocks
+  int nreal = nloc;
+  if (pmask != 0)
+    for (int bl = 0; bl < nblk; ++bl)
+      if ((pmask >> bl) & 1u) nreal -= min(kPruneBlockRows, nloc - bl * kPruneBlockRows);
+  auto live = [&](int i) { return ((pmask >> (i / kPruneBlockRows)) & 1u) == 0u; };
   const int L = scan_local_rank(k, vis);
   uint32_t floor_key = 0;                             // a chunk of at most L entries keeps them all
-  int n = nloc;                                       // entries at or above the floor
-  if (nloc > L) {
+  int n = nreal;                                      // entries at or above the floor
+  if (nreal > L) {
     find_digit(hist, kHistBins, (uint32_t)L, res);    // ends with a barrier
     const uint32_t d1 = res[0], above1 = res[1];
     for (int i = tid; i < kHistBins; i += kScanWaves * 64) hist[i] = 0;
     lds_barrier();
     for (int i = tid; i < nloc; i += kScanWaves * 64) {
       const uint32_t key = score_key(sc[i]);
-      if ((key >> (32 - kHistBits)) == d1) atomicAdd(&hist[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+      if (live(i) && (key >> (32 - kHistBits)) == d1)
+        atomicAdd(&hist[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
     }
     lds_barrier();
     find_digit(hist, kHistBins, (uint32_t)L - above1, res);
@@ -176,7 +198,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int i = u * kScanWaves * 64 + tid;
-    mine += (i < nloc && score_key(sc[i]) >= floor_key) ? 1u : 0u;
+    mine += (i < nloc && live(i) && score_key(sc[i]) >= floor_key) ? 1u : 0u;
   }
   const uint32_t x = wave_incl_sum(mine);
   int wbase = 0;
@@ -186,7 +208,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = u * kScanWaves * 64 + tid;
-      if (i < nloc && score_key(sc[i]) >= floor_key) list[pos++] = i;
+      if (i < nloc && live(i) && score_key(sc[i]) >= floor_key) list[pos++] = i;
     }
   }
   if (tid == 0) base = my_base;

@@ -60,18 +60,33 @@ class Cache:
     kv    [num_pages][page_size][272] uint8 (E2M1 codes + E8M0 scales)
     idx_k [num_pages][page_size][128] uint8 (E4M3FN)
     page_table [num_seqs][max_pages] int32, seq_lens [num_seqs] int32.
+    bounds (optional, bounds=True): [num_pages * page_size / 64][256] uint8,
+    the block-level representation of the indexer-K that block-level pruning
+    reads (csa2_idxk_bounds_build; layer steps refresh the blocks they append
+    to).
     """
 
     def __init__(self, num_pages: int, page_size: int, page_table: torch.Tensor,
-                 seq_lens: Optional[torch.Tensor] = None, device="cuda", kv=None, idx_k=None):
+                 seq_lens: Optional[torch.Tensor] = None, device="cuda", kv=None, idx_k=None, bounds: bool = False):
         self.kv = kv if kv is not None else torch.zeros((num_pages, page_size, KV_ROW_BYTES), dtype=torch.uint8, device=device)
         self.idx_k = idx_k if idx_k is not None else torch.zeros((num_pages, page_size, IDXK_ROW_BYTES), dtype=torch.uint8, device=device)
         self.page_table = page_table.to(device=device, dtype=torch.int32).contiguous()
         ns = self.page_table.shape[0]
         self.seq_lens = (seq_lens if seq_lens is not None else torch.zeros(ns, dtype=torch.int32)).to(device=device, dtype=torch.int32).contiguous()
         self.num_pages, self.page_size = num_pages, page_size
+        self.bounds = (torch.zeros((num_pages * page_size // L.PRUNE_BLOCK, L.PRUNE_BOUND_BYTES), dtype=torch.uint8,
+                                   device=device) if bounds else None)
         self._view = L.CacheView(_ptr(self.kv), _ptr(self.idx_k), _ptr(self.page_table), _ptr(self.seq_lens),
-                                 num_pages, page_size, ns, self.page_table.shape[1])
+                                 num_pages, page_size, ns, self.page_table.shape[1],
+                                 _ptr(self.bounds) if bounds else None)
+
+    def build_bounds(self, first_block: int = 0, n_blocks: Optional[int] = None, stream=None) -> None:
+        """Recomputes the block-level representation of blocks
+        first_block .. first_block + n_blocks - 1 (default: all) from idx_k."""
+        if n_blocks is None:
+            n_blocks = self.num_pages * self.page_size // L.PRUNE_BLOCK - first_block
+        L.check("csa2_idxk_bounds_build",
+                L.load().csa2_idxk_bounds_build(ctypes.byref(self._view), first_block, n_blocks, _stream(stream)))
 
     @property
     def view(self) -> L.CacheView:
@@ -210,13 +225,16 @@ class LayerCall:
                  new_idxk: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                  dense: bool = False, pool: Optional[torch.Tensor] = None, pool_cnt: Optional[torch.Tensor] = None,
                  dense_cand_factor: int = 0, attn_per_head_group: bool = False,
-                 timing: Optional["Timing"] = None):
+                 timing: Optional["Timing"] = None, seed: Optional[torch.Tensor] = None,
+                 seed_cnt: Optional[torch.Tensor] = None):
         """pool / pool_cnt ([nq][P], [nq] int32): hierarchical indexer; a Full
         layer writes its Top-P there, a Reindex layer scores only those.
         dense_cand_factor: the dense indexer's candidate factor (0 default,
         L.DENSE_RESCORE_ALL rescores every query).  attn_per_head_group: one
         attention workgroup per 16-head group even where the shared-row form
-        applies.  timing: device timestamps of this call's kernels."""
+        applies.  timing: device timestamps of this call's kernels.
+        seed / seed_cnt ([nq][k], [nq] int32): block-level pruning of the
+        indexer (needs a cache with bounds); the seed may be idx itself."""
         self.mode = mode
         self.cache = cache
         nq, h = q.shape[0], q.shape[1]
@@ -238,7 +256,11 @@ class LayerCall:
         if pool is not None:
             _shape(pool, _I32, (nq, pool.shape[1]), "pool")
             _shape(pool_cnt, _I32, (nq,), "pool_cnt")
-        self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws, pool, pool_cnt)
+        if seed is not None:
+            _shape(seed, _I32, (nq, k), "seed")
+            _shape(seed_cnt, _I32, (nq,), "seed_cnt")
+        self._keep = (q, q_seq, q_vis, idx, cnt, out, lse, q_idx, w, new_slots, new_kv, new_idxk, ws, pool, pool_cnt,
+                      seed, seed_cnt)
         a = L.StepArgs()
         a.cache = ctypes.pointer(cache.view)
         if mode == FULL and new_slots is not None and new_slots.numel() > 0:
@@ -257,6 +279,9 @@ class LayerCall:
         if pool is not None:
             a.flags |= L.STEP_POOL
             a.pool, a.pool_cnt, a.pool_k = _ptr(pool), _ptr(pool_cnt), pool.shape[1]
+        if seed is not None:
+            a.flags |= L.STEP_PRUNE
+            a.seed, a.seed_cnt = _ptr(seed), _ptr(seed_cnt)
         self.args = a
         self.timing = None
         self.set_timing(timing)

@@ -36,10 +36,14 @@ class DeviceCase:
 
     def __init__(self, spec: W.CaseSpec, gen_device: str = "cpu", device: str = "cuda",
                  dense: Optional[bool] = None, group: int = 0, shared_ws: bool = False,
-                 cand_factor: int = 0, attn_per_head_group: bool = False, poison_ws: bool = False):
+                 cand_factor: int = 0, attn_per_head_group: bool = False, poison_ws: bool = False,
+                 prune: bool = False):
         """poison_ws: before every layer call, fill the workspace bytes that
         carry no state between calls with 0xFF (a check that no kernel reads
-        what the same call did not write)."""
+        what the same call did not write).  prune: the cache keeps its
+        block-level representation and every Full and Reindex layer prunes
+        its indexer with its own previous selection as the seed (the first
+        call, with empty outputs, prunes nothing)."""
         self.spec = spec
         self.poison_ws = poison_ws
         self.cand_factor = cand_factor if (spec.prefill if dense is None else dense) else 0
@@ -53,11 +57,14 @@ class DeviceCase:
         pt = torch.from_numpy(W.page_table(spec))
         seq_lens = torch.tensor([spec.seq_len_after(s) for s in range(spec.num_seqs)], dtype=torch.int32)
         self.page_table = pt
-        self.cache = ops.Cache(spec.total_pages(), spec.page_size, pt, seq_lens, device=device)
+        self.prune = prune
+        self.cache = ops.Cache(spec.total_pages(), spec.page_size, pt, seq_lens, device=device, bounds=prune)
         self.q_seq = torch.from_numpy(spec.q_seq()).to(device)
         self.q_vis = torch.from_numpy(spec.q_vis()).to(device)
         self.max_vis = int(spec.q_vis().max()) if spec.nq else 0
         self._fill_cache()
+        if prune:
+            self.cache.build_bounds()
         self._layers()
 
     # -- cache fill: cached entries written by bulk append; new rows kept for the Full layer --
@@ -111,8 +118,8 @@ class DeviceCase:
             if mode == ops.REUSE:
                 idx, cnt = full_idx, full_cnt
             else:
-                idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
-                cnt = torch.empty(nq, dtype=torch.int32, device=dev)
+                idx = torch.full((nq, k), -1, dtype=torch.int32, device=dev)
+                cnt = torch.zeros(nq, dtype=torch.int32, device=dev)
                 if mode == ops.FULL:
                     full_idx, full_cnt = idx, cnt
             self.outputs.append(dict(idx=idx, cnt=cnt, out=out, lse=lse))
@@ -144,6 +151,8 @@ class DeviceCase:
         if mode == ops.REUSE:
             return ops.LayerCall(mode, *common, ws=ws, **opts)
         opts.update(dense=self.dense, pool=pool, pool_cnt=pool_cnt, dense_cand_factor=self.cand_factor)
+        if self.prune:
+            opts.update(seed=o["idx"], seed_cnt=o["cnt"])
         if mode == ops.FULL:
             return ops.LayerCall(mode, *common, q_idx=qi, w=w, new_slots=self.new_slots, new_kv=self.new_kv,
                                  new_idxk=self.new_ik, ws=ws, **opts)

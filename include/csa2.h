@@ -103,7 +103,30 @@ typedef struct {
   int32_t page_size;          /* power of two, >= CSA2_MIN_PAGE_SIZE          */
   int32_t num_seqs;
   int32_t max_pages;
+  uint8_t*       idxk_bounds; /* nullable: block-level representation of the
+                                 indexer-K for CSA2_STEP_PRUNE,
+                                 [num_pages * page_size / 64][2][128] E4M3
+                                 codes (see csa2_idxk_bounds_build)          */
 } csa2_cache_view;
+
+/* Block-level representation of the indexer-K, the summary the pruning of
+ * CSA2_STEP_PRUNE reads.  The indexer the hierarchical indexer is informed by
+ * scores token-level entries and prunes them by block-level representations
+ * ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+ * Related Work); the pages define no summary, the reading here: a block is
+ * CSA2_PRUNE_BLOCK consecutive physical rows (so a block never straddles a
+ * page), its representation 256 bytes, the E4M3 code of each dimension's
+ * largest value over the block's rows followed by that of its smallest.
+ * csa2_idxk_bounds_build recomputes blocks first_block .. first_block +
+ * n_blocks - 1 from c->idx_k (after bulk writes; csa2_layer_step refreshes
+ * the blocks of the rows it appends itself whenever c->idxk_bounds is set).
+ * Rows of a block that were never written count with whatever bytes they
+ * hold, which only widens the bounds.  Errors: CSA2_ERR_INVALID_ARG for a
+ * null or misaligned idxk_bounds (16 bytes), a bad cache or a block range
+ * outside the cache; CSA2_ERR_HIP if the launch fails. */
+#define CSA2_PRUNE_BLOCK 64
+csa2_status csa2_idxk_bounds_build(const csa2_cache_view* c, int32_t first_block, int32_t n_blocks,
+                                   hipStream_t s);
 
 /* Quantize-on-append ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
  * Compression", Method: FP4 global KV with an inference system built to
@@ -121,9 +144,11 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
  * per-query u32 arrays [nq] first (candidate counters, the dense indexer's
  * thresholds, its full-rescore counters), padded to 256 bytes; then (Full
  * and Reindex) per-query candidate indices [nq][round_up(max_vis + 2, 64)]
- * i32, their score keys of the same shape and the per-query scan's chunk key
- * floors [nq][ceil(max_vis / 2048)] u32, that region being at least
- * nq * 8 KB so a CSA2_STEP_POOL layer can score its pool there.
+ * i32, their score keys of the same shape, the per-query scan's chunk key
+ * floors [nq][ceil(max_vis / 2048)] u32 and the CSA2_STEP_PRUNE block masks
+ * of the same shape (bit i of word c: block 32c + i of the query's visible
+ * range holds no Top-k entry), that region being at least nq * 8 KB so a
+ * CSA2_STEP_POOL layer can score its pool there.
  * csa2_index_topk accepts a workspace sized by this call for the same shape;
  * attention needs none.  Only the first round_up(nq * 12, 256) bytes carry
  * state: every call leaves them zeroed for the next one, so zero the whole
@@ -264,6 +289,12 @@ typedef struct {
                                     full; must be 0 without the flag          */
   struct csa2_timing* timing;    /* nullable: device timestamps of this call's
                                     kernels (see csa2_timing)                  */
+  const int32_t*  seed;          /* CSA2_STEP_PRUNE: [nq][k] entry indices
+                                    whose scores set each query's threshold
+                                    (e.g. its previous Top-K row; may be idx
+                                    itself, read before the layer writes it) */
+  const int32_t*  seed_cnt;      /* CSA2_STEP_PRUNE: [nq] entries of each seed
+                                    row to use (clamped to [0, k])            */
 } csa2_step_args;
 
 /* Full/Reindex: score as csa2_prefill_index_topk (all queries of the call
@@ -280,6 +311,18 @@ typedef struct {
  * this flag keeps one workgroup per 16-head group instead.  Both forms give
  * identical bits (it exists to test and measure that). */
 #define CSA2_STEP_ATTN_PER_HEAD_GROUP 4u
+/* Block-level pruning of a Full or Reindex layer's per-query indexer (not
+ * with CSA2_STEP_DENSE_INDEX or CSA2_STEP_POOL; needs cache->idxk_bounds).
+ * Per query, the threshold T is the k-th largest score (the indexer's own
+ * arithmetic) of the distinct entries of seed[i][0 .. seed_cnt[i]) that lie
+ * in its visible range; with fewer than k of them nothing is pruned.  Every
+ * 64-entry block whose bound lies below T (bound: sum over heads of
+ * w_h * max(0, the largest (w_h >= 0) or smallest (w_h < 0) value q_h . k
+ * takes in the block's per-dimension box), widened by 2^-14 of its summed
+ * magnitudes against rounding) is never read.  At least k entries score
+ * T or more, so no pruned entry belongs to the Top-k: the selection, and
+ * everything after it, is the one without the flag, bit for bit. */
+#define CSA2_STEP_PRUNE 8u
 
 /* Hierarchical indexer: the indexer of a later (Reindex) layer scores only
  * the shared candidate pool an earlier indexer chose, and keeps its Top-k

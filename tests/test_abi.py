@@ -43,7 +43,7 @@ def test_workspace_bytes():
     full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
     assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
     vstride = (65537 + 2 + 63) // 64 * 64
-    assert full == reuse + 2 * 32 * vstride * 4 + 32 * 33 * 4   # candidates, keys, chunk floors
+    assert full == reuse + 2 * 32 * vstride * 4 + 2 * 32 * 33 * 4   # candidates, keys, chunk floors, prune masks
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4, 100, 8, 0, 512) == 0          # invalid h
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4096, 70000, 8, 64, 512) >= 4096 * 70000 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
@@ -120,7 +120,7 @@ def test_layer_step_mode_field_rules():
     assert lib.csa2_layer_step(L.CSA2_FULL, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG   # Full needs q_idx/w/ws
     a.nq = 0
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK              # nothing to do
-    a.flags = 8                                          # unknown flag bit
+    a.flags = 16                                         # unknown flag bit
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
     a.flags = L.STEP_DENSE_INDEX
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
@@ -153,7 +153,7 @@ def test_layer_step_per_call_knobs():
         assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
     a.flags, a.dense_cand_factor = L.STEP_ATTN_PER_HEAD_GROUP, 0
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_OK
-    a.flags = 8                                          # unknown bit
+    a.flags = 16                                         # unknown bit
     assert lib.csa2_layer_step(L.CSA2_REUSE, ctypes.byref(a), None) == L.CSA2_ERR_INVALID_ARG
 
 
@@ -344,3 +344,41 @@ def test_probe_library_exports_and_rejects():
     assert lib.csa2_probe_mfma_fp8(1, 4, 0, None, None) == invalid
     for src, nbytes, blocks in ((FAKE, 0, 1), (FAKE, 24, 1), (FAKE + 8, 32, 1), (FAKE, 32, 0), (None, 32, 1)):
         assert lib.csa2_probe_stream_read(src, nbytes, blocks, FAKE, None) == invalid
+
+
+def test_idxk_bounds_build_checks():
+    """The block-level representation's build rejects a cache without bounds,
+    misaligned bounds and block ranges outside the cache (4 pages x 64 rows =
+    4 blocks); an empty range is a no-op."""
+    lib = L.load()
+    assert lib.csa2_idxk_bounds_build(ctypes.byref(_view()), 0, 1, None) == L.CSA2_ERR_INVALID_ARG   # no bounds
+    assert lib.csa2_idxk_bounds_build(ctypes.byref(_view(idxk_bounds=FAKE + 4)), 0, 1, None) == L.CSA2_ERR_INVALID_ARG
+    v = _view(idxk_bounds=FAKE)
+    for first, n in ((-1, 1), (0, -1), (0, 5), (3, 2)):
+        assert lib.csa2_idxk_bounds_build(ctypes.byref(v), first, n, None) == L.CSA2_ERR_INVALID_ARG, (first, n)
+    assert lib.csa2_idxk_bounds_build(ctypes.byref(v), 4, 0, None) == L.CSA2_OK
+    assert lib.csa2_idxk_bounds_build(None, 0, 0, None) == L.CSA2_ERR_INVALID_ARG
+
+
+def test_layer_step_prune_field_rules():
+    """Block-level pruning: Full/Reindex only, not with the dense indexer or
+    the pool, needs the cache's bounds and a seed; seed fields without the
+    flag are rejected."""
+    lib = L.load()
+    for mode in (L.CSA2_FULL, L.CSA2_REINDEX, L.CSA2_REUSE):
+        for bounds, flags, seed, ok in ((FAKE, L.STEP_PRUNE, FAKE, True),
+                                        (None, L.STEP_PRUNE, FAKE, False),
+                                        (FAKE, L.STEP_PRUNE, None, False),
+                                        (FAKE, L.STEP_PRUNE | L.STEP_DENSE_INDEX, FAKE, False),
+                                        (FAKE, 0, FAKE, False)):
+            v = _view(idxk_bounds=bounds)
+            a = L.StepArgs()
+            a.cache = ctypes.pointer(v)
+            a.q, a.h, a.sm_scale, a.q_seq, a.q_vis, a.nq, a.k, a.max_vis = FAKE, 64, 0.04, FAKE, FAKE, 1, 64, 200
+            a.idx, a.cnt, a.out = FAKE, FAKE, FAKE
+            if mode != L.CSA2_REUSE:
+                a.q_idx, a.w, a.h_idx, a.ws, a.ws_bytes = FAKE, FAKE, 8, FAKE, 16   # workspace too small
+            a.flags, a.seed, a.seed_cnt = flags, seed, seed
+            st = lib.csa2_layer_step(mode, ctypes.byref(a), None)
+            want = L.CSA2_ERR_WORKSPACE if (ok and mode != L.CSA2_REUSE) else L.CSA2_ERR_INVALID_ARG
+            assert st == want, (mode, bounds, flags, seed, st)
