@@ -461,6 +461,57 @@ def time_hierarchical(dc, pool_k: int, steps: int):
             "entries_scored_per_query": {"exhaustive": int(spec.q_vis().max()), "pool": pool_k}}
 
 
+def time_block_pruning(spec, steps: int, scrub):
+    """Block-level pruning (CSA2_STEP_PRUNE) on the decode group: the bench's
+    own N(0,1) inputs and the same shape with clustered indexer-K rows (each
+    64-entry block near a centre of its own).  Each Full and Reindex layer's
+    seed is its selection of the previous step (same queries: the most a seed
+    can prune).  Scrubbed steps, per-layer calls, with and without the flag;
+    the selections must be identical."""
+    import dataclasses
+
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops, runner
+    from fp4_kv_cache_layer_amd import _lib as L
+    n_scan = sum(1 for m in spec.modes if m != ops.REUSE)
+    res = {"seed": "each Full / Reindex layer's own selection of the previous step (same queries)",
+           "execution": "one csa2_layer_step call per layer, a 512 MiB cache scrub before every step"}
+    for name, sp in (("bench_inputs", spec), ("clustered_inputs", dataclasses.replace(spec, clustered=True))):
+        row = {}
+        sel = {}
+        for prune in (False, True):
+            dc = runner.DeviceCase(sp, gen_device="cuda", prune=prune)
+            dc.run_layers()                                  # first step: empty seeds, nothing pruned
+            scrubbed_steps(dc.run_layers, 2, scrub)
+            tm = ops.Timing({L.KCLASS_SCAN: steps * n_scan})
+            dc.set_timing(tm)
+            ms = statistics.mean(scrubbed_steps(dc.run_layers, steps, scrub))
+            dc.set_timing(None)
+            scan = tm.durations_ms(L.KCLASS_SCAN)
+            entry = {"ms_per_step": round(ms, 5), "scan_us": _avg_us(scan),
+                     "scan_full_us": _avg_us(scan[0::n_scan]),
+                     "scan_reindex_us": _avg_us(scan[1::n_scan]) if n_scan > 1 else None}
+            if prune:
+                fr = []
+                for li, c in enumerate(dc.calls):             # one more step, masks read after each indexer layer
+                    c()
+                    if sp.modes[li] != ops.REUSE:
+                        fr.append(round(ops.pruned_block_fraction(ops.workspace_prune_masks(dc.ws, sp.nq, dc.max_vis),
+                                                                  sp.q_vis()), 4))
+                entry["pruned_block_fraction"] = fr
+                entry["scan_includes"] = "prune_mask_kernel + index_scan_kernel"
+            torch.cuda.synchronize()
+            sel[prune] = [o["idx"].cpu() for o in dc.outputs]
+            row["pruned" if prune else "plain"] = entry
+            del dc
+            torch.cuda.empty_cache()
+        row["identical_selection"] = all(torch.equal(a, b) for a, b in zip(sel[False], sel[True]))
+        row["step_speedup"] = round(row["plain"]["ms_per_step"] / row["pruned"]["ms_per_step"], 3)
+        res[name] = row
+    return res
+
+
 def cpu_sample_seqs(spec, n: int):
     """Sequences for the CPU baseline: the n whose lengths are closest to the
     workload's mean length (all equal for the uniform workloads)."""
@@ -599,6 +650,9 @@ def bench_decode(args, cfg, spec) -> int:
     out["lse_merge"] = time_lse_merge(dc.outputs[0]["out"], dc.outputs[0]["lse"])
     if args.pool_k and ops.REINDEX in spec.modes and cfg == 1:
         out["hierarchical_indexer"] = time_hierarchical(dc, args.pool_k, args.steps)
+    if args.prune and cfg == 1:
+        print("[bench] block pruning variant", file=sys.stderr, flush=True)
+        out["block_pruning"] = time_block_pruning(spec, args.steps, scrub)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_decode(spec, dc, cpu_sample_seqs(spec, 1 if cfg == 3 else 2))
@@ -720,6 +774,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pool-k", type=int, default=2048,
                     help="pool width of the hierarchical-indexer variant timed beside workload 1 (0: skip)")
+    ap.add_argument("--no-prune", dest="prune", action="store_false",
+                    help="skip the block-pruning variant timed beside workload 1")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)

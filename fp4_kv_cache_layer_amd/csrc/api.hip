@@ -134,6 +134,8 @@ IndexWs index_ws(void* ws, int32_t nq, int32_t max_vis, size_t score_off, bool d
   r.prune = prune ? reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4 +
                                                 (size_t)nq * (size_t)r.fstride * 4)
                   : nullptr;
+  r.bmax = dense ? nullptr : reinterpret_cast<uint32_t*>(p + score_off + 2 * (size_t)nq * (size_t)r.vstride * 4 +
+                                                        2 * (size_t)nq * (size_t)r.fstride * 4);
   return r;
 }
 

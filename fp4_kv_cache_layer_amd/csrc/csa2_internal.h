@@ -38,8 +38,9 @@ __device__ __forceinline__ int64_t entry_row_clamped(const int32_t* __restrict__
 //               words again.
 //   [Z, ...)    candidate indices [nq][vstride] i32, their score keys
 //               [nq][vstride] u32, then (per-query scan) the chunk key floors
-//               [nq][fstride] u32 and the pruned-block masks [nq][fstride]
-//               u32; no initial state needed.
+//               [nq][fstride] u32, the pruned-block masks [nq][fstride] u32
+//               and the block maximum keys [nq][fstride][32] u32; no initial
+//               state needed.
 struct IndexWs {
   uint32_t* cand_cnt;
   float* tau;            // dense indexer: the query's candidate threshold
@@ -49,8 +50,10 @@ struct IndexWs {
   int64_t vstride;
   int32_t vis_cap;       // max_vis of the call: visible counts are clamped to it
   // Per-query scan: the key floor below which each 2,048-entry chunk kept no
-  // candidate, [nq][fstride] u32; NULL for the dense indexer, whose
-  // candidates are exact above its threshold.
+  // candidate, [nq][fstride] u32 (a 22-bit key prefix; bit 0 set,
+  // kFloorBlockMax, when the chunk stored its block maximum keys in bmax);
+  // NULL for the dense indexer, whose candidates are exact above its
+  // threshold.
   uint32_t* floor;
   int32_t fstride;
   // Block-level pruning: per (query, chunk) the mask of its 64-entry blocks
@@ -58,8 +61,16 @@ struct IndexWs {
   // 32 * chunk + i); NULL when the call prunes nothing.  The query's
   // threshold is in tau.
   uint32_t* prune;
+  // Per-query scan: per (query, chunk) the largest score key of each of its
+  // 32 blocks of 64 entries, [nq][fstride][32] u32 (0 for a pruned block or
+  // one past the visible range), written only by chunks whose candidates
+  // crowd into one block (floor bit kFloorBlockMax), so the final select
+  // rescores only blocks that can hold entries it lacks; NULL for the dense
+  // indexer.
+  uint32_t* bmax;
 };
 
+constexpr uint32_t kFloorBlockMax = 1u;      // chunk floor bit: block maximum keys stored
 constexpr int kPruneBlockRows = 64;          // cache rows per block-level representation
 constexpr int kPruneBoundBytes = 256;        // per block: 128 maximum codes, 128 minimum codes
 

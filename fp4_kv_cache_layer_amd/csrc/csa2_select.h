@@ -5,20 +5,25 @@
 namespace csa2 {
 
 // Canonical score of one 16-entry tile for the query whose indexer heads are
-// the A operand a (head weights wv of this lane's four output rows): the
-// tile's 128-byte rows, loaded linearly (lin), reach the MFMA operand layout
-// through the wave's LDS slot; every lane returns the score of entry lane % 16
-// (a zero score as +0).  The scan and the select's repair both use it, so a
-// rescored entry has exactly the scan's bits.
-__device__ __forceinline__ float tile_score(const intx8& a, const float (&wv)[4], uint8_t* slot, const intx8& lin,
-                                            int lane) {
-  const intx8 b = fp8_tile_operand(slot, lin, lane);
+// the A operand a (head weights wv of this lane's four output rows), from the
+// tile's B operand b (lane (g, r): entry r's bytes in the load_fp8_operand
+// layout of group g): every lane returns the score of entry lane % 16 (a zero
+// score as +0).  The scan, the select's repair and the pruning threshold all
+// score through it, so an entry scored anywhere has exactly the scan's bits.
+__device__ __forceinline__ float operand_score(const intx8& a, const float (&wv)[4], const intx8& b) {
   floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
   const float part = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));
   uint32_t u32 = __float_as_uint(part);
   if ((u32 << 1) == 0) u32 = 0;                       // -0 -> +0
   return __uint_as_float(u32);
+}
+
+// The same from the tile's 128-byte rows loaded linearly (lin), which reach
+// the operand layout through the wave's LDS slot.
+__device__ __forceinline__ float tile_score(const intx8& a, const float (&wv)[4], uint8_t* slot, const intx8& lin,
+                                            int lane) {
+  return operand_score(a, wv, fp8_tile_operand(slot, lin, lane));
 }
 
 // Candidates a 2,048-entry chunk keeps: its top L entries (and the ties of

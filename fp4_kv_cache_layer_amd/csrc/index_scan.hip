@@ -36,6 +36,22 @@ namespace csa2 {
 constexpr int kScanWaves = 4;
 constexpr int kScanDepth = 6;           // tiles per wave in the load ring
 
+// DPP controls: rotate right within each row of 16 lanes
+constexpr int kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+
+// The largest of the wave's 64 values, in every lane: rotations within each
+// row of 16 lanes, then the rows' maxima across the two halves and pairs.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowRor8, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowRor4, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowRor2, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kDppRowRor1, 0xF, 0xF, false));
+  const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = max(h[0], h[1]);
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max(p[0], p[1]);
+}
+
 // Row stride of the per-query score and candidate arrays: at least two slots
 // past the longest visible range, which the indexer kernels use as write
 // sinks that are never read.
@@ -48,7 +64,8 @@ size_t zero_state_bytes(int32_t nq) {
 size_t index_score_bytes(int32_t nq, int32_t max_vis) {
   const size_t v = (size_t)index_vstride(max_vis);
   const size_t fstride = ((size_t)max_vis + kScanChunk - 1) / kScanChunk;
-  return (size_t)nq * 8 * v + (size_t)nq * fstride * 8;   // candidates, candidate keys, chunk floors, prune masks
+  // candidates, candidate keys, chunk floors, prune masks, block maximum keys
+  return (size_t)nq * 8 * v + (size_t)nq * fstride * 8 + (size_t)nq * fstride * 32 * 4;
 }
 
 __global__ void __launch_bounds__(kScanWaves * 64)
@@ -60,6 +77,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];   // then the candidate list
   __shared__ uint32_t res[2];
   __shared__ int nlist, base;                          // listed candidates, their place in the query's list
+  __shared__ int concentrated;                         // candidates crowd into one block
   // query-major: the chunks of one query are consecutive blocks.  On ragged
   // batches the grid is sized by the longest query and most blocks of the
   // short ones exit at once; in this order the working blocks of every query
@@ -184,22 +202,29 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   // The count is known from the histograms: reserve the candidates' place in
   // the query's list now, so the atomic's round trip overlaps the listing.
   int my_base = 0;                                    // (thread 0) waited on only after the listing
-  if (tid == 0) {
-    my_base = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
-    ws.floor[(int64_t)q * ws.fstride + chunk] = floor_key;
-  }
+  if (tid == 0) my_base = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)n);
   // candidates: every entry whose key reaches the floor, listed in LDS (one
   // scan and one reservation per wave)
   int32_t* const list = reinterpret_cast<int32_t*>(&stage[0][0]);
-  if (tid == 0) nlist = 0;
+  if (tid == 0) { nlist = 0; concentrated = 0; }
   lds_barrier();
   constexpr int kPer = kScanChunk / (kScanWaves * 64);
+  static_assert(kPer * kScanWaves == kScanChunk / kPruneBlockRows, "a wave's 64 entries of a round are one block");
+  // A chunk whose candidates crowd into one block (more than a quarter of L
+  // there) is one the final select may have to rescore; for it the largest
+  // key of every block is stored too, so that only blocks that can hold
+  // missing entries are rescored.
+  const int crowd = max(16, L / 4);
   uint32_t mine = 0;
+  bool crowded = false;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int i = u * kScanWaves * 64 + tid;
-    mine += (i < nloc && live(i) && score_key(sc[i]) >= floor_key) ? 1u : 0u;
+    const int i = u * kScanWaves * 64 + tid;         // block 4u + wave, entry lane
+    const bool c = i < nloc && live(i) && score_key(sc[i]) >= floor_key;
+    mine += c ? 1u : 0u;
+    crowded |= __builtin_popcountll(__builtin_amdgcn_ballot_w64(c)) > crowd;   // (uniform)
   }
+  if (crowded && floor_key != 0 && lane == 0) concentrated = 1;   // (a chunk that kept everything is never rescored)
   const uint32_t x = wave_incl_sum(mine);
   int wbase = 0;
   if (lane == 63 && x) wbase = atomicAdd(&nlist, (int)x);
@@ -212,7 +237,22 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
     }
   }
   if (tid == 0) base = my_base;
-  lds_barrier();                                     // the list and the reservation
+  lds_barrier();                                     // the list, the reservation and the crowding flag
+  const bool with_bmax = concentrated != 0;          // uniform
+  if (tid == 0) ws.floor[(int64_t)q * ws.fstride + chunk] = floor_key | (with_bmax ? kFloorBlockMax : 0u);
+  if (with_bmax) {
+    uint32_t blk_max = 0;                            // lane u: the largest key of block 4u + wave
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * kScanWaves * 64 + tid;
+      // (0 past the end and in a pruned block, none of whose entries can
+      // reach the Top-k)
+      const uint32_t m = wave_max((i < nloc && live(i)) ? score_key(sc[i]) : 0u);
+      if (lane == u) blk_max = m;
+    }
+    if (lane < kPer)
+      ws.bmax[((int64_t)q * ws.fstride + chunk) * (kScanChunk / kPruneBlockRows) + lane * kScanWaves + wave] = blk_max;
+  }
   int32_t* cand = ws.cand + (int64_t)q * ws.vstride + base;
   uint32_t* ckey = ws.ckey + (int64_t)q * ws.vstride + base;
   for (int j = tid; j < n; j += kScanWaves * 64) {

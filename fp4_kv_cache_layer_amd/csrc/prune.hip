@@ -28,14 +28,17 @@
 #include "csa2.h"
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
 namespace {
 
-constexpr int kPruneThreads = 256;
+constexpr int kPruneThreads = 1024;
 constexpr int kPruneWaves = kPruneThreads / 64;
 constexpr float kBoundSlack = 1.0f / 16384.0f;     // 2^-14 of the summed magnitudes
+constexpr int kSeedBatch = 4;                      // seed tiles per wave with their loads in flight together
+constexpr int kMaxSplit = 16;                      // workgroups per query of the mask kernel
 
 // Order key of an E4M3 code by value: negative codes below positive ones,
 // larger magnitudes further from the middle (+-0 differ only in the key).
@@ -90,26 +93,59 @@ idxk_bounds_kernel(const uint8_t* __restrict__ idx_k, uint8_t* __restrict__ boun
   bounds[blk * kPruneBoundBytes + kIndexDim + tid] = (uint8_t)lo;
 }
 
-// One workgroup per query: the threshold of its seed, then the pruned-block
-// mask of every 2,048-entry chunk of its visible range (bit i of word c: block
-// 32c + i), written to ws.prune; the threshold goes to ws.tau (the scan's
-// floor of a fully pruned chunk).  Fewer than k distinct visible seed entries:
+// The pruned-block masks, spread over nsplit workgroups per query (the
+// seed's threshold is recomputed by each, so no workgroup waits on another):
+// 16-wave workgroup (q, split) takes chunks split * 16 + wave, then every
+// 16 * nsplit further.  Each computes T from the seed, writes the mask word
+// of each of its chunks (bit i of word c: block 32c + i) to ws.prune; split
+// 0 writes T
+// to ws.tau (the scan's floor of a fully pruned chunk, the final select's
+// lower bound of the k-th key).  Fewer than k distinct visible seed entries:
 // no threshold (-inf), nothing pruned.
 __global__ void __launch_bounds__(kPruneThreads)
 prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t* __restrict__ q_idx,
                   const float* __restrict__ w, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
                   const int32_t* __restrict__ seed, const int32_t* __restrict__ seed_cnt, int h_idx, int k,
-                  IndexWs ws) {
+                  int nsplit, IndexWs ws) {
   __shared__ int32_t sd[CSA2_MAX_K];
   __shared__ __attribute__((aligned(16))) uint8_t stage[kPruneWaves][kFp8SlotBytes];
   __shared__ float tmin[kPruneWaves];
   __shared__ int nvalid_s, unsorted;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int q = blockIdx.x / nsplit, split = blockIdx.x - q * nsplit;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int V = clamp_vis(q_vis[q], ws);
+  const int nchunks = (V + kScanChunk - 1) / kScanChunk;
+  if (split > 0 && split * kPruneWaves >= nchunks) return;          // uniform: no chunk here, T written by split 0
   const int ns = min(max(seed_cnt[q], 0), k);
   const int32_t* pt_row = c.page_table + (int64_t)q_seq[q] * c.max_pages;
+
+  // the query's operands: heads as rows (h_idx <= 16)
+  intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (r < h_idx) a = load_fp8_operand(q_idx + ((int64_t)q * h_idx + r) * kIndexDim, g);
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < h_idx) ? w[(int64_t)q * h_idx + 4 * g + i] : 0.0f;
+
+  // the bounds of this wave's first chunk, in flight while the seed is read
+  // (lane (g, r): block r of each half, the 32-byte operand pieces of group g)
+  const int nblocks = (V + kPruneBlockRows - 1) / kPruneBlockRows;
+  auto bound_ptr = [&](int ch, int half) {
+    const int bc = min(ch * (kScanChunk / kPruneBlockRows) + 16 * half + r, nblocks - 1);
+    const int64_t pblk = entry_row_clamped(pt_row, bc * kPruneBlockRows, c) / kPruneBlockRows;
+    return bounds + pblk * kPruneBoundBytes;
+  };
+  const int ch0 = split * kPruneWaves + wave;
+  intx8 M0[2], m0[2];
+  if (ch0 < nchunks) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint8_t* bp = bound_ptr(ch0, half);
+      M0[half] = load_fp8_operand(bp, g);
+      m0[half] = load_fp8_operand(bp + kIndexDim, g);
+    }
+  }
 
   // the seed, sorted (a Top-K row is already ascending; others are sorted
   // here) so duplicates are neighbours
@@ -127,8 +163,8 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
         for (int i = tid; i < n2 / 2; i += kPruneThreads) {
           const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
           const bool up = (lo & size) == 0;
-          const int32_t a = sd[lo], b = sd[hi];
-          if ((a > b) == up) { sd[lo] = b; sd[hi] = a; }
+          const int32_t x = sd[lo], y = sd[hi];
+          if ((x > y) == up) { sd[lo] = y; sd[hi] = x; }
         }
         __syncthreads();
       }
@@ -141,40 +177,33 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
   }
   if (mine) atomicAdd(&nvalid_s, mine);
   __syncthreads();
-  const bool prune = nvalid_s >= k;                  // uniform
+  const bool prune = nvalid_s >= k;                  // uniform; then all ns == k entries are distinct and visible
 
-  // the query's operands: heads as rows (h_idx <= 16), q+ / q- / |q| codes
-  intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (r < h_idx) a = load_fp8_operand(q_idx + ((int64_t)q * h_idx + r) * kIndexDim, g);
-  float wv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < h_idx) ? w[(int64_t)q * h_idx + 4 * g + i] : 0.0f;
-
-  // threshold: the smallest score of the k distinct visible seed entries,
-  // each scored as the scan scores it (gathered rows, the scan's operand
-  // path and reduction)
+  // threshold: the smallest score of the seed's k entries, each scored as the
+  // scan scores it (tile_score: the scan's operand path, MFMA and
+  // reduction).  A wave takes 16-entry tiles wave, wave + 16, ..., kSeedBatch
+  // at a time with every row load issued before the first score (lane l:
+  // bytes [32 (l % 4), +32) of entry l / 4's row, as a linear 2 KB tile load
+  // would hold them).
   float T = -INFINITY;
   if (prune) {
     float m = INFINITY;
-    for (int base = 16 * wave; base < ns; base += 16 * kPruneWaves) {
-      const int i = min(base + (lane >> 2), ns - 1);
-      const int32_t t = sd[i];
-      const int64_t row = entry_row_clamped(pt_row, t, c);
-      const uint8_t* src = c.idx_k + row * kIndexDim + 32 * (lane & 3);
-      const intx4 lo = *reinterpret_cast<const intx4*>(src);
-      const intx4 hi = *reinterpret_cast<const intx4*>(src + 16);
-      const intx8 b = fp8_tile_operand(stage[wave], intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
-                                       lane);
-      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
-      float s = halves_sum(rows_pair_sum(relu_weighted(acc, wv)));   // every lane: entry base + r's score
-      uint32_t u32 = __float_as_uint(s);
-      if ((u32 << 1) == 0) u32 = 0;                  // -0 -> +0
-      s = __uint_as_float(u32);
-      const int ie = base + r;
-      const int32_t te = sd[min(ie, ns - 1)];
-      const bool valid = ie < ns && te >= 0 && te < V && (ie == 0 || sd[ie - 1] != te);
-      if (valid) m = (s == s) ? fminf(m, s) : -INFINITY;   // a NaN score: no threshold
+    const int ntiles = (ns + 15) >> 4;
+    for (int b0 = wave; b0 < ntiles; b0 += kSeedBatch * kPruneWaves) {
+      intx8 lin[kSeedBatch];
+#pragma unroll
+      for (int u = 0; u < kSeedBatch; ++u) {
+        const int i = min(16 * min(b0 + u * kPruneWaves, ntiles - 1) + (lane >> 2), ns - 1);
+        const uint8_t* src = c.idx_k + entry_row_clamped(pt_row, sd[i], c) * kIndexDim + 32 * (lane & 3);
+        const intx4 lo = *reinterpret_cast<const intx4*>(src);
+        const intx4 hi = *reinterpret_cast<const intx4*>(src + 16);
+        lin[u] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int u = 0; u < kSeedBatch; ++u) {
+        const float sv = tile_score(a, wv, stage[wave], lin[u], lane);   // every lane: entry r's score
+        if (16 * (b0 + u * kPruneWaves) + r < ns) m = (sv == sv) ? fminf(m, sv) : -INFINITY;   // NaN: no threshold
+      }
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = fminf(m, __shfl_xor(m, o));
@@ -184,10 +213,9 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
 #pragma unroll
     for (int i = 1; i < kPruneWaves; ++i) T = fminf(T, tmin[i]);
   }
-  if (tid == 0) ws.tau[q] = T;
+  if (split == 0 && tid == 0) ws.tau[q] = T;
 
-  // block bounds, 16 blocks per tile, two tiles per chunk word; wave w takes
-  // chunks w, w + 4, ...
+  // q+, q- and |q| codes of the query
   const uint32_t neg[8] = {negative4(a[0]), negative4(a[1]), negative4(a[2]), negative4(a[3]),
                            negative4(a[4]), negative4(a[5]), negative4(a[6]), negative4(a[7])};
   intx8 qpos, qneg, qabs;
@@ -197,18 +225,20 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
     qneg[i] = (int)((uint32_t)a[i] & neg[i]);
     qabs[i] = (int)((uint32_t)a[i] & 0x7F7F7F7Fu);
   }
-  const int nblocks = (V + kPruneBlockRows - 1) / kPruneBlockRows;
-  const int nchunks = (V + kScanChunk - 1) / kScanChunk;
-  for (int ch = wave; ch < nchunks; ch += kPruneWaves) {
+  // block bounds, 16 blocks per MFMA tile, two tiles per chunk word
+  for (int ch = ch0; ch < nchunks; ch += kPruneWaves * nsplit) {
     uint32_t word = 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int b = ch * (kScanChunk / kPruneBlockRows) + 16 * half + r;   // this lane's block (column r)
-      const int bc = min(b, nblocks - 1);
-      const int t0 = bc * kPruneBlockRows;
-      const int64_t pblk = entry_row_clamped(pt_row, t0, c) / kPruneBlockRows;
-      const uint8_t* bp = bounds + pblk * kPruneBoundBytes;
-      const intx8 M = load_fp8_operand(bp, g), mn = load_fp8_operand(bp + kIndexDim, g);
+      intx8 M, mn;
+      if (ch == ch0) {
+        M = M0[half];
+        mn = m0[half];
+      } else {
+        const uint8_t* bp = bound_ptr(ch, half);
+        M = load_fp8_operand(bp, g);
+        mn = load_fp8_operand(bp + kIndexDim, g);
+      }
       intx8 X;
 #pragma unroll
       for (int i = 0; i < 8; ++i) X[i] = (int)max_magnitude4((uint32_t)M[i], (uint32_t)mn[i]);
@@ -219,7 +249,7 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
       lo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qneg, M, lo, 0, 0, 0, 0, 0, 0);
       const floatx4 mag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qabs, X, z, 0, 0, 0, 0, 0, 0);
       // this lane's four heads 4g .. 4g+3 of block r
-      float s = 0.0f, sabs = 0.0f;
+      float sacc = 0.0f, sabs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float d = kBoundSlack * mag[i];
@@ -227,12 +257,13 @@ prune_mask_kernel(CacheArgs c, const uint8_t* __restrict__ bounds, const uint8_t
         // the block): the bound turns NaN and the block is kept
         const float hu = hi[i] + d, ld = lo[i] - d;
         const float up = hu < 0.0f ? 0.0f : hu, dn = ld < 0.0f ? 0.0f : ld;
-        s += wv[i] * (wv[i] >= 0.0f ? up : dn);
+        sacc += wv[i] * (wv[i] >= 0.0f ? up : dn);
         sabs += fabsf(wv[i]) * up;
       }
-      s = halves_sum(rows_pair_sum(s));
+      sacc = halves_sum(rows_pair_sum(sacc));
       sabs = halves_sum(rows_pair_sum(sabs));
-      const float ub = s + kBoundSlack * sabs + 1e-30f;
+      const float ub = sacc + kBoundSlack * sabs + 1e-30f;
+      const int b = ch * (kScanChunk / kPruneBlockRows) + 16 * half + r;
       const bool pruned = prune && b < nblocks && ub < T;
       const uint64_t bal = __builtin_amdgcn_ballot_w64(pruned && g == 0);
       word |= (uint32_t)(bal & 0xFFFFu) << (16 * half);
@@ -258,8 +289,12 @@ hipError_t launch_prune_mask(const CacheArgs& c, const uint8_t* bounds, const ui
     record_empty(ev, s);
     return hipSuccess;
   }
-  launch(prune_mask_kernel, dim3((unsigned)nq), dim3(kPruneThreads), s, ev, c, bounds, q_idx, w, q_seq, q_vis, seed,
-         seed_cnt, h_idx, k, ws);
+  // workgroups per query: 16 chunks each, at most kMaxSplit (longer
+  // contexts give each wave several chunks)
+  const int per = (ws.fstride + kPruneWaves - 1) / kPruneWaves;
+  const int nsplit = per < 1 ? 1 : per > kMaxSplit ? kMaxSplit : per;
+  launch(prune_mask_kernel, dim3((unsigned)(nq * nsplit)), dim3(kPruneThreads), s, ev, c, bounds, q_idx, w, q_seq,
+         q_vis, seed, seed_cnt, h_idx, k, nsplit, ws);
   return hipGetLastError();
 }
 

@@ -36,7 +36,11 @@ namespace csa2 {
 namespace {
 
 constexpr int kSelCap = 2048;
-constexpr int kRepairWaves = 8;             // waves of the final workgroup that rescore a chunk
+constexpr int kRepairWaves = kSelectThreads / 64;                  // every wave rescores
+constexpr int kRepairBatch = 8;                                     // tiles per wave with their loads in flight together
+constexpr int kBlocksPerChunk = kScanChunk / kPruneBlockRows;       // 32
+constexpr int kTilesPerBlock = kPruneBlockRows / 16;                // 4
+constexpr int kPairCap = kTieCap * 2;                               // (chunk, block) pairs listed per pass
 
 // Appends value for every lane where flag holds, one atomic per wave.
 template <typename T>
@@ -69,9 +73,9 @@ struct SelShared {
   int32_t selcnt;
   int32_t tiecnt;
   int32_t repair;
+  int32_t ncand;                                // candidates, with those the repair appends
+  int32_t npairs;                               // (chunk, block) pairs listed for the repair
 };
-static_assert(sizeof(uint64_t) * kTieCap >= (size_t)kRepairWaves * kFp8SlotBytes,
-              "the parking buffer holds the repairing waves' operand slots");
 
 }  // namespace
 
@@ -97,7 +101,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
   lds_barrier();
   for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
-  if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; S.repair = 0; }
+  if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; S.repair = 0; S.ncand = nc; }
   lds_barrier();
 
   uint32_t need = (uint32_t)k;
@@ -125,69 +129,121 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     // arithmetic as the scan) and add its entries in [pfloor, floor); the k-th
     // key can only rise, so afterwards every entry at or above it is a
     // candidate (rare: it takes more of the Top-k in one chunk than it keeps).
-    const uint32_t pfloor = ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
+    // With block-level pruning, tau holds the query's threshold T, and at
+    // least k entries score T or more: the k-th key is at least T's, so
+    // chunks that left out only entries below T (every fully pruned chunk)
+    // need no rescoring.
+    uint32_t pfloor = ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
+    if (ws.prune != nullptr) pfloor = max(pfloor, score_key(ws.tau[q]) & ~((1u << (32 - 2 * kHistBits)) - 1u));
     const int nch = (V + kScanChunk - 1) / kScanChunk;
     const uint32_t* fl = ws.floor + (int64_t)q * ws.fstride;
+    // the chunks to rescore, listed in the selection buffer (free until the
+    // candidates are partitioned)
     for (int cc = tid; cc < nch; cc += kSelectThreads)
-      if (fl[cc] > pfloor) atomicOr(&S.repair, 1);
-    lds_barrier();
-    if (S.repair) {
-      const int lane_r = tid & 63, wave_r = tid >> 6;
-      const int g = lane_r >> 4, r = lane_r & 15;
-      intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-      float wv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (wave_r < kRepairWaves) {
-        if (r < sa.h_idx) a = load_fp8_operand(sa.q_idx + ((int64_t)q * sa.h_idx + r) * kIndexDim, g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          wv[i] = (4 * g + i < sa.h_idx) ? sa.w[(int64_t)q * sa.h_idx + 4 * g + i] : 0.0f;
+      if ((fl[cc] & ~kFloorBlockMax) > pfloor) {
+        const int i = atomicAdd(&S.repair, 1);
+        if (i < kSelCap) S.sel[i] = cc;
       }
-      // the parking buffer is free until the candidates are read: it holds
-      // the repairing waves' operand slots
-      uint8_t* const slot = reinterpret_cast<uint8_t*>(S.tie) + wave_r * kFp8SlotBytes;
+    lds_barrier();
+    const int nflag = S.repair;
+    if (nflag) {
+      // Only blocks of flagged chunks whose largest key reaches pfloor can
+      // hold what the chunks left out (a chunk without stored block maxima
+      // offers all its blocks).  They are listed as (chunk, block)
+      // pairs in the parking buffer (free until the candidates are
+      // partitioned), kPairCap at a time, and their 16-entry tiles rescored
+      // by all waves, kRepairBatch per wave at a time with all their row
+      // loads in flight before the first score (lane (g, r) loads entry r's
+      // operand bytes directly).  A wave scores a batch, then reserves the
+      // place of all its additions at once.
+      const int g = lane >> 4, r = lane & 15;
+      const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+      intx8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+      float wv[4];
+      if (r < sa.h_idx) a = load_fp8_operand(sa.q_idx + ((int64_t)q * sa.h_idx + r) * kIndexDim, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < sa.h_idx) ? sa.w[(int64_t)q * sa.h_idx + 4 * g + i] : 0.0f;
       const int32_t* pt_row = sa.c.page_table + (int64_t)sa.q_seq[q] * sa.c.max_pages;
       int32_t* cand_w = ws.cand + (int64_t)q * ws.vstride;
       uint32_t* ckey_w = ws.ckey + (int64_t)q * ws.vstride;
-      for (int cc = 0; cc < nch; ++cc) {
-        const uint32_t fc = fl[cc];                   // uniform
-        if (fc <= pfloor || wave_r >= kRepairWaves) continue;
-        const int c0 = cc * kScanChunk, c1 = min(V, c0 + kScanChunk);
-        const int ntl = (c1 - c0 + 15) >> 4;
-        for (int j = wave_r; j < ntl; j += kRepairWaves) {
-          const int ts = c0 + 16 * j;                 // tiles never straddle pages
-          const int page = clamp_page(pt_row[ts >> sa.c.lg_page], sa.c);
-          const intx8 lin = load_fp8_tile_linear(
-              sa.c.idx_k + (((int64_t)page << sa.c.lg_page) + (ts & ((1 << sa.c.lg_page) - 1))) * kIndexDim, lane_r);
-          const float sv = tile_score(a, wv, slot, lin, lane_r);
-          const uint32_t key = score_key(sv);
-          const int t = ts + r;
+      const uint32_t* bm = ws.bmax + (int64_t)q * ws.fstride * kBlocksPerChunk;
+      uint32_t* const pairs = reinterpret_cast<uint32_t*>(S.tie);
+      // chunk slots: the flagged list, or every chunk were it to overflow.
+      // (Fewer than ceil(k / L) chunks are ever flagged, L >= 16 the scan's
+      // local rank: ceil(k / L) flagged chunks would hold k candidates above
+      // the k-th key.  So at most 127 for k <= 2,048, one pass of pairs.)
+      const bool listed = nflag <= kSelCap;
+      const int nslots = listed ? nflag : nch;
+      for (int s0 = 0; s0 < nslots; s0 += kPairCap / kBlocksPerChunk) {
+        const int s1 = min(nslots, s0 + kPairCap / kBlocksPerChunk);
+        if (tid == 0) S.npairs = 0;
+        lds_barrier();
+        for (int x = tid; x < (s1 - s0) * kBlocksPerChunk; x += kSelectThreads) {
+          const int slot = s0 + x / kBlocksPerChunk, bl = x % kBlocksPerChunk;
+          const int cc = listed ? S.sel[slot] : slot;
+          const uint32_t f = fl[cc];
+          // every block of a chunk that stored no block maxima
+          if ((f & ~kFloorBlockMax) > pfloor && bl * kPruneBlockRows < V - cc * kScanChunk &&
+              (!(f & kFloorBlockMax) || bm[(int64_t)cc * kBlocksPerChunk + bl] >= pfloor)) {
+            const int i = atomicAdd(&S.npairs, 1);
+            pairs[i] = (uint32_t)(cc * kBlocksPerChunk + bl);
+          }
+        }
+        lds_barrier();
+        const int ntl = S.npairs * kTilesPerBlock;
+        for (int f0 = wave_s; f0 < ntl; f0 += kRepairBatch * kRepairWaves) {   // uniform
+          intx8 b[kRepairBatch];
+          int tstart[kRepairBatch];
+#pragma unroll
+          for (int u = 0; u < kRepairBatch; ++u) {
+            const int f = min(f0 + u * kRepairWaves, ntl - 1);
+            const uint32_t pr = pairs[f / kTilesPerBlock];
+            tstart[u] = (int)pr * kPruneBlockRows + 16 * (f % kTilesPerBlock);
+            const int c1 = min(V, (int)(pr / kBlocksPerChunk) * kScanChunk + kScanChunk);
+            const int t = min(tstart[u] + r, c1 - 1);
+            b[u] = load_fp8_operand(sa.c.idx_k + entry_row_clamped(pt_row, t, sa.c) * kIndexDim, g);
+          }
           // entries below the chunk's floor that reach the k-th candidate's bin
-          const bool add = g == 0 && t < c1 && key >= pfloor && key < fc;
-          const uint64_t m = __builtin_amdgcn_ballot_w64(add);
-          if (m) {
-            const int leader = __builtin_ctzll(m);
+          uint32_t key[kRepairBatch];
+          uint64_t mk[kRepairBatch];
+          int tot = 0;
+#pragma unroll
+          for (int u = 0; u < kRepairBatch; ++u) {
+            key[u] = score_key(operand_score(a, wv, b[u]));
+            const int cc = tstart[u] / kScanChunk;
+            const int t = tstart[u] + r;
+            const bool add = g == 0 && f0 + u * kRepairWaves < ntl && t < min(V, cc * kScanChunk + kScanChunk) &&
+                             key[u] >= pfloor && key[u] < (fl[cc] & ~kFloorBlockMax);
+            mk[u] = __builtin_amdgcn_ballot_w64(add);
+            tot += __builtin_popcountll(mk[u]);
+          }
+          if (tot) {                                  // uniform
             int b0 = 0;
-            if (lane_r == leader) b0 = (int)atomicAdd(&ws.cand_cnt[q], (uint32_t)__builtin_popcountll(m));
-            b0 = __builtin_amdgcn_readlane(b0, leader);
-            const int pos = b0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (add) {
-              cand_w[pos] = t;
-              ckey_w[pos] = key;
-              atomicAdd(&S.h[key >> (32 - kHistBits)], 1u);
+            // this workgroup alone appends to the query's list now: an LDS count
+            if (lane == 0) b0 = atomicAdd(&S.ncand, tot);
+            b0 = __builtin_amdgcn_readlane(b0, 0);
+#pragma unroll
+            for (int u = 0; u < kRepairBatch; ++u) {
+              if ((mk[u] >> lane) & 1u) {
+                const int pos = b0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk[u] >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mk[u], 0));
+                cand_w[pos] = tstart[u] + r;
+                ckey_w[pos] = key[u];
+                atomicAdd(&S.h[key[u] >> (32 - kHistBits)], 1u);
+              }
+              b0 += __builtin_popcountll(mk[u]);
             }
           }
         }
+        lds_barrier();                                // the pair list is rebuilt by the next pass
       }
       __syncthreads();                                // new candidates (global) and histogram counts complete
       find_digit(S.h, kHistBins, need, S.res);
       dstar = (int)S.res[0];
     }
   }
-  // the count as the repair left it (an atomic load: other waves added to it)
-  const int ncand = ws.floor != nullptr
-                        ? (int)__hip_atomic_load(&ws.cand_cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : nc;
+  // the count as the repair left it
+  const int ncand = S.ncand;
   uint64_t P = (uint64_t)dstar;
   need -= S.res[1];
   uint32_t cnt_eq = S.h[dstar];

@@ -112,6 +112,30 @@ def workspace_state_bytes(nq: int) -> int:
     return (nq * 12 + 255) // 256 * 256
 
 
+def workspace_prune_masks(ws: torch.Tensor, nq: int, max_vis: int) -> torch.Tensor:
+    """The CSA2_STEP_PRUNE block masks of the last pruned call on ws, a
+    [nq][ceil(max_vis / 2048)] int32 view (bit i of word c: block 32c + i of
+    the query's visible range was pruned; words past a query's visible range
+    are not written).  Layout as csa2_workspace_bytes documents it: state
+    head, candidates, their keys, chunk floors, masks, block maximum keys."""
+    vstride = (max_vis + 2 + 63) // 64 * 64
+    fstride = (max_vis + 2047) // 2048
+    off = workspace_state_bytes(nq) + 2 * nq * vstride * 4 + nq * fstride * 4
+    return ws[off: off + nq * fstride * 4].view(torch.int32).view(nq, fstride)
+
+
+def pruned_block_fraction(masks: torch.Tensor, q_vis) -> float:
+    """Share of the visible 64-entry blocks a mask view marks, over all queries."""
+    import numpy as np
+    m = masks.cpu().numpy().view(np.uint8).reshape(masks.shape[0], -1)
+    pruned = total = 0
+    for i, v in enumerate(q_vis):
+        nb = (int(v) + 63) // 64
+        pruned += int(np.unpackbits(m[i], bitorder="little")[:nb].sum())
+        total += nb
+    return pruned / max(total, 1)
+
+
 def csa2_workspace_init(ws: torch.Tensor, stream=None) -> None:
     L.check("csa2_workspace_init", L.load().csa2_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 

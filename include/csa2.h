@@ -145,10 +145,11 @@ csa2_status csa2_append_quant_fp4(const csa2_cache_view* c, const int32_t* slots
  * thresholds, its full-rescore counters), padded to 256 bytes; then (Full
  * and Reindex) per-query candidate indices [nq][round_up(max_vis + 2, 64)]
  * i32, their score keys of the same shape, the per-query scan's chunk key
- * floors [nq][ceil(max_vis / 2048)] u32 and the CSA2_STEP_PRUNE block masks
- * of the same shape (bit i of word c: block 32c + i of the query's visible
- * range holds no Top-k entry), that region being at least nq * 8 KB so a
- * CSA2_STEP_POOL layer can score its pool there.
+ * floors [nq][ceil(max_vis / 2048)] u32, the CSA2_STEP_PRUNE block masks of
+ * the same shape (bit i of word c: block 32c + i of the query's visible
+ * range holds no Top-k entry) and the scan's largest score key of every
+ * 64-entry block [nq][ceil(max_vis / 2048)][32] u32, that region being at
+ * least nq * 8 KB so a CSA2_STEP_POOL layer can score its pool there.
  * csa2_index_topk accepts a workspace sized by this call for the same shape;
  * attention needs none.  Only the first round_up(nq * 12, 256) bytes carry
  * state: every call leaves them zeroed for the next one, so zero the whole

@@ -43,10 +43,33 @@ def test_workspace_bytes():
     full = lib.csa2_workspace_bytes(L.CSA2_FULL, 32, 65537, 8, 64, 512)
     assert full == lib.csa2_workspace_bytes(L.CSA2_REINDEX, 32, 65537, 8, 64, 512)
     vstride = (65537 + 2 + 63) // 64 * 64
-    assert full == reuse + 2 * 32 * vstride * 4 + 2 * 32 * 33 * 4   # candidates, keys, chunk floors, prune masks
+    # candidates, keys, chunk floors, prune masks, block maximum keys
+    assert full == reuse + 2 * 32 * vstride * 4 + 2 * 32 * 33 * 4 + 32 * 33 * 32 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4, 100, 8, 0, 512) == 0          # invalid h
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 4096, 70000, 8, 64, 512) >= 4096 * 70000 * 4
     assert lib.csa2_workspace_bytes(L.CSA2_FULL, 0, 100, 8, 64, 512) == 0
+
+
+def test_prune_mask_view_ends_the_workspace():
+    """ops.workspace_prune_masks reads the masks where the library puts them:
+    just before the last nq * ceil(max_vis / 2048) * 32 words (the block
+    maximum keys) of a Full workspace whose candidate region is larger than
+    the pool region."""
+    import numpy as np
+    import torch
+
+    from fp4_kv_cache_layer_amd import ops
+    for nq, max_vis in ((32, 65537), (3, 70000), (17, 2049)):
+        ws = torch.zeros(ops.csa2_workspace_bytes(ops.FULL, nq, max_vis, 8, 64, 512), dtype=torch.uint8)
+        m = ops.workspace_prune_masks(ws, nq, max_vis)
+        assert m.shape == (nq, (max_vis + 2047) // 2048)
+        assert m.data_ptr() + m.numel() * 4 + m.numel() * 32 * 4 == ws.data_ptr() + ws.numel()
+    # the block count of a mask view: bit i of word c is block 32c + i
+    m = torch.zeros((2, 3), dtype=torch.int32)
+    m[0, 0] = 0b101
+    m[0, 2] = 1                               # block 64, past query 0's 40 blocks
+    m[1, 1] = -1                              # blocks 32..63 of query 1
+    assert ops.pruned_block_fraction(m, np.array([40 * 64, 96 * 64])) == (2 + 32) / (40 + 96)
 
 
 def _topk(lib, view, fn="csa2_index_topk", **kw):

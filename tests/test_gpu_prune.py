@@ -21,22 +21,10 @@ def _ops():
 
 
 def _mask_fraction(dc, ws) -> float:
-    """Share of the visible 64-entry blocks that the prune pass of the last
-    call on ws marked (the masks follow the state head, the candidates, their
-    keys and the chunk floors)."""
+    """Share of the visible 64-entry blocks the prune pass of the last call on
+    ws marked."""
     ops, _ = _ops()
-    nq, vis = dc.spec.nq, dc.spec.q_vis()
-    vstride = (dc.max_vis + 2 + 63) // 64 * 64
-    fstride = (dc.max_vis + 2047) // 2048
-    off = ops.workspace_state_bytes(nq) + 2 * nq * vstride * 4 + nq * fstride * 4
-    masks = ws[off: off + nq * fstride * 4].cpu().numpy()
-    pruned = total = 0
-    for i in range(nq):
-        nb = (int(vis[i]) + 63) // 64
-        bits = np.unpackbits(masks[i * fstride * 4: (i + 1) * fstride * 4], bitorder="little")[:nb]
-        pruned += int(bits.sum())
-        total += nb
-    return pruned / max(total, 1)
+    return ops.pruned_block_fraction(ops.workspace_prune_masks(ws, dc.spec.nq, dc.max_vis), dc.spec.q_vis())
 
 
 def _run_layers(dc):
