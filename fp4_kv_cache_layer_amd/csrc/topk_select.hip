@@ -79,6 +79,10 @@ struct SelShared {
 
 }  // namespace
 
+// kFloors: the per-query scan's candidates (ws.floor set; chunks may need
+// rescoring), else the dense indexer's.  The dense form carries none of the
+// rescoring code, so it keeps twice the occupancy for its many queries.
+template <bool kFloors>
 __global__ void __launch_bounds__(kSelectThreads)
 topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, int k,
                   int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt) {
@@ -96,7 +100,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   }
   // the candidate count: the dense indexer's full rescore appended after its
   // first pass's candidates
-  const int nc = (int)ws.cand_cnt[q] + (ws.floor != nullptr ? 0 : (int)ws.cnt2[q]);
+  const int nc = (int)ws.cand_cnt[q] + (kFloors ? 0 : (int)ws.cnt2[q]);
   // the histogram of the candidates' keys
   for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
   lds_barrier();
@@ -109,7 +113,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   find_digit(S.h, kHistBins, need, S.res);
   int dstar = (int)S.res[0];
 
-  if (ws.floor != nullptr) {
+  if constexpr (kFloors) {
     // The k-th candidate key to 22 bits: a second digit over the candidates
     // in its 11-bit bin (counted into the parking buffer, free until later).
     const int ncand0 = ws.cand_cnt[q];
@@ -399,7 +403,10 @@ hipError_t launch_topk_final(const IndexWs& ws, const ScanArgs& sa, const int32_
     record_empty(ev, s);
     return hipSuccess;
   }
-  launch(topk_final_kernel, dim3(nq), dim3(kSelectThreads), s, ev, ws, sa, q_vis, k, out_idx, out_cnt);
+  if (ws.floor != nullptr)
+    launch(topk_final_kernel<true>, dim3(nq), dim3(kSelectThreads), s, ev, ws, sa, q_vis, k, out_idx, out_cnt);
+  else
+    launch(topk_final_kernel<false>, dim3(nq), dim3(kSelectThreads), s, ev, ws, sa, q_vis, k, out_idx, out_cnt);
   return hipGetLastError();
 }
 
