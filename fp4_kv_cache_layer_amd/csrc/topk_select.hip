@@ -110,8 +110,16 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
 
   uint32_t need = (uint32_t)k;
   int nbits = kHistBits;
-  find_digit(S.h, kHistBins, need, S.res);
-  int dstar = (int)S.res[0];
+  // Block-level pruning can leave a query with fewer than k candidates
+  // (chunks keep only their top L, and pruned chunks none): then there is no
+  // k-th candidate key yet, and the repair below, from the threshold alone,
+  // brings in every entry that scores T or more, at least k of them.
+  const bool short_list = kFloors && nc < k;
+  int dstar = 0;
+  if (!short_list) {
+    find_digit(S.h, kHistBins, need, S.res);
+    dstar = (int)S.res[0];
+  }
 
   if constexpr (kFloors) {
     // The k-th candidate key to 22 bits: a second digit over the candidates
@@ -119,14 +127,16 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     const int ncand0 = ws.cand_cnt[q];
     const uint32_t* ckey_r = ws.ckey + (int64_t)q * ws.vstride;
     uint32_t* const h2 = reinterpret_cast<uint32_t*>(S.tie);
-    for (int i = tid; i < kHistBins; i += kSelectThreads) h2[i] = 0;
-    lds_barrier();
-    for (int i = tid; i < ncand0; i += kSelectThreads) {
-      const uint32_t key = ckey_r[i];
-      if ((int)(key >> (32 - kHistBits)) == dstar) atomicAdd(&h2[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+    if (!short_list) {
+      for (int i = tid; i < kHistBins; i += kSelectThreads) h2[i] = 0;
+      lds_barrier();
+      for (int i = tid; i < ncand0; i += kSelectThreads) {
+        const uint32_t key = ckey_r[i];
+        if ((int)(key >> (32 - kHistBits)) == dstar) atomicAdd(&h2[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+      }
+      lds_barrier();
+      find_digit(h2, kHistBins, need - S.res[1], S.res2);
     }
-    lds_barrier();
-    find_digit(h2, kHistBins, need - S.res[1], S.res2);
     // Every entry a chunk left out has a key below the chunk's floor.  A chunk
     // whose floor lies above the k-th candidate key's 22-bit prefix pfloor may
     // have left out entries at or above the k-th key: rescore it (same
@@ -137,7 +147,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     // least k entries score T or more: the k-th key is at least T's, so
     // chunks that left out only entries below T (every fully pruned chunk)
     // need no rescoring.
-    uint32_t pfloor = ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
+    uint32_t pfloor = short_list ? 0u : ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
     if (ws.prune != nullptr) pfloor = max(pfloor, score_key(ws.tau[q]) & ~((1u << (32 - 2 * kHistBits)) - 1u));
     const int nch = (V + kScanChunk - 1) / kScanChunk;
     const uint32_t* fl = ws.floor + (int64_t)q * ws.fstride;
@@ -241,6 +251,8 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
         }
         lds_barrier();                                // the pair list is rebuilt by the next pass
       }
+    }
+    if (nflag || short_list) {
       __syncthreads();                                // new candidates (global) and histogram counts complete
       find_digit(S.h, kHistBins, need, S.res);
       dstar = (int)S.res[0];
@@ -254,7 +266,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   lds_barrier();
 
   // heavily tied inputs: refine the prefix over the candidate list until its class fits in LDS
-  while (cnt_eq > (uint32_t)kTieCap) {
+  while (cnt_eq > (uint32_t)kTieCap && nbits < 64) {
     const int d = min(kHistBits, 64 - nbits);
     for (int i = tid; i < (1 << d); i += kSelectThreads) S.h[i] = 0;
     lds_barrier();

@@ -150,3 +150,49 @@ def test_other_seeds_keep_the_selection(kind):
     for li, (a, b) in enumerate(zip(got, plain)):
         for key in ("idx", "cnt", "out", "lse"):
             assert np.array_equal(a[key], b[key]), (kind, li, key)
+
+
+@pytest.mark.parametrize("k", [128, 512])
+def test_pruning_when_one_chunk_holds_the_topk(k):
+    """Clustered integer rows, with indexer-K rows 2,048..4,095 of sequence 0
+    pointing along its query's weighted heads: that chunk holds all of the
+    Full layer's Top-k, keeps only its local top entries, and pruning removes
+    nearly every other block, so the select starts with fewer than k
+    candidates and must take the rest from the threshold alone.  Pruned,
+    unpruned and oracle selections agree bit for bit."""
+    ops, runner = _ops()
+    spec = W.small_case("prune_hot", 91 + k, [20000, 7000], n_new=1, h_idx=8, h=16, k=k,
+                        modes=(W.FULL, W.REINDEX), integer_indexer=True, clustered=True, page_size=128)
+    qi, w, _ = W.layer_queries(spec, 0, "cpu")
+    qv = qi[0].view(torch.float8_e4m3fn).float().numpy()
+    u = (w[0].numpy()[:, None] * qv).sum(0)
+    rng = np.random.default_rng(k)
+    hot = (np.where(u >= 0, 1.0, -1.0)[None, :] * rng.integers(4, 9, (2048, 128))).astype(np.float32)
+    hot_bits = torch.from_numpy((hot.view(np.uint32) >> 16).astype(np.uint16).view(np.int16))
+    say(f"[prune hot chunk] k={k}")
+    pt = W.page_table(spec)
+    slots = torch.from_numpy(W.slots_for(spec, pt, 0, 2048, 4096)).cuda()
+    kv_bits = W.kv_rows(spec, 0, "cpu")[2048:4096].contiguous().cuda()
+    results = {}
+    for prune in (False, True):
+        dc = runner.DeviceCase(spec, gen_device="cpu", prune=prune, poison_ws=True)
+        ops.csa2_append_quant_fp4(dc.cache, slots, kv_bits, hot_bits.cuda())
+        if prune:
+            dc.cache.build_bounds()
+            _run_layers(dc)                                   # no seed yet
+        fr = _run_layers(dc)
+        results[prune] = dc.results_host()
+        if prune:
+            say(f"  pruned blocks {fr}")
+            assert fr[0] > 0.5, fr
+    case = CB.build(spec)
+    case.ik_src[0] = case.ik_src[0].copy()
+    case.ik_src[0][2048:4096] = hot_bits.numpy().view(np.uint16)
+    ref = CB.run_group(case)
+    assert int(((ref[0]["idx"][0] >= 2048) & (ref[0]["idx"][0] < 4096)).sum()) == k   # all in the hot chunk
+    for li in range(2):
+        for key in ("idx", "cnt"):
+            assert np.array_equal(results[True][li][key], ref[li][key]), (li, key)
+            assert np.array_equal(results[False][li][key], ref[li][key]), (li, key)
+        for key in ("out", "lse"):
+            assert np.array_equal(results[True][li][key], results[False][li][key]), (li, key)
