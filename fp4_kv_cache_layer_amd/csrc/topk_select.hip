@@ -116,6 +116,10 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   // brings in every entry that scores T or more, at least k of them.
   const bool short_list = kFloors && nc < k;
   int dstar = 0;
+  // with no repair, the candidates' k-th key is known to 22 bits (its class
+  // eq22 candidates wide, above22 above it) and the parking starts there
+  bool digits22 = false;
+  uint32_t eq22 = 0;
   if (!short_list) {
     find_digit(S.h, kHistBins, need, S.res);
     dstar = (int)S.res[0];
@@ -136,6 +140,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
       }
       lds_barrier();
       find_digit(h2, kHistBins, need - S.res[1], S.res2);
+      eq22 = h2[S.res2[0]];
     }
     // Every entry a chunk left out has a key below the chunk's floor.  A chunk
     // whose floor lies above the k-th candidate key's 22-bit prefix pfloor may
@@ -160,6 +165,7 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
       }
     lds_barrier();
     const int nflag = S.repair;
+    digits22 = !short_list && nflag == 0;
     if (nflag) {
       // Only blocks of flagged chunks whose largest key reaches pfloor can
       // hold what the chunks left out (a chunk without stored block maxima
@@ -263,6 +269,12 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   uint64_t P = (uint64_t)dstar;
   need -= S.res[1];
   uint32_t cnt_eq = S.h[dstar];
+  if (digits22) {
+    P = (P << kHistBits) | (uint64_t)S.res2[0];
+    need -= S.res2[1];
+    cnt_eq = eq22;
+    nbits = 2 * kHistBits;
+  }
   lds_barrier();
 
   // heavily tied inputs: refine the prefix over the candidate list until its class fits in LDS
