@@ -36,6 +36,8 @@ namespace csa2 {
 namespace {
 
 constexpr int kSelCap = 2048;
+constexpr int kRegList = 4;                 // candidates per thread held in registers
+constexpr int kListCap = kRegList * kSelectThreads;
 constexpr int kRepairWaves = kSelectThreads / 64;                  // every wave rescores
 constexpr int kRepairBatch = 8;                                     // tiles per wave with their loads in flight together
 constexpr int kBlocksPerChunk = kScanChunk / kPruneBlockRows;       // 32
@@ -101,10 +103,32 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   // the candidate count: the dense indexer's full rescore appended after its
   // first pass's candidates
   const int nc = (int)ws.cand_cnt[q] + (kFloors ? 0 : (int)ws.cnt2[q]);
-  // the histogram of the candidates' keys
+  // per-query scan: this thread's chunk floor, read now (used by the repair test)
+  const int nch = (V + kScanChunk - 1) / kScanChunk;
+  const uint32_t* fl = kFloors ? ws.floor + (int64_t)q * ws.fstride : nullptr;
+  const uint32_t fl_mine = (kFloors && tid < nch) ? fl[tid] : 0u;
+  // the histogram of the candidates' keys; a per-query scan's list of at
+  // most kListCap candidates stays in registers (thread tid: entries tid +
+  // 1,024 u), where the second digit and the partition read it, the indices'
+  // loads completing while the digits are searched
+  const bool in_regs = kFloors && nc <= kListCap;
+  uint32_t rkey[kRegList];
+  int32_t rcand[kRegList];
   for (int i = tid; i < kHistBins; i += kSelectThreads) S.h[i] = 0;
   lds_barrier();
-  for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRegList; ++u) rkey[u] = tid + u * kSelectThreads < nc ? ckey[tid + u * kSelectThreads] : 0u;
+#pragma unroll
+    for (int u = 0; u < kRegList; ++u)
+      if (tid + u * kSelectThreads < nc) atomicAdd(&S.h[rkey[u] >> (32 - kHistBits)], 1u);
+    // the indices are requested only now, so the histogram never waits for them
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kRegList; ++u) rcand[u] = tid + u * kSelectThreads < nc ? cand[tid + u * kSelectThreads] : 0;
+  } else {
+    for (int i = tid; i < nc; i += kSelectThreads) atomicAdd(&S.h[ckey[i] >> (32 - kHistBits)], 1u);
+  }
   if (tid == 0) { S.selcnt = 0; S.tiecnt = 0; S.repair = 0; S.ncand = nc; }
   lds_barrier();
 
@@ -134,9 +158,15 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     if (!short_list) {
       for (int i = tid; i < kHistBins; i += kSelectThreads) h2[i] = 0;
       lds_barrier();
-      for (int i = tid; i < ncand0; i += kSelectThreads) {
-        const uint32_t key = ckey_r[i];
+      auto count2 = [&](uint32_t key) {
         if ((int)(key >> (32 - kHistBits)) == dstar) atomicAdd(&h2[(key >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+      };
+      if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < kRegList; ++u)
+          if (tid + u * kSelectThreads < ncand0) count2(rkey[u]);
+      } else {
+        for (int i = tid; i < ncand0; i += kSelectThreads) count2(ckey_r[i]);
       }
       lds_barrier();
       find_digit(h2, kHistBins, need - S.res[1], S.res2);
@@ -154,12 +184,10 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
     // need no rescoring.
     uint32_t pfloor = short_list ? 0u : ((uint32_t)dstar << (32 - kHistBits)) | (S.res2[0] << (32 - 2 * kHistBits));
     if (ws.prune != nullptr) pfloor = max(pfloor, score_key(ws.tau[q]) & ~((1u << (32 - 2 * kHistBits)) - 1u));
-    const int nch = (V + kScanChunk - 1) / kScanChunk;
-    const uint32_t* fl = ws.floor + (int64_t)q * ws.fstride;
     // the chunks to rescore, listed in the selection buffer (free until the
     // candidates are partitioned)
     for (int cc = tid; cc < nch; cc += kSelectThreads)
-      if ((fl[cc] & ~kFloorBlockMax) > pfloor) {
+      if (((cc == tid ? fl_mine : fl[cc]) & ~kFloorBlockMax) > pfloor) {
         const int i = atomicAdd(&S.repair, 1);
         if (i < kSelCap) S.sel[i] = cc;
       }
@@ -301,6 +329,16 @@ topk_final_kernel(IndexWs ws, ScanArgs sa, const int32_t* __restrict__ q_vis, in
   // Batches of kCandBatch per thread: all their indices and keys are in
   // flight together.
   constexpr int kCandBatch = 4;
+  if (in_regs && ncand == nc) {                      // the list in registers, nothing appended
+#pragma unroll
+    for (int u = 0; u < kRegList; ++u) {
+      const bool valid = tid + u * kSelectThreads < nc;
+      const uint64_t C = ((uint64_t)rkey[u] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)rcand[u]);
+      const uint64_t pre = C >> (64 - nbits);
+      wave_append<int32_t>(valid && pre > P, rcand[u], &S.selcnt, S.sel, kSelCap);
+      wave_append<uint64_t>(valid && pre == P, C, &S.tiecnt, S.tie, kTieCap);
+    }
+  } else
   for (int i0 = 0; i0 < ncand; i0 += kCandBatch * kSelectThreads) {
     int t[kCandBatch];
     uint32_t kv[kCandBatch];
