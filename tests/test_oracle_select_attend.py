@@ -162,3 +162,36 @@ def test_attention_output_within_row_hull():
     o, lse = O.attend(cache, 0, q_bits, sel, 20, 1 / np.sqrt(512))
     x = O.dequantize_kv_rows(cache.kv_rows(0, sel))
     assert (o >= x.min(0) - 1e-12).all() and (o <= x.max(0) + 1e-12).all()
+
+
+def test_sparse_attention_over_a_selection_is_dense_attention_over_its_rows():
+    """Several sequences in shuffled pages, selections shorter than k in
+    arbitrary order with -1 padding: every query's output equals torch's
+    dense attention over exactly its selected rows, located here through the
+    workload's own slot arithmetic (page table row, page size) rather than
+    the oracle's cache walk."""
+    import workloads as W
+    from tests import casebuild as CB
+    spec = W.small_case("attn_subset", 33, [700, 1500, 90], n_new=0, h=4, k=128, modes=(O.FULL,), page_size=64)
+    case = CB.build(spec)
+    cache = case.fresh_cache()
+    rng = np.random.default_rng(34)
+    q_seq, q_vis = spec.q_seq(), spec.q_vis()
+    nq, k = len(q_seq), spec.k
+    idx = np.full((nq, k), -1, dtype=np.int32)
+    cnt = np.zeros(nq, dtype=np.int32)
+    for i in range(nq):
+        c = int(rng.integers(1, min(k, int(q_vis[i])) + 1))
+        idx[i, :c] = rng.choice(int(q_vis[i]), size=c, replace=False)
+        cnt[i] = c
+    q = case.layers[0].q                                              # [nq][H][512] bf16 bits
+    scale = spec.sm_scale
+    out, lse = O.sparse_attn(cache, q, q_seq, idx, cnt, scale)
+    flat = cache.kv.reshape(-1, O.KV_ROW_BYTES)
+    for i in range(nq):
+        s = int(q_seq[i])
+        slots = np.array([W.slots_for(spec, case.page_table, s, int(t), int(t) + 1)[0] for t in idx[i, :cnt[i]]])
+        x = O.dequantize_kv_rows(flat[slots])
+        ro, rl = _torch_dense(O.bf16_to_f64(q[i]), x, scale)
+        np.testing.assert_allclose(out[i], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[i], rl, rtol=1e-13, atol=1e-13)
