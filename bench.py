@@ -105,6 +105,13 @@ def pool_scan_bytes(nq: int, pool_k: int, h_idx: int) -> int:
 # timing helpers
 # ---------------------------------------------------------------------------
 
+def percentiles(xs) -> dict:
+    """p10 / p50 / p90 of per-step durations (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {f"p{p}": round(float(np.percentile(a, p)), 5) for p in (10, 50, 90)}
+
+
 def _avg_us(xs):
     return round(statistics.mean(xs) * 1e3, 2) if xs else None
 
@@ -587,6 +594,7 @@ def bench_decode(args, cfg, spec) -> int:
         "group_bytes": gb,
         "group_hbm_frac": round(gb / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "timed_region_wall_ms": round(wall_ms, 3),
+        "step_ms_percentiles": percentiles(step_ms),
     }
     if args.only_timed:
         out["cpu_baseline"] = None
