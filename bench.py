@@ -120,15 +120,17 @@ def event_avg_ms(launch, reps: int) -> float:
     """Mean duration of `reps` back-to-back launches on the current stream,
     bracketed by one pair of device events (for single-kernel calls)."""
     import torch
+
+    from fp4_kv_cache_layer_amd import ops
     launch()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = ops.HipEvent(), ops.HipEvent()
     e0.record()
     for _ in range(reps):
         launch()
     e1.record()
-    e1.synchronize()
-    return e0.elapsed_time(e1) / reps
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) / reps
 
 
 class Scrubber:
@@ -147,16 +149,20 @@ class Scrubber:
 
 def scrubbed_steps(step, n: int, scrub) -> list:
     """n steps, each after a cache scrub and bracketed by device events on
-    the current stream; returns the step durations in ms."""
+    the current stream (timing events without the system-scope fence, whose
+    cache write-back would slow the step they bracket); returns the step
+    durations in ms."""
     import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    from fp4_kv_cache_layer_amd import ops
+    evs = [(ops.HipEvent(), ops.HipEvent()) for _ in range(n)]
     for e0, e1 in evs:
         scrub()
         e0.record()
         step()
         e1.record()
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    return [a.elapsed_ms(b) for a, b in evs]
 
 
 def time_lse_merge(o_a, lse_a, reps: int = 20):

@@ -253,9 +253,17 @@ csa2_status prepare_step(int32_t mode_value, const csa2_step_args* a, Step* p) {
   return CSA2_OK;
 }
 
+// A Full layer's few appended rows ride in the scan launch (one launch less):
+// per-query scan, no pool, no block-level representation to refresh.
+bool append_in_scan(const Step& p) {
+  const csa2_step_args* a = p.a;
+  return p.mode == CSA2_FULL && a->n_new > 0 && a->n_new <= kMaxFusedAppend && a->nq > 0 && a->max_vis > 0 &&
+         !p.dense && !p.pool && !p.prune && a->cache->idxk_bounds == nullptr;
+}
+
 csa2_status stage_append(const Step& p, hipStream_t s) {
   const csa2_step_args* a = p.a;
-  if (p.mode != CSA2_FULL || a->n_new == 0) return CSA2_OK;
+  if (p.mode != CSA2_FULL || a->n_new == 0 || append_in_scan(p)) return CSA2_OK;
   TimedLaunch t(p.tm, CSA2_KCLASS_APPEND);
   uint8_t* const bounds = a->cache->idxk_bounds;
   if (!bounds)
@@ -285,6 +293,11 @@ csa2_status stage_scan(const Step& p, hipStream_t s) {
     if (st != CSA2_OK) return st;
     return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k, a->max_vis,
                                         p.iw, s, t.ev.last()));
+  }
+  if (append_in_scan(p)) {
+    const AppendArgs ap{p.ca.kv, p.ca.idx_k, a->new_slots, a->new_kv, a->new_idxk, a->n_new};
+    return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx, a->k,
+                                        a->max_vis, p.iw, s, t.ev, &ap));
   }
   return hip_status(launch_index_scan(p.ca, a->q_idx, a->w, a->q_seq, a->q_vis, a->nq, a->h_idx,
                                       p.pool ? a->pool_k : a->k, a->max_vis, p.iw, s, t.ev));
@@ -652,9 +665,13 @@ csa2_status csa2_group_step(int32_t n, const csa2_mode* modes, const csa2_step_a
         if (aux_of[j] >= 0 && need_done[j] && layers_conflict(steps[j], p) &&
             !hip(hipStreamWaitEvent(s, ev_done(j), 0)))
           return CSA2_ERR_HIP;
+      // the append is done after stage_append, or after stage_scan when the
+      // scan launch carries it
+      const bool in_scan = append_in_scan(p);
       st = stage_append(p, s);
-      if (st == CSA2_OK && need_append[i] && !record_s(ev_append(i), &seq_of_append[i])) st = CSA2_ERR_HIP;
+      if (st == CSA2_OK && need_append[i] && !in_scan && !record_s(ev_append(i), &seq_of_append[i])) st = CSA2_ERR_HIP;
       if (st == CSA2_OK) st = stage_scan(p, s);
+      if (st == CSA2_OK && need_append[i] && in_scan && !record_s(ev_append(i), &seq_of_append[i])) st = CSA2_ERR_HIP;
       if (st == CSA2_OK) st = stage_select(p, s);
       if (st == CSA2_OK && need_sel[i] && !record_s(ev_sel(i), &seq_of_sel[i])) st = CSA2_ERR_HIP;
       if (st == CSA2_OK) st = stage_attn(p, s);

@@ -18,38 +18,9 @@ __global__ void __launch_bounds__(256)
 append_quant_kernel(uint8_t* __restrict__ kv, uint8_t* __restrict__ idx_k,
                     const int32_t* __restrict__ slots,
                     const uint16_t* __restrict__ kv_rows, const uint16_t* __restrict__ idxk_rows, int n) {
-  const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  const int64_t slot = slots[row];
-
-  // ---- main-KV row ----
-  const uint4 raw = *reinterpret_cast<const uint4*>(kv_rows + (int64_t)row * kLatent + 8 * lane);
-  float x[8];
-  const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(wds[i] << 16);
-    x[2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  const int e = block_exponent(amax);
-  uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= e2m1_code(ldexpf(x[i], -e)) << (4 * i);
-  uint8_t* dst = kv + slot * kKvRowBytes;
-  *reinterpret_cast<uint32_t*>(dst + 4 * lane) = packed;
-  if ((lane & 3) == 0) dst[kCodeBytes + (lane >> 2)] = (uint8_t)(e + 127);
-
-  // ---- indexer-K row ----
-  const uint32_t iw = *reinterpret_cast<const uint32_t*>(idxk_rows + (int64_t)row * kIndexDim + 2 * lane);
-  const uint32_t c0 = e4m3_code(__uint_as_float(iw << 16));
-  const uint32_t c1 = e4m3_code(__uint_as_float(iw & 0xFFFF0000u));
-  *reinterpret_cast<uint16_t*>(idx_k + slot * kIndexDim + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  append_row(kv, idx_k, slots, kv_rows, idxk_rows, row, threadIdx.x & 63);
 }
 
 hipError_t launch_append_quant(uint8_t* kv, uint8_t* idx_k, const int32_t* slots, const uint16_t* kv_rows,

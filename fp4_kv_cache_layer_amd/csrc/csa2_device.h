@@ -67,6 +67,45 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return c | sign;
 }
 
+// Quantize-on-append of one row by one wavefront (lane = 0..63): the bf16
+// latent row kv_rows[row] -> 256 E2M1 code bytes and 16 E8M0 scale bytes,
+// the bf16 indexer row idxk_rows[row] -> 128 E4M3FN bytes, both written at
+// physical slot slots[row].  Lane l owns latent elements 8l..8l+7 (one
+// 16-byte load), so a 32-element scale block is 4 adjacent lanes and its
+// amax is two lane swaps away; the same lane owns indexer elements 2l, 2l+1.
+__device__ __forceinline__ void append_row(uint8_t* __restrict__ kv, uint8_t* __restrict__ idx_k,
+                                           const int32_t* __restrict__ slots,
+                                           const uint16_t* __restrict__ kv_rows,
+                                           const uint16_t* __restrict__ idxk_rows, int row, int lane) {
+  const int64_t slot = slots[row];
+  // ---- main-KV row ----
+  const uint4 raw = *reinterpret_cast<const uint4*>(kv_rows + (int64_t)row * kLatent + 8 * lane);
+  float x[8];
+  const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(wds[i] << 16);
+    x[2 * i + 1] = __uint_as_float(wds[i] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = block_exponent(amax);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed |= e2m1_code(ldexpf(x[i], -e)) << (4 * i);
+  uint8_t* dst = kv + slot * kKvRowBytes;
+  *reinterpret_cast<uint32_t*>(dst + 4 * lane) = packed;
+  if ((lane & 3) == 0) dst[kCodeBytes + (lane >> 2)] = (uint8_t)(e + 127);
+  // ---- indexer-K row ----
+  const uint32_t iw = *reinterpret_cast<const uint32_t*>(idxk_rows + (int64_t)row * kIndexDim + 2 * lane);
+  const uint32_t c0 = e4m3_code(__uint_as_float(iw << 16));
+  const uint32_t c1 = e4m3_code(__uint_as_float(iw & 0xFFFF0000u));
+  *reinterpret_cast<uint16_t*>(idx_k + slot * kIndexDim + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+}
+
 // fp32 score -> unsigned key whose order is the float order; -0 counts as +0.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);

@@ -120,9 +120,21 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // the entries at or above the chunk's local rank threshold as candidates
 // (indices, score keys, their histogram, and the chunk's key floor); the final
 // select then completes the exact Top-k (k is needed for the local rank).
+// A layer step's quantize-on-append of at most kMaxFusedAppend rows can run
+// inside the scan launch (its own workgroups write the rows; scan workgroups
+// whose chunk holds one score it from the bf16 source).
+struct AppendArgs {
+  uint8_t* kv;
+  uint8_t* idx_k;
+  const int32_t* slots;
+  const uint16_t* kv_rows;
+  const uint16_t* idxk_rows;
+  int n;
+};
+constexpr int kMaxFusedAppend = 64;
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                              const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                             hipStream_t s, const KEvents& ev = {});
+                             hipStream_t s, const KEvents& ev = {}, const AppendArgs* ap = nullptr);
 // Inputs of the final select's repair of a chunk whose local threshold lies
 // above the k-th key's bin (per-query scan only).
 struct ScanArgs {

@@ -68,24 +68,43 @@ size_t index_score_bytes(int32_t nq, int32_t max_vis) {
   return (size_t)nq * 8 * v + (size_t)nq * fstride * 8 + (size_t)nq * fstride * 32 * 4;
 }
 
+// kAppend: the launch also appends ap.n <= kMaxFusedAppend rows: its first
+// ceil(n / 4) workgroups write them (one wave per row), and a chunk that
+// holds an appended row takes that row's E4M3 codes from its bf16 source
+// instead of the cache, so no tile depends on those stores.
+template <bool kAppend>
 __global__ void __launch_bounds__(kScanWaves * 64)
 index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                   const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_vis,
-                  int nq, int h_idx, int k, IndexWs ws) {
+                  int nq, int h_idx, int k, IndexWs ws, AppendArgs ap) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ float sc[kScanChunk + 1];                // the chunk's scores (+ a sink slot)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kScanWaves][kFp8SlotBytes];   // then the candidate list
   __shared__ uint32_t res[2];
   __shared__ int nlist, base;                          // listed candidates, their place in the query's list
   __shared__ int concentrated;                         // candidates crowd into one block
+  constexpr int kPatch = kAppend ? kMaxFusedAppend : 1;
+  __shared__ int npatch_s;                             // appended rows inside this chunk
+  __shared__ int patch_pos[kPatch], patch_src[kPatch];   // their position in the chunk, their source row
+  __shared__ uint32_t patch_code[kPatch][kIndexDim / 4];  // their E4M3 codes
+  int bid = blockIdx.x;
+  if constexpr (kAppend) {
+    const int na = (ap.n + 3) >> 2;
+    if (bid < na) {                                    // an appending workgroup
+      const int row = bid * 4 + (threadIdx.x >> 6);
+      if (row < ap.n) append_row(ap.kv, ap.idx_k, ap.slots, ap.kv_rows, ap.idxk_rows, row, threadIdx.x & 63);
+      return;
+    }
+    bid -= na;
+  }
   // query-major: the chunks of one query are consecutive blocks.  On ragged
   // batches the grid is sized by the longest query and most blocks of the
   // short ones exit at once; in this order the working blocks of every query
   // are dispatched together (chunk-major order left the long queries' chunks
   // to a thin tail: 0.43 -> 0.62 of HBM on the ragged decode workload)
-  const int nch = gridDim.x / nq;
-  const int q = blockIdx.x / nch;
-  const int chunk = blockIdx.x - q * nch;
+  const int nch = ws.fstride;                          // chunks per query
+  const int q = bid / nch;
+  const int chunk = bid - q * nch;
   const int vis = clamp_vis(q_vis[q], ws);
   const int t0 = chunk * kScanChunk;
   if (t0 >= vis || vis <= k) return;                  // uniform; with V <= k the select takes everything
@@ -125,7 +144,56 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int npg = ((t1 - 1) >> c.lg_page) - pg0 + 1;
   const int page_of_lane = lane < npg ? clamp_page(pt_row[pg0 + lane], c) : 0;
   const int ntiles = (t1 - t0 + 15) >> 4;
+  if constexpr (kAppend) {
+    // the appended rows inside this chunk: lane i checks row i's slot
+    // against the chunk's pages
+    if (wave == 0) {
+      int pos = -1;
+      if (lane < ap.n) {
+        const int sl = ap.slots[lane];
+        const int pg = sl >> c.lg_page;
+        for (int p = 0; p < npg; ++p)
+          if (__builtin_amdgcn_readlane(page_of_lane, p) == pg) {
+            const int t = ((pg0 + p) << c.lg_page) + (sl & ((1 << c.lg_page) - 1));
+            if (t >= t0 && t < t1) pos = t - t0;
+          }
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(pos >= 0);
+      if (pos >= 0) {
+        const int at = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        patch_pos[at] = pos;
+        patch_src[at] = lane;
+      }
+      if (lane == 0) npatch_s = __builtin_popcountll(m);
+    }
+  }
   lds_barrier();
+  const int npatch = kAppend ? npatch_s : 0;          // uniform
+  if constexpr (kAppend) {
+    if (npatch > 0) {
+      // their codes, encoded as the appending workgroups encode them
+      for (int x = tid; x < npatch * (kIndexDim / 4); x += kScanWaves * 64) {
+        const int p = x / (kIndexDim / 4), d = x % (kIndexDim / 4);
+        const uint2 bf = *reinterpret_cast<const uint2*>(ap.idxk_rows + (int64_t)patch_src[p] * kIndexDim + 4 * d);
+        patch_code[p][d] = e4m3_code(__uint_as_float(bf.x << 16)) | (e4m3_code(__uint_as_float(bf.x & 0xFFFF0000u)) << 8) |
+                           (e4m3_code(__uint_as_float(bf.y << 16)) << 16) |
+                           (e4m3_code(__uint_as_float(bf.y & 0xFFFF0000u)) << 24);
+      }
+      lds_barrier();
+    }
+  }
+  // a loaded tile j with its appended rows' bytes replaced (lane l holds
+  // bytes [32 (l % 4), +32) of the tile's row l / 4)
+  auto patch = [&](int j, intx8& lin) {
+    for (int p = 0; p < npatch; ++p) {                // uniform
+      const int pos = patch_pos[p];
+      if ((pos >> 4) == j && (lane >> 2) == (pos & 15)) {
+        const uint32_t* src = &patch_code[p][8 * (lane & 3)];
+        lin = intx8{(int)src[0], (int)src[1], (int)src[2], (int)src[3], (int)src[4], (int)src[5], (int)src[6],
+                    (int)src[7]};
+      }
+    }
+  };
 
   // Tiles j = wave, wave + 4, ... of this wave, kScanDepth - 1 in flight ahead
   // of the one in use (a ring of buffers addressed by name after unrolling).  A tile's 16 rows are 2 KB of
@@ -150,7 +218,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   intx8 buf[kScanDepth];
 #pragma unroll
   for (int d = 0; d + 1 < kScanDepth; ++d) load(wave + d * kScanWaves, buf[d]);
-  if (ntiles == kScanChunk / 16 && pmask == 0) {
+  if (ntiles == kScanChunk / 16 && pmask == 0 && npatch == 0) {
     // full chunk: a fixed schedule, unrolled, so every wait on the ring is exact
     constexpr int kSteps = kScanChunk / 16 / kScanWaves;
 #pragma unroll
@@ -167,7 +235,10 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
         const int jl = j + (u + kScanDepth - 1) * kScanWaves;
         if (!pruned_tile(min(jl, ntiles - 1))) load(jl, buf[(u + kScanDepth - 1) % kScanDepth]);
         if (j + u * kScanWaves >= ntiles) break;
-        if (!pruned_tile(j + u * kScanWaves)) process(j + u * kScanWaves, buf[u]);
+        if (!pruned_tile(j + u * kScanWaves)) {
+          if (kAppend && npatch > 0) patch(j + u * kScanWaves, buf[u]);
+          process(j + u * kScanWaves, buf[u]);
+        }
       }
     }
   }
@@ -264,15 +335,21 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 
 hipError_t launch_index_scan(const CacheArgs& c, const uint8_t* q_idx, const float* w, const int32_t* q_seq,
                              const int32_t* q_vis, int nq, int h_idx, int k, int max_vis, const IndexWs& ws,
-                             hipStream_t s, const KEvents& ev) {
+                             hipStream_t s, const KEvents& ev, const AppendArgs* ap) {
   const int nchunks = (max_vis + kScanChunk - 1) / kScanChunk;
   const int64_t blocks = (int64_t)nq * nchunks;
+  if (ap != nullptr && ap->n > 0) {
+    // the rows are written whatever the scan covers
+    launch(index_scan_kernel<true>, dim3((unsigned)(blocks + (ap->n + 3) / 4)), dim3(kScanWaves * 64), s, ev, c,
+           q_idx, w, q_seq, q_vis, nq, h_idx, k, ws, *ap);
+    return hipGetLastError();
+  }
   if (blocks <= 0) {
     record_empty(ev, s);
     return hipSuccess;
   }
-  launch(index_scan_kernel, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis, nq,
-         h_idx, k, ws);
+  launch(index_scan_kernel<false>, dim3((unsigned)blocks), dim3(kScanWaves * 64), s, ev, c, q_idx, w, q_seq, q_vis,
+         nq, h_idx, k, ws, AppendArgs{});
   return hipGetLastError();
 }
 

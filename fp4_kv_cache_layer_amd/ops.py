@@ -448,25 +448,53 @@ class GroupCall:
             L.check("csa2_group_step", st)
 
 
+# Timing events skip the system-scope fence of a plain event: they only
+# measure, and read after a device synchronisation, and the fence's cache
+# write-back would otherwise slow the work being timed.
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvent:
+    """A timing hipEvent created without the system-scope fence (see
+    hipEventDisableSystemFence in hip_runtime_api.h)."""
+
+    def __init__(self):
+        self.lib = L.load()
+        self.handle = ctypes.c_void_p()
+        if self.lib.hipEventCreateWithFlags(ctypes.byref(self.handle), _HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream=None) -> None:
+        if self.lib.hipEventRecord(self.handle, ctypes.c_void_p(_stream(stream))) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            self.lib.hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+
 class TimingRing:
     """Device-event ring for one kernel class: start/stop hipEvent pairs that
     the library records through the launches of calls carrying it."""
 
     def __init__(self, capacity: int):
-        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(capacity)]
-        for a, b in self.events:          # materialise the hipEvent handles
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        self._start = (ctypes.c_void_p * capacity)(*[a.cuda_event for a, _ in self.events])
-        self._stop = (ctypes.c_void_p * capacity)(*[b.cuda_event for _, b in self.events])
+        self.events = [(HipEvent(), HipEvent()) for _ in range(capacity)]
+        self._start = (ctypes.c_void_p * capacity)(*[a.handle.value for a, _ in self.events])
+        self._stop = (ctypes.c_void_p * capacity)(*[b.handle.value for _, b in self.events])
         self.ring = L.TimingRing(ctypes.cast(self._start, ctypes.POINTER(ctypes.c_void_p)),
                                  ctypes.cast(self._stop, ctypes.POINTER(ctypes.c_void_p)), capacity, 0)
 
     def durations_ms(self):
         torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in self.events[:self.ring.count]]
+        return [a.elapsed_ms(b) for a, b in self.events[:self.ring.count]]
 
 
 class Timing:

@@ -174,6 +174,25 @@ def test_group_integer_exact(seed, cached, h_idx, k):
     _compare_group(spec, exact_topk=True)
 
 
+@pytest.mark.parametrize("seed,cached,n_new", [
+    (26, [2047, 4095, 1], 1),              # an appended row ending a full chunk; a one-row chunk
+    (27, [2046, 6143, 300], 3),            # appended rows across a chunk boundary
+    (28, [700] * 30, 3),                   # 90 appended rows: more than one launch carries
+])
+def test_full_layer_append_positions(seed, cached, n_new):
+    """Appended rows at chunk ends, across chunk boundaries and in numbers
+    past what the scan launch carries itself: every layer's selection
+    bit-exact against the oracle, and the appended rows' cache bytes equal to
+    the oracle's encoding."""
+    spec = W.small_case("append_pos", seed, cached, n_new=n_new, h_idx=8, h=16, k=128, integer_indexer=True)
+    dc, got, ref = _compare_group(spec, exact_topk=True)
+    case = CB.build(spec)
+    kv = dc.cache.kv.reshape(-1, O.KV_ROW_BYTES)[torch.from_numpy(case.new_slots.astype(np.int64)).cuda()].cpu().numpy()
+    ik = dc.cache.idx_k.reshape(-1, 128)[torch.from_numpy(case.new_slots.astype(np.int64)).cuda()].cpu().numpy()
+    assert np.array_equal(kv, O.quantize_kv_rows(O.bf16_to_f64(case.new_kv)))
+    assert np.array_equal(ik, O.quantize_idxk_rows(O.bf16_to_f64(case.new_ik)))
+
+
 @pytest.mark.parametrize("seed,cached,h", [
     (31, [4096, 1500, 700], 64),
     (32, [3000, 200], 24),
