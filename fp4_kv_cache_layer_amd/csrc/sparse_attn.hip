@@ -556,12 +556,13 @@ sparse_attn_hg_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
 // The waves merge their (O, running max, running sum) through LDS at the end,
 // each wave producing 16 / W n-tiles of the output.
 constexpr int kDsHalf = 256;                        // output dims per workgroup
+constexpr int kPtRegPages = 256;                    // page-table rows held in registers up to this length
 constexpr int kDsStride = 2 * kDsHalf + 32;         // bytes per staged bf16 row (512 + 32 pad)
 
 template <int W>
 struct AttnDsShared {
   uint8_t xs[W][kTileRows * kDsStride];    // [wave] staged rows of its current tile, this half (17,408 B each)
-  uint32_t row[kMaxShareRows];             // physical row of every selected entry (8,192 B)
+  uint32_t row[kMaxShareRows + 1];         // physical row of every selected entry (8,192 B), a sink slot
   float m[W][16];
   float l[W][16];
 };
@@ -592,43 +593,86 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
   // this workgroup's half (their dequantised rows are staged for P.V), slots
   // 2 and 3 the other half (Q.X^T only).  chunk(s) = (s + 2 half) mod 4.
   const int ch_of[4] = {2 * half, 2 * half + 1, 2 - 2 * half, 3 - 2 * half};
-  // Q^T operand: head r; slot s, K-step t holds dims 128 chunk(s) + 32 g + 8 t .. +7
+  // Physical rows of this wave's own tiles (wv, wv + W, ...; half a wave per
+  // tile), resolved by the wave itself, so no workgroup barrier stands
+  // between a wave's lookups and its first gathers.  The loads the lookups
+  // need go out first and together: the page-table row when it has at most
+  // kPtRegPages entries (into the wave's registers, lane l: entries l + 64 i,
+  // looked up with cross-lane reads; a longer row is read per index) and the
+  // indices of the wave's first eight tiles (clamped to the k-entry row and
+  // loaded whatever the count, so they wait neither for it nor for each
+  // other), with the Q operand's loads in the same trip.  (Index loads under
+  // a branch each waited for the one before: four trips, then four more for
+  // the page ids.)
+  const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
+  const int32_t* irow = idx + (int64_t)qi * k;
+  const int ktiles = (k + kTileRows - 1) / kTileRows;
+  const bool pt_regs = c.max_pages <= kPtRegPages;        // uniform
+  const int npr = (c.max_pages + 63) >> 6;
+  int ptv[kPtRegPages / 64];
+  // indices of tiles wv + W (i0 + 2u), u < 4, with i0 = i0b + (lane >= 32)
+  auto index_loads = [&](int i0b, int (&tv)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int T = wv + W * (i0b + (lane >> 5) + 2 * u);
+      tv[u] = irow[min(T * kTileRows + (lane & 31), k - 1)];
+    }
+  };
+  const int tmax = (c.max_pages << c.lg_page) - 1;
+  // (kRegs: the row is in ptv; neither form loads under a branch)
+  auto lookups = [&](int i0b, const int (&tv)[4], auto regs) {
+    constexpr bool kRegs = decltype(regs)::value;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int T = wv + W * (i0b + (lane >> 5) + 2 * u);
+      const int j = T * kTileRows + (lane & 31);
+      const int t = min(max(tv[u], 0), tmax);            // (as entry_row_clamped)
+      const int pg = t >> c.lg_page;
+      int page = 0;
+      if constexpr (kRegs) {
+#pragma unroll
+        for (int i = 0; i < kPtRegPages / 64; ++i)
+          if (i < npr) {                                 // (uniform)
+            const int v = __builtin_amdgcn_ds_bpermute((pg & 63) << 2, ptv[i]);
+            page = (pg >> 6) == i ? v : page;
+          }
+      } else {
+        page = pt_row[pg];
+      }
+      // (stored by every lane, the ones outside the selection into a sink
+      // slot, so no load above moves into a branch)
+      S.row[T < ktiles && j < n ? j : kMaxShareRows] =
+          ((uint32_t)clamp_page(page, c) << c.lg_page) + (uint32_t)(t & ((1 << c.lg_page) - 1));
+    }
+  };
+  // Q^T operand: head r; slot s, K-step t holds dims 128 chunk(s) + 32 g + 8 t .. +7.
+  // Lanes of heads past h load head 0 (their columns of S and rows of O are
+  // computed but never stored).
   bf16x8 qop[4][4];
-  {
-    const bool ok = head < h;
-    const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)qi * h + (ok ? head : 0)) * kLatent + 32 * g);
+  const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((int64_t)qi * h + (head < h ? head : 0)) * kLatent + 32 * g);
+  // (one instance per form, each with its loads in the order above)
+  auto prologue = [&](auto regs) {
+    if constexpr (decltype(regs)::value) {
+#pragma unroll
+      for (int i = 0; i < kPtRegPages / 64; ++i) ptv[i] = pt_row[min(lane + 64 * i, c.max_pages - 1)];
+    }
+    int tv0[4];
+    index_loads(0, tv0);
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        qop[sl][t] = __builtin_bit_cast(bf16x8, ok ? src[16 * ch_of[sl] + t] : make_uint4(0, 0, 0, 0));
-  }
-  {
-    // physical rows of this wave's own tiles (wv, wv + W, ...; half a wave
-    // per tile), resolved by the wave itself, so no workgroup barrier stands
-    // between a wave's lookups and its first gathers.  The index loads run
-    // over the k-entry row (clamped to it) and are issued four at a time, so
-    // they wait neither for the count nor for each other; only the
-    // page-table lookups need the count.
-    const int32_t* pt_row = c.page_table + (int64_t)q_seq[qi] * c.max_pages;
-    const int32_t* irow = idx + (int64_t)qi * k;
-    const int ktiles = (k + kTileRows - 1) / kTileRows;
-    for (int i0 = lane >> 5; wv + W * i0 < ktiles; i0 += 8) {
+      for (int t = 0; t < 4; ++t) qop[sl][t] = __builtin_bit_cast(bf16x8, qsrc[16 * ch_of[sl] + t]);
+    lookups(0, tv0, regs);
+    for (int i0b = 8; wv + W * i0b < ktiles; i0b += 8) {    // (k > 32 W tiles only)
       int tv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int T = wv + W * (i0 + 2 * u);
-        const int j = T * kTileRows + (lane & 31);
-        tv[u] = T < ktiles ? irow[min(j, k - 1)] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int T = wv + W * (i0 + 2 * u);
-        const int j = T * kTileRows + (lane & 31);
-        if (T < ktiles && j < n) S.row[j] = (uint32_t)entry_row_clamped(pt_row, tv[u], c);
-      }
+      index_loads(i0b, tv);
+      lookups(i0b, tv, regs);
     }
-  }
+  };
+  if (pt_regs)
+    prologue(std::true_type{});
+  else
+    prologue(std::false_type{});
   __builtin_amdgcn_wave_barrier();                       // the wave's row writes stay above its gathers
 
   floatx4 oacc[16];
