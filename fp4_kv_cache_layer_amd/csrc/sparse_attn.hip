@@ -658,6 +658,9 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
     }
     int tv0[4];
     index_loads(0, tv0);
+    // (the Q loads stay behind the index loads: loads complete in order, so
+    // the lookups then wait for the indices alone)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -823,12 +826,21 @@ sparse_attn_ds_kernel(CacheArgs c, const uint16_t* __restrict__ q, const int32_t
   if (my_tiles > 0) {
     Gath ga, gb;
     gather(0, ga);
-    for (int tt = 0; tt < my_tiles; tt += 2) {
+    int tt = 0;
+    for (; tt + 2 < my_tiles; tt += 2) {                 // two or more tiles after these
       gather(tt + 1, gb);
       process(tt, ga);
-      if (tt + 1 >= my_tiles) break;
       gather(tt + 2, ga);
       process(tt + 1, gb);
+    }
+    // the last one or two: nothing is gathered past the wave's tiles, so the
+    // merge below waits for no load
+    if (tt + 1 < my_tiles) {
+      gather(tt + 1, gb);
+      process(tt, ga);
+      process(tt + 1, gb);
+    } else {
+      process(tt, ga);
     }
   }
 
