@@ -38,7 +38,13 @@ namespace csa2 {
 // to whichever CUs finish first (64K decode group: 52.5 -> 48.5 us against
 // four waves and one round; 16 waves: 59 us).
 constexpr int kScanWaves = 8;
-constexpr int kScanDepth = 6;           // tiles per wave in the load ring
+// Ring of 4 tiles per wave: three loads ahead of the one in use, so a launch
+// keeps about 24 MB of loads in flight, enough to cover HBM latency; deeper
+// rings only lengthen the memory queues, and every other load of the launch
+// (a new workgroup's page ids, its query, the reservation atomics) waits
+// behind them (64K decode group: 48.9 -> 47.3 us against 6 tiles; 3 tiles
+// 49.4 us).
+constexpr int kScanDepth = 4;
 
 // DPP controls: rotate right within each row of 16 lanes
 constexpr int kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
@@ -126,6 +132,8 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
   const int pg0 = t0 >> c.lg_page;
   const int npg = ((t1 - 1) >> c.lg_page) - pg0 + 1;
   const int pt_entry = pt_row[pg0 + min(lane, npg - 1)];   // (unconditional: nothing waits for it here)
+  // the appended rows' slots (lane i: row i), in the same trip
+  const int ap_slot = kAppend ? ap.slots[min(lane, max(ap.n, 1) - 1)] : 0;
   // block-level pruning: blocks of this chunk that cannot hold a Top-k entry
   const uint32_t pmask = ws.prune ? ws.prune[(int64_t)q * ws.fstride + chunk] : 0u;
   const int nblk = (t1 - t0 + kPruneBlockRows - 1) / kPruneBlockRows;
@@ -156,13 +164,31 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
 
   const int page_of_lane = lane < npg ? clamp_page(pt_entry, c) : 0;
   const int ntiles = (t1 - t0 + 15) >> 4;
+
+  // Tiles j = wave, wave + kScanWaves, ... of this wave, kScanDepth - 1 in flight ahead
+  // of the one in use (a ring of buffers addressed by name after unrolling).  A tile's 16 rows are 2 KB of
+  // contiguous memory: loaded coalesced, turned into the MFMA operand through
+  // the wave's LDS slot.  Loads past the end re-read the last tile.  The
+  // ring's first loads go out before the appended rows are located (their
+  // bytes are replaced when a tile is scored), so they wait for the page ids
+  // alone.
+  auto load = [&](int j, intx8& lin) {
+    j = min(j, ntiles - 1);
+    const int ts = t0 + 16 * j;                       // tiles never straddle pages
+    const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
+    lin = load_fp8_tile_linear(c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim,
+                               lane);
+  };
+  intx8 buf[kScanDepth];
+#pragma unroll
+  for (int d = 0; d + 1 < kScanDepth; ++d) load(wave + d * kScanWaves, buf[d]);
   if constexpr (kAppend) {
     // the appended rows inside this chunk: lane i checks row i's slot
     // against the chunk's pages
     if (wave == 0) {
       int pos = -1;
       if (lane < ap.n) {
-        const int sl = ap.slots[lane];
+        const int sl = ap_slot;
         const int pg = sl >> c.lg_page;
         for (int p = 0; p < npg; ++p)
           if (__builtin_amdgcn_readlane(page_of_lane, p) == pg) {
@@ -207,18 +233,7 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
     }
   };
 
-  // Tiles j = wave, wave + kScanWaves, ... of this wave, kScanDepth - 1 in flight ahead
-  // of the one in use (a ring of buffers addressed by name after unrolling).  A tile's 16 rows are 2 KB of
-  // contiguous memory: loaded coalesced, turned into the MFMA operand through
-  // the wave's LDS slot.  Loads past the end re-read the last tile.
   uint8_t* const slot = stage[wave];
-  auto load = [&](int j, intx8& lin) {
-    j = min(j, ntiles - 1);
-    const int ts = t0 + 16 * j;                       // tiles never straddle pages
-    const int page = __builtin_amdgcn_readlane(page_of_lane, (ts >> c.lg_page) - pg0);
-    lin = load_fp8_tile_linear(c.idx_k + (((int64_t)page << c.lg_page) + (ts & ((1 << c.lg_page) - 1))) * kIndexDim,
-                               lane);
-  };
   auto process = [&](int j, const intx8& lin) {
     const float sv = tile_score(a, wv, slot, lin, lane);   // every lane: entry r's score
     const int i = 16 * j + r;                         // position in the chunk
@@ -227,9 +242,6 @@ index_scan_kernel(CacheArgs c, const uint8_t* __restrict__ q_idx, const float* _
       if (t0 + i < t1) atomicAdd(&hist[score_key(sv) >> (32 - kHistBits)], 1u);
     }
   };
-  intx8 buf[kScanDepth];
-#pragma unroll
-  for (int d = 0; d + 1 < kScanDepth; ++d) load(wave + d * kScanWaves, buf[d]);
   if (ntiles == kScanChunk / 16 && pmask == 0 && npatch == 0) {
     // full chunk: a fixed schedule, unrolled, so every wait on the ring is exact
     constexpr int kSteps = kScanChunk / 16 / kScanWaves;
